@@ -1,0 +1,256 @@
+"""Throughput of one exact-attention training step on one MI355X.
+
+A step is the whole path once: the forward pass (O and LSE) and the
+recomputation backward pass (delta = rowsum(dO o O), then dK/dV, then dQ) on
+B=1, H=32, n=4096, d=128 bf16 inputs already resident in device memory, each
+stage called through the C ABI on the current stream.
+
+value      = algorithmic FLOP of the step / step time, in TFLOP/s:
+             forward 4*B*H*n^2*d, backward 10*B*H*n^2*d (five products per
+             visible query-key pair); the causal variant counts only visible
+             pairs.
+roofline   = the kernel taking the largest share of the step, its algorithmic
+             FLOP per launch over its mean launch time from HIP events recorded
+             around it inside the timed loop, against the bf16 dense
+             matrix-core peak.
+cpu_baseline = the fp64 oracle timed on a bounded sample of the same workload.
+
+One JSON line is printed.  Only one GPU is supported: --gpus above 1 exits.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 matrix cores
+PEAK_HBM_GBS = 8000.0
+METRIC = "attention fwd/bwd TFLOP/s (4·B·H·n²·d/t) and % bf16 MFMA peak at n=4096,d=128"
+
+KERNEL_SOURCES = {
+    "fwd": "exact_attention_05_amd/csrc/fa_fwd.hip",
+    "bwd_preprocess": "exact_attention_05_amd/csrc/fa_bwd.hip",
+    "bwd_dkdv": "exact_attention_05_amd/csrc/fa_bwd.hip",
+    "bwd_dq": "exact_attention_05_amd/csrc/fa_bwd.hip",
+}
+
+
+def visible_pairs(n_q: int, n_k: int, causal: bool) -> int:
+    if not causal:
+        return n_q * n_k
+    m = min(n_q, n_k)
+    # rows 0..m-1 see i+1 keys; rows m..n_q-1 see all n_k keys
+    return m * (m + 1) // 2 + (n_q - m) * n_k
+
+
+def kernel_flops(B, H, n, d, causal):
+    """Algorithmic FLOP per launch of each stage (what the method must do)."""
+    pairs = B * H * visible_pairs(n, n, causal)
+    return {
+        "fwd": 4 * d * pairs,             # S = QK^T and P V
+        "bwd_preprocess": 2 * B * H * n * d,
+        "bwd_dkdv": 8 * d * pairs,        # S recomputed, dP, dV, dK
+        "bwd_dq": 2 * d * pairs,          # dQ (its S, dP recompute is overhead)
+    }
+
+
+def kernel_bytes(B, H, n, d, e=2):
+    """Algorithmic HBM bytes per launch (each operand read once, results written once)."""
+    t = B * H * n * d * e
+    r = B * H * n * 4
+    return {
+        "fwd": 3 * t + t + r,                     # read q k v, write o lse
+        "bwd_preprocess": 2 * t + r,              # read o dO, write delta
+        "bwd_dkdv": 4 * t + 2 * r + 2 * t,        # read q k v dO lse delta, write dk dv
+        "bwd_dq": 4 * t + 2 * r + t,              # read q k v dO lse delta, write dq
+    }
+
+
+def load_traffic(kernel: str):
+    """HBM bytes per launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE,
+    if recorded for the current source of that kernel; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    src = os.path.join(ROOT, KERNEL_SOURCES[kernel])
+    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if rec.get("source_sha256") != digest:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w, budget_s: float):
+    """The fp64 oracle (forward + explicit backward) on whole (b, h) units of
+    the same workload, repeated until about ``budget_s`` seconds of CPU work."""
+    import numpy as np
+
+    import oracle
+
+    try:
+        import threadpoolctl
+
+        info = threadpoolctl.threadpool_info()
+        threads = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
+    except Exception:  # noqa: BLE001
+        threads = None
+    B, H, n, d = w.q.shape
+    units = [(0, h) for h in range(H)]
+    t0 = time.perf_counter()
+    done = 0
+    while done < len(units):
+        b, h = units[done]
+        q, k, v, do = (x[b, h].to(dtype=w.q.dtype).float().numpy().astype(np.float64)
+                       for x in (w.q, w.k, w.v, w.do))
+        oracle.attention_fwd(q, k, v, w.scale, w.causal)
+        oracle.attention_bwd(q, k, v, do, w.scale, w.causal)
+        done += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    flops = done * 14 * d * visible_pairs(n, n, w.causal)
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{done} of {B * H} (b,h) units, fp64 numpy forward + explicit backward, {dt:.1f} s",
+    }
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--causal", action="store_true", help="causal mask (default: non-causal)")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle CPU work")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(heads shard across GPUs with no exchange; see DESIGN.md)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import exact_attention_05_amd as fa
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda:0")
+    w = workloads.c3_train(args.causal)
+    B, H, n, d = w.q.shape
+    q, k, v, do = (t.to(dev).contiguous() for t in (w.q, w.k, w.v, w.do))
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, n), dtype=torch.float32, device=dev)
+    delta = torch.empty((B, H, n), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    causal = args.causal
+
+    stages = ["fwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq"]
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        fa.forward(q, k, v, causal=causal, scale=w.scale, out=o, lse=lse)
+        if ev is not None:
+            ev[1].record()
+        fa.backward_preprocess(o, do, delta)
+        if ev is not None:
+            ev[2].record()
+        fa.backward_dkdv(q, k, v, do, lse, delta, causal=causal, scale=w.scale, dk=dk, dv=dv)
+        if ev is not None:
+            ev[3].record()
+        fa.backward_dq(q, k, v, do, lse, delta, causal=causal, scale=w.scale, dq=dq)
+        if ev is not None:
+            ev[4].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    per_stage = {s: 0.0 for s in stages}
+    step_ms = []
+    for ev in events:
+        for j, s in enumerate(stages):
+            per_stage[s] += ev[j].elapsed_time(ev[j + 1])
+        step_ms.append(ev[0].elapsed_time(ev[4]))
+    per_stage = {s: t / args.steps for s, t in per_stage.items()}
+    ms_per_step = wall * 1e3 / args.steps
+
+    flops = kernel_flops(B, H, n, d, causal)
+    nbytes = kernel_bytes(B, H, n, d)
+    step_flops = (4 + 10) * d * B * H * visible_pairs(n, n, causal)
+    value = step_flops / (ms_per_step * 1e-3) / 1e12
+
+    kernels = {}
+    for s in stages:
+        t = per_stage[s] * 1e-3
+        kernels[s] = {
+            "ms": round(per_stage[s], 4),
+            "tflops": round(flops[s] / t / 1e12, 2),
+            "gbs": round(nbytes[s] / t / 1e9, 1),
+        }
+    dominant = max(stages, key=lambda s: per_stage[s])
+    dom_t = per_stage[dominant] * 1e-3
+    achieved = flops[dominant] / dom_t / 1e12
+    traffic = load_traffic(dominant)
+    fwd_lit = 4 * B * H * n * n * d / (per_stage["fwd"] * 1e-3) / 1e12
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) q, k, v, dO; no dataset)",
+        "config": {"workload": w.name, "B": B, "H": H, "n": n, "d": d, "causal": causal,
+                   "scale": w.scale, "step": "fa_forward + fa_backward stages"},
+        "fwd_tflops_literal": round(fwd_lit, 2),
+        "fwd_pct_bf16_peak": round(100 * flops["fwd"] / (per_stage["fwd"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+        "kernels": kernels,
+        "roofline": {
+            "kernel": dominant,
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+        },
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+        out["cpu_baseline"]["value"] = round(out["cpu_baseline"]["value"], 6)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

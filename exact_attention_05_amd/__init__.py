@@ -1,0 +1,27 @@
+"""Exact scaled dot-product attention for AMD Instinct MI355X (gfx950).
+
+The computation runs in hand-written HIP kernels behind the C ABI declared in
+``include/fa.h`` (library ``lib/libfa.so``); this package is its Python
+binding.  See ``forward`` and ``backward``.
+"""
+from .binding import (  # noqa: F401
+    FA_DTYPE_BF16,
+    FA_DTYPE_FP32,
+    FA_ERR_ALIGNMENT,
+    FA_ERR_INVALID_ARG,
+    FA_ERR_LAUNCH,
+    FA_ERR_UNSUPPORTED,
+    FA_ERR_WORKSPACE,
+    FA_OK,
+    FaError,
+    backward,
+    backward_dkdv,
+    backward_dq,
+    backward_preprocess,
+    backward_workspace_size,
+    forward,
+    lib,
+    library_path,
+    status_string,
+    version,
+)

@@ -1,0 +1,211 @@
+"""ctypes binding of the C ABI in include/fa.h.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``lib/libfa.so``.  PyTorch supplies device memory and the current
+stream.  There is no fallback: if the library is missing, or a tensor is not
+on the GPU, the call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+__all__ = [
+    "FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_WORKSPACE", "FA_ERR_LAUNCH",
+    "FA_ERR_ALIGNMENT", "FA_DTYPE_FP32", "FA_DTYPE_BF16", "FaError", "library_path", "lib",
+    "forward", "backward", "backward_workspace_size", "backward_preprocess", "backward_dkdv",
+    "backward_dq", "status_string", "version",
+]
+
+FA_OK = 0
+FA_ERR_INVALID_ARG = 1
+FA_ERR_UNSUPPORTED = 2
+FA_ERR_WORKSPACE = 3
+FA_ERR_LAUNCH = 4
+FA_ERR_ALIGNMENT = 5
+FA_DTYPE_FP32 = 0
+FA_DTYPE_BF16 = 1
+
+_DTYPES = {torch.float32: FA_DTYPE_FP32, torch.bfloat16: FA_DTYPE_BF16}
+
+_lib = None
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+        self.status = status
+
+
+def library_path() -> str:
+    return os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libfa.so")
+
+
+def lib() -> ctypes.CDLL:
+    """Load libfa.so (built by ``python -m exact_attention_05_amd.build``)."""
+    global _lib
+    if _lib is None:
+        path = library_path()
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it with `python -m exact_attention_05_amd.build`")
+        L = ctypes.CDLL(path)
+        vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        L.fa_forward.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp]
+        L.fa_forward.restype = i
+        L.fa_backward_workspace_size.argtypes = [i, i, i, i, i, i]
+        L.fa_backward_workspace_size.restype = sz
+        L.fa_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
+                                  i, i, i, i, i, f, i, i, vp]
+        L.fa_backward.restype = i
+        L.fa_backward_preprocess.argtypes = [vp, vp, vp, i, i, i, i, i, vp]
+        L.fa_backward_preprocess.restype = i
+        L.fa_backward_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp]
+        L.fa_backward_dkdv.restype = i
+        L.fa_backward_dq.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp]
+        L.fa_backward_dq.restype = i
+        L.fa_status_string.argtypes = [i]
+        L.fa_status_string.restype = ctypes.c_char_p
+        L.fa_version.argtypes = []
+        L.fa_version.restype = i
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().fa_status_string(int(status)).decode()
+
+
+def version() -> int:
+    return int(lib().fa_version())
+
+
+def _stream(device: torch.device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ptr(t: torch.Tensor | None) -> ctypes.c_void_p:
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _check(status: int, where: str) -> None:
+    if status != FA_OK:
+        raise FaError(status, where)
+
+
+def _check_qkv(q, k, v):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor):
+            raise ValueError(f"{name} must be a tensor")
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be (B, H, n, d), got {tuple(t.shape)}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.dtype not in _DTYPES:
+            raise ValueError(f"{name}: dtype {t.dtype} not supported (float32 or bfloat16)")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must share a dtype")
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k, v must be on one device")
+    B, H, n_q, d = q.shape
+    if k.shape[:2] != (B, H) or v.shape[:2] != (B, H) or k.shape[3] != d or v.shape[3] != d:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
+    if k.shape[2] != v.shape[2]:
+        raise ValueError("k and v must have the same number of rows")
+    return B, H, n_q, k.shape[2], d
+
+
+def _scale(scale, d):
+    return 1.0 / math.sqrt(d) if scale is None else float(scale)
+
+
+def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None):
+    """O, LSE = attention(q, k, v).  q: (B,H,n_q,d); k, v: (B,H,n_k,d).
+
+    Returns O (q's dtype, (B,H,n_q,d)) and LSE (float32, (B,H,n_q)).
+    ``scale`` defaults to 1/sqrt(d).
+    """
+    B, H, n_q, n_k, d = _check_qkv(q, k, v)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, n_q), dtype=torch.float32, device=q.device)
+    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous() or out.device != q.device:
+        raise ValueError("out must be a contiguous tensor like q")
+    if lse.shape != (B, H, n_q) or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.device != q.device:
+        raise ValueError("lse must be a contiguous float32 (B, H, n_q) tensor")
+    st = lib().fa_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, n_q, n_k, d,
+                          _scale(scale, d), int(bool(causal)), _DTYPES[q.dtype], _stream(q.device))
+    _check(st, "fa_forward")
+    return out, lse
+
+
+def backward_workspace_size(B, H, n_q, n_k, d, dtype: torch.dtype) -> int:
+    return int(lib().fa_backward_workspace_size(B, H, n_q, n_k, d, _DTYPES[dtype]))
+
+
+def _check_like(name, t, ref):
+    if t.shape != ref.shape or t.dtype != ref.dtype or not t.is_contiguous() or t.device != ref.device:
+        raise ValueError(f"{name} must be a contiguous tensor shaped and typed like {tuple(ref.shape)} {ref.dtype}")
+
+
+def backward(q, k, v, o, do, lse, causal: bool = False, scale: float | None = None,
+             dq=None, dk=None, dv=None, workspace=None):
+    """dQ, dK, dV from the saved o and lse of ``forward``."""
+    B, H, n_q, n_k, d = _check_qkv(q, k, v)
+    _check_like("o", o, q)
+    _check_like("do", do, q)
+    if lse.shape != (B, H, n_q) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 (B, H, n_q) tensor")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _check_like("dq", dq, q)
+    _check_like("dk", dk, k)
+    _check_like("dv", dv, v)
+    ws_bytes = backward_workspace_size(B, H, n_q, n_k, d, q.dtype)
+    if workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    st = lib().fa_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq),
+                           _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                           B, H, n_q, n_k, d, _scale(scale, d), int(bool(causal)),
+                           _DTYPES[q.dtype], _stream(q.device))
+    _check(st, "fa_backward")
+    return dq, dk, dv
+
+
+def backward_preprocess(o, do, delta=None):
+    """delta = rowsum(do * o) in float32, (B, H, n_q)."""
+    B, H, n_q, d = o.shape
+    _check_like("do", do, o)
+    if delta is None:
+        delta = torch.empty((B, H, n_q), dtype=torch.float32, device=o.device)
+    st = lib().fa_backward_preprocess(_ptr(o), _ptr(do), _ptr(delta), B, H, n_q, d,
+                                      _DTYPES[o.dtype], _stream(o.device))
+    _check(st, "fa_backward_preprocess")
+    return delta
+
+
+def backward_dkdv(q, k, v, do, lse, delta, causal=False, scale=None, dk=None, dv=None):
+    B, H, n_q, n_k, d = _check_qkv(q, k, v)
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    st = lib().fa_backward_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(delta),
+                                _ptr(dk), _ptr(dv), B, H, n_q, n_k, d, _scale(scale, d),
+                                int(bool(causal)), _DTYPES[q.dtype], _stream(q.device))
+    _check(st, "fa_backward_dkdv")
+    return dk, dv
+
+
+def backward_dq(q, k, v, do, lse, delta, causal=False, scale=None, dq=None):
+    B, H, n_q, n_k, d = _check_qkv(q, k, v)
+    dq = torch.empty_like(q) if dq is None else dq
+    st = lib().fa_backward_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(delta),
+                              _ptr(dq), B, H, n_q, n_k, d, _scale(scale, d), int(bool(causal)),
+                              _DTYPES[q.dtype], _stream(q.device))
+    _check(st, "fa_backward_dq")
+    return dq

@@ -1,0 +1,178 @@
+// C ABI of the exact-attention library: argument validation, dispatch to the
+// gfx950 kernels, status strings.  Every check runs on the host before any
+// HIP call, so invalid arguments never launch anything and never touch the
+// outputs.
+#include "fa.h"
+#include "fa_internal.hpp"
+
+#include <climits>
+#include <cmath>
+#include <cstdint>
+
+namespace {
+
+constexpr int kVersion = 1 * 10000 + 0 * 100 + 0;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_sizes(int B, int H, int n_q, int n_k, int d, int dtype) {
+  if (B < 1 || H < 1 || n_q < 1 || n_k < 1) return FA_ERR_INVALID_ARG;
+  if ((long long)B * (long long)H > INT_MAX) return FA_ERR_INVALID_ARG;
+  // Workgroups per launch: at most ceil(n / 32) per (batch, head).
+  const long long tiles = ((long long)(n_q > n_k ? n_q : n_k) + 31) / 32;
+  if (tiles * (long long)B * (long long)H > INT_MAX) return FA_ERR_INVALID_ARG;
+  if (dtype != FA_DTYPE_FP32 && dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
+  if (d != 32 && d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  return FA_OK;
+}
+
+int check_scale_causal(float scale, int causal) {
+  if (!std::isfinite(scale) || scale < 0.f) return FA_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+  return FA_OK;
+}
+
+int check_tensor(const void* p) {
+  if (p == nullptr) return FA_ERR_INVALID_ARG;
+  if (!aligned(p, 16)) return FA_ERR_ALIGNMENT;
+  return FA_OK;
+}
+
+int check_rowvec(const float* p) {
+  if (p == nullptr) return FA_ERR_INVALID_ARG;
+  if (!aligned(p, 4)) return FA_ERR_ALIGNMENT;
+  return FA_OK;
+}
+
+// First nonzero status of a list of checks.
+template <typename... T>
+int first_error(T... s) {
+  int r = FA_OK;
+  ((r = (r != FA_OK ? r : s)), ...);
+  return r;
+}
+
+size_t delta_bytes(int B, int H, int n_q) {
+  const size_t raw = (size_t)B * (size_t)H * (size_t)n_q * sizeof(float);
+  return (raw + 255) / 256 * 256;
+}
+
+fa::BwdArgs make_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                     const float* lse, float* delta, void* dq, void* dk, void* dv, int B, int H,
+                     int n_q, int n_k, float scale) {
+  fa::BwdArgs a;
+  a.q = q; a.k = k; a.v = v; a.o = o; a.dO = dO; a.lse = lse; a.delta = delta;
+  a.dq = dq; a.dk = dk; a.dv = dv;
+  a.BH = B * H; a.n_q = n_q; a.n_k = n_k;
+  a.scale = scale;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  return a;
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+int fa_version(void) { return kVersion; }
+
+const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "ok";
+    case FA_ERR_INVALID_ARG: return "invalid argument";
+    case FA_ERR_UNSUPPORTED: return "unsupported head width or dtype";
+    case FA_ERR_WORKSPACE: return "workspace missing or too small";
+    case FA_ERR_LAUNCH: return "kernel launch failed";
+    case FA_ERR_ALIGNMENT: return "tensor pointer misaligned";
+    default: return "unknown status";
+  }
+}
+
+int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+               int n_q, int n_k, int d, float scale, int causal, int dtype, void* stream) {
+  int st = first_error(check_sizes(B, H, n_q, n_k, d, dtype), check_scale_causal(scale, causal),
+                       check_tensor(q), check_tensor(k), check_tensor(v), check_tensor(o),
+                       check_rowvec(lse));
+  if (st != FA_OK) return st;
+  fa::FwdArgs a;
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+  a.BH = B * H; a.n_q = n_q; a.n_k = n_k;
+  a.scale = scale;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return status_of(dtype == FA_DTYPE_BF16 ? fa::launch_fwd_bf16(a, d, causal != 0, s)
+                                          : fa::launch_fwd_f32(a, d, causal != 0, s));
+}
+
+size_t fa_backward_workspace_size(int B, int H, int n_q, int n_k, int d, int dtype) {
+  if (check_sizes(B, H, n_q, n_k, d, dtype) != FA_OK) return 0;
+  return delta_bytes(B, H, n_q);
+}
+
+int fa_backward_preprocess(const void* o, const void* dO, float* delta, int B, int H, int n_q,
+                           int d, int dtype, void* stream) {
+  int st = first_error(check_sizes(B, H, n_q, 1, d, dtype), check_tensor(o), check_tensor(dO),
+                       check_rowvec(delta));
+  if (st != FA_OK) return st;
+  fa::BwdArgs a = make_bwd(nullptr, nullptr, nullptr, o, dO, nullptr, delta, nullptr, nullptr,
+                           nullptr, B, H, n_q, 1, 0.f);
+  return status_of(fa::launch_bwd_preprocess(a, d, dtype == FA_DTYPE_BF16,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+int fa_backward_dkdv(const void* q, const void* k, const void* v, const void* dO,
+                     const float* lse, const float* delta, void* dk, void* dv, int B, int H,
+                     int n_q, int n_k, int d, float scale, int causal, int dtype, void* stream) {
+  int st = first_error(check_sizes(B, H, n_q, n_k, d, dtype), check_scale_causal(scale, causal),
+                       check_tensor(q), check_tensor(k), check_tensor(v), check_tensor(dO),
+                       check_rowvec(lse), check_rowvec(delta), check_tensor(dk),
+                       check_tensor(dv));
+  if (st != FA_OK) return st;
+  fa::BwdArgs a = make_bwd(q, k, v, nullptr, dO, lse, const_cast<float*>(delta), nullptr, dk, dv,
+                           B, H, n_q, n_k, scale);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return status_of(dtype == FA_DTYPE_BF16 ? fa::launch_bwd_dkdv_bf16(a, d, causal != 0, s)
+                                          : fa::launch_bwd_dkdv_f32(a, d, causal != 0, s));
+}
+
+int fa_backward_dq(const void* q, const void* k, const void* v, const void* dO, const float* lse,
+                   const float* delta, void* dq, int B, int H, int n_q, int n_k, int d,
+                   float scale, int causal, int dtype, void* stream) {
+  int st = first_error(check_sizes(B, H, n_q, n_k, d, dtype), check_scale_causal(scale, causal),
+                       check_tensor(q), check_tensor(k), check_tensor(v), check_tensor(dO),
+                       check_rowvec(lse), check_rowvec(delta), check_tensor(dq));
+  if (st != FA_OK) return st;
+  fa::BwdArgs a = make_bwd(q, k, v, nullptr, dO, lse, const_cast<float*>(delta), dq, nullptr,
+                           nullptr, B, H, n_q, n_k, scale);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return status_of(dtype == FA_DTYPE_BF16 ? fa::launch_bwd_dq_bf16(a, d, causal != 0, s)
+                                          : fa::launch_bwd_dq_f32(a, d, causal != 0, s));
+}
+
+int fa_backward(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                const float* lse, void* dq, void* dk, void* dv, void* workspace,
+                size_t workspace_bytes, int B, int H, int n_q, int n_k, int d, float scale,
+                int causal, int dtype, void* stream) {
+  int st = first_error(check_sizes(B, H, n_q, n_k, d, dtype), check_scale_causal(scale, causal),
+                       check_tensor(q), check_tensor(k), check_tensor(v), check_tensor(o),
+                       check_tensor(dO), check_rowvec(lse), check_tensor(dq), check_tensor(dk),
+                       check_tensor(dv));
+  if (st != FA_OK) return st;
+  if (workspace == nullptr || workspace_bytes < delta_bytes(B, H, n_q)) return FA_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return FA_ERR_ALIGNMENT;
+  float* delta = static_cast<float*>(workspace);
+  fa::BwdArgs a = make_bwd(q, k, v, o, dO, lse, delta, dq, dk, dv, B, H, n_q, n_k, scale);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool bf16 = dtype == FA_DTYPE_BF16;
+  hipError_t e = fa::launch_bwd_preprocess(a, d, bf16, s);
+  if (e != hipSuccess) return FA_ERR_LAUNCH;
+  e = bf16 ? fa::launch_bwd_dkdv_bf16(a, d, causal != 0, s)
+           : fa::launch_bwd_dkdv_f32(a, d, causal != 0, s);
+  if (e != hipSuccess) return FA_ERR_LAUNCH;
+  e = bf16 ? fa::launch_bwd_dq_bf16(a, d, causal != 0, s)
+           : fa::launch_bwd_dq_f32(a, d, causal != 0, s);
+  return status_of(e);
+}
+
+}  // extern "C"

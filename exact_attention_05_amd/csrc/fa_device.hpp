@@ -1,0 +1,93 @@
+// Device-side building blocks for the gfx950 (CDNA4) attention kernels:
+// vector types, the matrix-core (MFMA) operations used, the LDS transpose
+// read, and small numeric helpers.
+//
+// Matrix-core lane layouts (wave64), as used throughout:
+//
+//  v_mfma_f32_32x32x16_bf16  C[32x32] += A[32x16] * B[16x32]
+//    A: lane l holds row (l % 32), k = 8*(l / 32) + 0..7     (8 x bf16)
+//    B: lane l holds col (l % 32), k = 8*(l / 32) + 0..7     (8 x bf16)
+//    C: lane l, element i holds row 8*(i/4) + 4*(l/32) + (i%4), col (l % 32)
+//
+//  v_mfma_f32_32x32x2_f32    C[32x32] += A[32x2] * B[2x32]
+//    A: lane l holds row (l % 32), k = l / 32;  B: col (l % 32), k = l / 32
+//    C: as above.
+//
+//  ds_read_b64_tr_b16: within each group of 16 lanes, lane 4r+j supplies the
+//    address of 4 consecutive 16-bit values = row r, columns 4j..4j+3 of a
+//    4 x 16 tile; lane i of the group receives column i (rows 0..3).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define FA_LDS __attribute__((address_space(3)))
+
+__device__ __forceinline__ f32x16 mfma_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 mfma_f32(float a, float b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+// `p` must point into LDS (a __shared__ array); it is converted to the LDS
+// address space for the instruction.
+__device__ __forceinline__ bf16x4 lds_read_tr16(const __bf16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((FA_LDS bf16x4*)(const_cast<__bf16*>(p)));
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Value from the lane 32 positions away (the other half of the wave).
+__device__ __forceinline__ float swap_halves(float x) {
+  return __shfl_xor(x, 32, 64);
+}
+
+// Round-to-nearest-even float -> bf16 pair.
+__device__ __forceinline__ bf16x2 to_bf16x2(float a, float b) {
+  bf16x2 r;
+  r[0] = (__bf16)a;
+  r[1] = (__bf16)b;
+  return r;
+}
+
+__device__ __forceinline__ bf16x8 to_bf16x8(const float* x) {
+  bf16x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = (__bf16)x[i];
+  return r;
+}
+
+template <typename T, typename U>
+__device__ __forceinline__ T bit_cast(const U& u) {
+  static_assert(sizeof(T) == sizeof(U), "size mismatch");
+  return __builtin_bit_cast(T, u);
+}
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kXcds = 8;  // MI355X: 8 accelerator complex dies, each with its own L2
+
+// Map a linear workgroup id to a work index so that consecutive work indices
+// land on the same XCD (workgroups are dispatched round-robin over the XCDs).
+// Work indices [x*per, (x+1)*per) run on XCD x.  Falls back to the identity
+// when the grid does not split evenly.
+__device__ __forceinline__ int xcd_remap(int bid, int total) {
+  if (total % kXcds != 0) return bid;
+  const int per = total / kXcds;
+  return (bid % kXcds) * per + bid / kXcds;
+}
+
+}  // namespace fa

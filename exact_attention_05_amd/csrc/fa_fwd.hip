@@ -1,0 +1,472 @@
+// Forward pass of exact attention on gfx950: O = softmax(scale Q K^T [+ M]) V
+// and the per-row natural-log LSE, one key block at a time with an online
+// softmax ("Attention Mechanism: Revolusi Representasi Sequence", section 13,
+// running max m and running sum l; the old output is rescaled by
+// exp(m_old - m_new) and normalised once at the end).  No score or
+// probability block ever leaves the chip.
+//
+// bf16 kernel (the hot path)
+// --------------------------
+// A workgroup is 4 waves (one per SIMD) and owns 256 consecutive query rows
+// of one (batch, head); each wave owns 64 of them as two 32-row blocks.  Key
+// and value blocks of 64 rows stream through double-buffered LDS: the global
+// loads of block t+1 are in flight while block t is computed, and one
+// barrier per block separates the two buffers.
+//
+// The wave computes the transposed score tile S^T = K Q^T on the
+// 32x32x16 bf16 matrix cores, with K read from LDS as the A operand and Q
+// held in registers as the B operand for the whole pass.  In the S^T
+// accumulator layout a lane holds one query column and 16 keys, so a row
+// maximum needs only the lane's own values plus one swap with the other half
+// of the wave, and the row sum needs no cross-lane step until the end.
+// The probabilities are rounded to bf16 and used directly, from registers,
+// as the B operand of O^T += V^T P^T; the V^T operand comes from LDS through
+// the transposing read ds_read_b64_tr_b16.  Exponentials are base 2 with
+// scale * log2(e) folded into one fused multiply-add.
+//
+// Grid: one workgroup per (query tile, batch*head), remapped so that the
+// workgroups of one head run on the same XCD and share its L2; with the
+// causal mask the longest query tiles are issued first.
+//
+// fp32 kernel
+// -----------
+// Same dataflow with float32 operands on the 32x32x2 f32 matrix cores,
+// 4 waves x 32 query rows and 32-key blocks; probabilities stay in fp32.
+#include "fa_internal.hpp"
+#include "fa_device.hpp"
+
+#include <cmath>
+
+namespace fa {
+namespace {
+
+template <int D>
+struct Bf16FwdCfg {
+  static constexpr int kWaves = 4;
+  static constexpr int kThreads = kWaves * 64;
+  static constexpr int kQB = 2;                    // 32-row query blocks per wave
+  static constexpr int kBM = kWaves * kQB * 32;    // query rows per workgroup
+  static constexpr int kBN = 64;                   // keys per block
+  static constexpr int kKB = kBN / 32;             // 32-key sub-blocks
+  static constexpr int kDC = D / 16;               // 16-wide chunks of the head dim
+  static constexpr int kDB = D / 32;               // 32-row blocks of O^T
+  static constexpr int kKStride = D + 8;           // LDS row pitch of K (elements)
+  static constexpr int kVStride = D + 16;          // LDS row pitch of V (elements)
+  static constexpr int kChunks = D / 8;            // 16-byte chunks per row
+  static constexpr int kLoads = kBN * kChunks / kThreads;
+  static_assert(kLoads * kThreads == kBN * kChunks, "tile load split");
+};
+
+// Online-softmax update of one 32-query block held as S^T fragments
+// s[kb] (kb = 32-key sub-block).  Turns s into unnormalised probabilities
+// exp2(scale_log2 * s - m_new), updates the running max m and the lane's
+// partial running sum l, and returns the rescale factor for the old output.
+// With MASK, hidden entries (hide bit set) are left out of the max and get
+// probability 0 (this also covers scale == 0, where -inf * 0 would be NaN).
+template <int KB, bool MASK>
+__device__ __forceinline__ float softmax_block(f32x16 (&s)[KB], float& m, float& l,
+                                               float scale_log2, const uint32_t* hide) {
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (MASK && ((hide[kb] >> i) & 1u)) continue;
+      mx = fmaxf(mx, s[kb][i]);
+    }
+  mx = fmaxf(mx, swap_halves(mx));
+  const float mt = (mx == -INFINITY) ? -INFINITY : mx * scale_log2;
+  const float m_new = fmaxf(m, mt);
+  const float ref = (m_new == -INFINITY) ? 0.f : m_new;
+  const float alpha = fast_exp2(m - ref);
+  float rs = 0.f;
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float p = fast_exp2(fmaf(s[kb][i], scale_log2, -ref));
+      if (MASK && ((hide[kb] >> i) & 1u)) p = 0.f;
+      s[kb][i] = p;
+      rs += p;
+    }
+  l = alpha * l + rs;
+  m = m_new;
+  return alpha;
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdArgs a, int n_qtiles) {
+  using C = Bf16FwdCfg<D>;
+  __shared__ __attribute__((aligned(16))) __bf16 sk[2][C::kBN * C::kKStride];
+  __shared__ __attribute__((aligned(16))) __bf16 sv[2][C::kBN * C::kVStride];
+
+  const int work = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = work / n_qtiles;
+  int qt = work - bh * n_qtiles;
+  if (CAUSAL) qt = n_qtiles - 1 - qt;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+  const int q0 = qt * C::kBM;
+  const int qw = q0 + wave * (C::kQB * 32);
+  const int n_q = a.n_q, n_k = a.n_k;
+
+  const __bf16* qp = static_cast<const __bf16*>(a.q) + (size_t)bh * n_q * D;
+  const __bf16* kp = static_cast<const __bf16*>(a.k) + (size_t)bh * n_k * D;
+  const __bf16* vp = static_cast<const __bf16*>(a.v) + (size_t)bh * n_k * D;
+
+  // Q fragments: B operand of S^T = K Q^T, kept for the whole pass.
+  bf16x8 qf[C::kQB][C::kDC];
+#pragma unroll
+  for (int qb = 0; qb < C::kQB; ++qb) {
+    const int row = qw + qb * 32 + l32;
+#pragma unroll
+    for (int c = 0; c < C::kDC; ++c) {
+      if (row < n_q)
+        qf[qb][c] = *reinterpret_cast<const bf16x8*>(qp + (size_t)row * D + 16 * c + 8 * hi);
+      else
+        qf[qb][c] = bf16x8{};
+    }
+  }
+
+  const int q_end = min(n_q, q0 + C::kBM);
+  const int k_end = CAUSAL ? min(n_k, q_end) : n_k;
+  const int ntiles = (k_end + C::kBN - 1) / C::kBN;
+
+  u32x4 kst[C::kLoads], vst[C::kLoads];
+  auto gload = [&](int t) {
+#pragma unroll
+    for (int i = 0; i < C::kLoads; ++i) {
+      const int idx = tid + i * C::kThreads;
+      const int row = idx / C::kChunks;
+      const int ch = idx - row * C::kChunks;
+      const int key = t * C::kBN + row;
+      if (key < n_k) {
+        kst[i] = *reinterpret_cast<const u32x4*>(kp + (size_t)key * D + ch * 8);
+        vst[i] = *reinterpret_cast<const u32x4*>(vp + (size_t)key * D + ch * 8);
+      } else {
+        kst[i] = u32x4{0u, 0u, 0u, 0u};
+        vst[i] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  };
+  auto swrite = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < C::kLoads; ++i) {
+      const int idx = tid + i * C::kThreads;
+      const int row = idx / C::kChunks;
+      const int ch = idx - row * C::kChunks;
+      *reinterpret_cast<u32x4*>(&sk[buf][row * C::kKStride + ch * 8]) = kst[i];
+      *reinterpret_cast<u32x4*>(&sv[buf][row * C::kVStride + ch * 8]) = vst[i];
+    }
+  };
+
+  f32x16 oacc[C::kDB][C::kQB];
+#pragma unroll
+  for (int db = 0; db < C::kDB; ++db)
+#pragma unroll
+    for (int qb = 0; qb < C::kQB; ++qb) oacc[db][qb] = f32x16{};
+  float m[C::kQB], l[C::kQB];
+#pragma unroll
+  for (int qb = 0; qb < C::kQB; ++qb) { m[qb] = -INFINITY; l[qb] = 0.f; }
+
+  // Lane coordinates of the transposing V read (see fa_device.hpp).
+  const int grp = lane >> 4;
+  const int tr_row = (lane & 15) >> 2;
+  const int tr_col = 16 * (grp & 1) + 4 * (lane & 3);
+
+  gload(0);
+  swrite(0);
+  __syncthreads();
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int buf = t & 1;
+    if (t + 1 < ntiles) gload(t + 1);
+    const int k0 = t * C::kBN;
+
+    // S^T = K Q^T for 64 keys x 64 queries.
+    f32x16 s[C::kQB][C::kKB];
+#pragma unroll
+    for (int qb = 0; qb < C::kQB; ++qb)
+#pragma unroll
+      for (int kb = 0; kb < C::kKB; ++kb) s[qb][kb] = f32x16{};
+#pragma unroll
+    for (int c = 0; c < C::kDC; ++c) {
+#pragma unroll
+      for (int kb = 0; kb < C::kKB; ++kb) {
+        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(
+            &sk[buf][(kb * 32 + l32) * C::kKStride + 16 * c + 8 * hi]);
+#pragma unroll
+        for (int qb = 0; qb < C::kQB; ++qb) s[qb][kb] = mfma_bf16(ka, qf[qb][c], s[qb][kb]);
+      }
+    }
+
+    const bool need_mask = (k0 + C::kBN > n_k) || (CAUSAL && k0 + C::kBN - 1 > qw);
+#pragma unroll
+    for (int qb = 0; qb < C::kQB; ++qb) {
+      float alpha;
+      if (need_mask) {
+        uint32_t hide[C::kKB];
+        const int qi = qw + qb * 32 + l32;
+#pragma unroll
+        for (int kb = 0; kb < C::kKB; ++kb) {
+          uint32_t bits = 0;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = k0 + kb * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
+            const bool h = key >= n_k || (CAUSAL && key > qi);
+            bits |= (h ? 1u : 0u) << i;
+          }
+          hide[kb] = bits;
+        }
+        alpha = softmax_block<C::kKB, true>(s[qb], m[qb], l[qb], a.scale_log2, hide);
+      } else {
+        alpha = softmax_block<C::kKB, false>(s[qb], m[qb], l[qb], a.scale_log2, nullptr);
+      }
+#pragma unroll
+      for (int db = 0; db < C::kDB; ++db) oacc[db][qb] *= alpha;
+    }
+
+    // O^T += V^T P^T, 16 keys per matrix-core step.
+#pragma unroll
+    for (int kb = 0; kb < C::kKB; ++kb) {
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2) {
+        bf16x8 pb[C::kQB];
+#pragma unroll
+        for (int qb = 0; qb < C::kQB; ++qb) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pb[qb][e] = (__bf16)s[qb][kb][8 * c2 + e];
+        }
+        const int key_a = kb * 32 + 16 * c2 + 4 * hi + tr_row;
+#pragma unroll
+        for (int db = 0; db < C::kDB; ++db) {
+          const int col = 32 * db + tr_col;
+          const bf16x4 va = lds_read_tr16(&sv[buf][key_a * C::kVStride + col]);
+          const bf16x4 vb = lds_read_tr16(&sv[buf][(key_a + 8) * C::kVStride + col]);
+          const bf16x8 vop = {va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]};
+#pragma unroll
+          for (int qb = 0; qb < C::kQB; ++qb) oacc[db][qb] = mfma_bf16(vop, pb[qb], oacc[db][qb]);
+        }
+      }
+    }
+
+    if (t + 1 < ntiles) swrite(buf ^ 1);
+    __syncthreads();
+  }
+
+  // Epilogue: normalise, store O (bf16) and LSE (natural log).
+#pragma unroll
+  for (int qb = 0; qb < C::kQB; ++qb) {
+    const float lt = l[qb] + swap_halves(l[qb]);
+    const float inv = 1.f / lt;
+    const int qi = qw + qb * 32 + l32;
+    if (qi < n_q) {
+      __bf16* op = static_cast<__bf16*>(a.o) + ((size_t)bh * n_q + qi) * D;
+#pragma unroll
+      for (int db = 0; db < C::kDB; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          bf16x4 r;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) r[e] = (__bf16)(oacc[db][qb][4 * g4 + e] * inv);
+          *reinterpret_cast<bf16x4*>(op + 32 * db + 8 * g4 + 4 * hi) = r;
+        }
+      if (hi == 0) a.lse[(size_t)bh * n_q + qi] = (m[qb] + fast_log2(lt)) * kLn2;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ fp32
+
+template <int D>
+struct F32FwdCfg {
+  static constexpr int kWaves = 4;
+  static constexpr int kThreads = kWaves * 64;
+  static constexpr int kBM = kWaves * 32;          // one 32-row block per wave
+  static constexpr int kBN = 32;
+  static constexpr int kDB = D / 32;
+  static constexpr int kKStride = D + 2;           // floats
+  static constexpr int kVStride = D + 8;
+  static constexpr int kChunks = D / 4;            // 16-byte chunks per row
+  static constexpr int kLoads = kBN * kChunks / kThreads;
+  static_assert(kLoads * kThreads == kBN * kChunks, "tile load split");
+};
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256) void fwd_f32_kernel(FwdArgs a, int n_qtiles) {
+  using C = F32FwdCfg<D>;
+  __shared__ __attribute__((aligned(16))) float sk[2][C::kBN * C::kKStride];
+  __shared__ __attribute__((aligned(16))) float sv[2][C::kBN * C::kVStride];
+
+  const int work = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = work / n_qtiles;
+  int qt = work - bh * n_qtiles;
+  if (CAUSAL) qt = n_qtiles - 1 - qt;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+  const int q0 = qt * C::kBM;
+  const int qw = q0 + wave * 32;
+  const int n_q = a.n_q, n_k = a.n_k;
+
+  const float* qp = static_cast<const float*>(a.q) + (size_t)bh * n_q * D;
+  const float* kp = static_cast<const float*>(a.k) + (size_t)bh * n_k * D;
+  const float* vp = static_cast<const float*>(a.v) + (size_t)bh * n_k * D;
+
+  const int qi = qw + l32;
+  float qf[D / 2];
+#pragma unroll
+  for (int c = 0; c < D / 2; ++c) qf[c] = (qi < n_q) ? qp[(size_t)qi * D + 2 * c + hi] : 0.f;
+
+  const int q_end = min(n_q, q0 + C::kBM);
+  const int k_end = CAUSAL ? min(n_k, q_end) : n_k;
+  const int ntiles = (k_end + C::kBN - 1) / C::kBN;
+
+  // The 16-byte row chunks are stored unaligned into the padded K rows
+  // (pitch D + 2), so K goes through LDS as float2 pairs.
+  f32x4 kst[C::kLoads], vst[C::kLoads];
+  auto gload = [&](int t) {
+#pragma unroll
+    for (int i = 0; i < C::kLoads; ++i) {
+      const int idx = tid + i * C::kThreads;
+      const int row = idx / C::kChunks;
+      const int ch = idx - row * C::kChunks;
+      const int key = t * C::kBN + row;
+      if (key < n_k) {
+        kst[i] = *reinterpret_cast<const f32x4*>(kp + (size_t)key * D + ch * 4);
+        vst[i] = *reinterpret_cast<const f32x4*>(vp + (size_t)key * D + ch * 4);
+      } else {
+        kst[i] = f32x4{};
+        vst[i] = f32x4{};
+      }
+    }
+  };
+  auto swrite = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < C::kLoads; ++i) {
+      const int idx = tid + i * C::kThreads;
+      const int row = idx / C::kChunks;
+      const int ch = idx - row * C::kChunks;
+      float* kd = &sk[buf][row * C::kKStride + ch * 4];
+      kd[0] = kst[i][0]; kd[1] = kst[i][1]; kd[2] = kst[i][2]; kd[3] = kst[i][3];
+      *reinterpret_cast<f32x4*>(&sv[buf][row * C::kVStride + ch * 4]) = vst[i];
+    }
+  };
+
+  f32x16 oacc[C::kDB];
+#pragma unroll
+  for (int db = 0; db < C::kDB; ++db) oacc[db] = f32x16{};
+  float m = -INFINITY, l = 0.f;
+
+  gload(0);
+  swrite(0);
+  __syncthreads();
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int buf = t & 1;
+    if (t + 1 < ntiles) gload(t + 1);
+    const int k0 = t * C::kBN;
+
+    f32x16 s[1];
+    s[0] = f32x16{};
+#pragma unroll
+    for (int c = 0; c < D / 2; ++c)
+      s[0] = mfma_f32(sk[buf][l32 * C::kKStride + 2 * c + hi], qf[c], s[0]);
+
+    const bool need_mask = (k0 + C::kBN > n_k) || (CAUSAL && k0 + C::kBN - 1 > qw);
+    float alpha;
+    if (need_mask) {
+      uint32_t bits = 0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = k0 + 8 * (i >> 2) + 4 * hi + (i & 3);
+        const bool h = key >= n_k || (CAUSAL && key > qi);
+        bits |= (h ? 1u : 0u) << i;
+      }
+      alpha = softmax_block<1, true>(s, m, l, a.scale_log2, &bits);
+    } else {
+      alpha = softmax_block<1, false>(s, m, l, a.scale_log2, nullptr);
+    }
+#pragma unroll
+    for (int db = 0; db < C::kDB; ++db) oacc[db] *= alpha;
+
+    // O^T += V^T P^T: accumulator element i of this lane is the probability
+    // of key 8*(i/4) + 4*hi + (i%4), which is exactly the B operand slot.
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int key = 8 * (i >> 2) + 4 * hi + (i & 3);
+#pragma unroll
+      for (int db = 0; db < C::kDB; ++db)
+        oacc[db] = mfma_f32(sv[buf][key * C::kVStride + 32 * db + l32], s[0][i], oacc[db]);
+    }
+
+    if (t + 1 < ntiles) swrite(buf ^ 1);
+    __syncthreads();
+  }
+
+  const float lt = l + swap_halves(l);
+  const float inv = 1.f / lt;
+  if (qi < n_q) {
+    float* op = static_cast<float*>(a.o) + ((size_t)bh * n_q + qi) * D;
+#pragma unroll
+    for (int db = 0; db < C::kDB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        f32x4 r;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r[e] = oacc[db][4 * g4 + e] * inv;
+        *reinterpret_cast<f32x4*>(op + 32 * db + 8 * g4 + 4 * hi) = r;
+      }
+    if (hi == 0) a.lse[(size_t)bh * n_q + qi] = (m + fast_log2(lt)) * kLn2;
+  }
+}
+
+template <typename Kernel>
+hipError_t launch(Kernel kernel, int grid, const FwdArgs& a, int n_qtiles, hipStream_t stream) {
+  FwdArgs args = a;
+  int nq = n_qtiles;
+  void* params[] = {&args, &nq};
+  return hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3(grid), dim3(256), params, 0,
+                         stream);
+}
+
+template <int D, bool CAUSAL>
+hipError_t fwd_bf16_t(const FwdArgs& a, hipStream_t stream) {
+  const int n_qtiles = (a.n_q + Bf16FwdCfg<D>::kBM - 1) / Bf16FwdCfg<D>::kBM;
+  return launch(fwd_bf16_kernel<D, CAUSAL>, n_qtiles * a.BH, a, n_qtiles, stream);
+}
+
+template <int D, bool CAUSAL>
+hipError_t fwd_f32_t(const FwdArgs& a, hipStream_t stream) {
+  const int n_qtiles = (a.n_q + F32FwdCfg<D>::kBM - 1) / F32FwdCfg<D>::kBM;
+  return launch(fwd_f32_kernel<D, CAUSAL>, n_qtiles * a.BH, a, n_qtiles, stream);
+}
+
+}  // namespace
+
+hipError_t launch_fwd_bf16(const FwdArgs& a, int d, bool causal, hipStream_t stream) {
+  switch (d) {
+    case 32: return causal ? fwd_bf16_t<32, true>(a, stream) : fwd_bf16_t<32, false>(a, stream);
+    case 64: return causal ? fwd_bf16_t<64, true>(a, stream) : fwd_bf16_t<64, false>(a, stream);
+    case 128: return causal ? fwd_bf16_t<128, true>(a, stream) : fwd_bf16_t<128, false>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_fwd_f32(const FwdArgs& a, int d, bool causal, hipStream_t stream) {
+  switch (d) {
+    case 32: return causal ? fwd_f32_t<32, true>(a, stream) : fwd_f32_t<32, false>(a, stream);
+    case 64: return causal ? fwd_f32_t<64, true>(a, stream) : fwd_f32_t<64, false>(a, stream);
+    case 128: return causal ? fwd_f32_t<128, true>(a, stream) : fwd_f32_t<128, false>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace fa

@@ -1,0 +1,54 @@
+// Internal kernel parameters and launchers shared by the C ABI and the
+// kernel translation units.  Not part of the public interface.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace fa {
+
+// Arguments of one forward launch.  All tensors contiguous (B,H,n,d).
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int BH;           // B * H
+  int n_q;
+  int n_k;
+  float scale;      // softmax scale on q . k
+  float scale_log2; // scale * log2(e): scores are exponentiated base 2
+};
+
+// Arguments of the backward stages.
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dO;
+  const float* lse;
+  float* delta;     // (B,H,n_q) float32 row sums of dO * O
+  void* dq;
+  void* dk;
+  void* dv;
+  int BH;
+  int n_q;
+  int n_k;
+  float scale;
+  float scale_log2;
+};
+
+// Each launcher enqueues its kernel(s) on `stream` and returns the HIP status
+// of the launch.  Shapes were validated by the caller.
+hipError_t launch_fwd_bf16(const FwdArgs& a, int d, bool causal, hipStream_t stream);
+hipError_t launch_fwd_f32(const FwdArgs& a, int d, bool causal, hipStream_t stream);
+
+hipError_t launch_bwd_preprocess(const BwdArgs& a, int d, bool bf16, hipStream_t stream);
+hipError_t launch_bwd_dkdv_bf16(const BwdArgs& a, int d, bool causal, hipStream_t stream);
+hipError_t launch_bwd_dq_bf16(const BwdArgs& a, int d, bool causal, hipStream_t stream);
+hipError_t launch_bwd_dkdv_f32(const BwdArgs& a, int d, bool causal, hipStream_t stream);
+hipError_t launch_bwd_dq_f32(const BwdArgs& a, int d, bool causal, hipStream_t stream);
+
+}  // namespace fa

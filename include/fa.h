@@ -1,0 +1,136 @@
+/*
+ * fa.h -- C ABI of the exact-attention library for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (the definitions this library implements):
+ *
+ *   O = softmax(scale * Q K^T [+ M]) V,  row by row over the keys,
+ *
+ * the scaled dot-product attention of "Attention Mechanism: Revolusi
+ * Representasi Sequence", section 3 ("Scaled Dot-Product Attention: Formula
+ * Inti"): Q is (n_q, d), K is (n_k, d), V is (n_k, d) (value width equal to
+ * the key width).  With causal = 1 the mask M of section 4.4 ("Causal /
+ * Masked Attention") hides key j from query i exactly when j > i, counted
+ * from the first row and first key (top-left alignment when n_q != n_k), so
+ * every query sees at least key 0.
+ *
+ * The forward pass streams key/value blocks through on-chip memory with an
+ * online softmax (running row maximum and running row sum, "Attention
+ * Mechanism" section 13, with the exp(m_old - m_new) factor on the old output
+ * that the printed update leaves out), so the n_q x n_k score matrix is never
+ * written to device memory ("Apa itu FlashAttention", section "Cara kerja
+ * teknik Tiling dan Recomputation"; "Flash Attention Nedir?", sections
+ * "Tiling" and "Online Softmax").  It returns O and the per-row natural-log
+ * log-sum-exp LSE_i = ln sum_j exp(scale * q_i . k_j) over visible keys.
+ *
+ * The backward pass recomputes the probabilities block by block from Q, K and
+ * the saved LSE instead of storing them ("Apa itu FlashAttention" and "Flash
+ * Attention Nedir?", sections on recomputation), and applies the chain rule
+ * through O = P V and P = softmax(S):
+ *   D_i = sum_c dO_ic O_ic,  P_ij = exp(scale q_i . k_j - LSE_i),
+ *   dV = P^T dO,  dP = dO V^T,  dS = P o (dP - D),
+ *   dQ = scale dS K,  dK = scale dS^T Q.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Layout   q, o, dO, dq: contiguous (B, H, n_q, d); k, v, dk, dv: contiguous
+ *          (B, H, n_k, d); lse and delta: contiguous (B, H, n_q) float32.
+ *          Rows are row-major with d innermost.
+ * dtype    FA_DTYPE_BF16: q, k, v, o, dO, dq, dk, dv hold bfloat16 and all
+ *          accumulation is float32; results are rounded to nearest-even.
+ *          FA_DTYPE_FP32: those tensors hold float32 and every product runs
+ *          on float32 matrix cores.  lse and delta are always float32.
+ * Pointers All tensor pointers are device pointers.  q, k, v, o, dO, dq, dk,
+ *          dv must be 16-byte aligned; lse and delta 4-byte aligned.
+ * Ownership The caller owns every buffer.  The library allocates and frees
+ *          nothing, never synchronises, and does not modify inputs.  Outputs
+ *          are fully overwritten (never accumulated into) and must not alias
+ *          any input; aliasing is undefined.
+ * Stream   Work is enqueued on `stream` (a hipStream_t; NULL = the null
+ *          stream) and the call returns once it is enqueued; results are
+ *          valid after the caller synchronises that stream.  The calls keep
+ *          no state and are safe to make from several threads.
+ * Sizes    B, H, n_q, n_k >= 1; d is 32, 64 or 128; B*H and each of n_q, n_k
+ *          at most 2^31 - 1; scale finite and >= 0; causal 0 or 1.
+ * Errors   Every argument is validated on the host before anything is
+ *          launched; on failure the call returns a nonzero fa_status and
+ *          leaves all outputs untouched.  A failed launch is reported as
+ *          FA_ERR_LAUNCH.  Faults inside a kernel surface as HIP errors at the
+ *          caller's next synchronisation.  Non-finite input values are not
+ *          checked and propagate into the outputs.  No C++ exception crosses
+ *          this interface and nothing is printed.
+ */
+#ifndef EXACT_ATTENTION_FA_H
+#define EXACT_ATTENTION_FA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fa_status {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARG = 1,   /* NULL pointer, size < 1, bad causal, non-finite or negative scale */
+  FA_ERR_UNSUPPORTED = 2,   /* head width d or dtype this build does not provide */
+  FA_ERR_WORKSPACE = 3,     /* backward workspace missing or smaller than required */
+  FA_ERR_LAUNCH = 4,        /* the HIP runtime refused a kernel launch */
+  FA_ERR_ALIGNMENT = 5      /* a tensor pointer is not aligned as required */
+} fa_status;
+
+typedef enum fa_dtype {
+  FA_DTYPE_FP32 = 0,
+  FA_DTYPE_BF16 = 1
+} fa_dtype;
+
+/* Forward pass.  Writes o (B,H,n_q,d; dtype) and lse (B,H,n_q; float32).
+ * One kernel launch on `stream`. */
+int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int H, int n_q, int n_k, int d, float scale, int causal,
+               int dtype, void* stream);
+
+/* Bytes of device workspace fa_backward needs for these sizes (the float32
+ * row sums D, B*H*n_q*4 bytes rounded up to 256).  Returns 0 for invalid or
+ * unsupported sizes. */
+size_t fa_backward_workspace_size(int B, int H, int n_q, int n_k, int d, int dtype);
+
+/* Backward pass from the saved o and lse of fa_forward (same q, k, v, scale,
+ * causal).  Writes dq, dk, dv in dtype.  `workspace` is caller-owned device
+ * memory of at least fa_backward_workspace_size(...) bytes, 256-byte aligned;
+ * its contents on entry do not matter.  Runs the three stages below in order
+ * on `stream`; it is deterministic (no atomics; bitwise repeatable). */
+int fa_backward(const void* q, const void* k, const void* v, const void* o,
+                const void* dO, const float* lse, void* dq, void* dk, void* dv,
+                void* workspace, size_t workspace_bytes,
+                int B, int H, int n_q, int n_k, int d, float scale, int causal,
+                int dtype, void* stream);
+
+/* Backward stage 1: delta_i = sum_c dO_ic * o_ic in float32, (B,H,n_q).
+ * The row term D of the softmax gradient, taken from the saved output. */
+int fa_backward_preprocess(const void* o, const void* dO, float* delta,
+                           int B, int H, int n_q, int d, int dtype, void* stream);
+
+/* Backward stage 2: dk and dv.  One pass over the query blocks for every key
+ * block, recomputing P from lse, with dV = P^T dO and dK = scale dS^T Q. */
+int fa_backward_dkdv(const void* q, const void* k, const void* v, const void* dO,
+                     const float* lse, const float* delta, void* dk, void* dv,
+                     int B, int H, int n_q, int n_k, int d, float scale, int causal,
+                     int dtype, void* stream);
+
+/* Backward stage 3: dq = scale dS K.  One pass over the key blocks for every
+ * query block, recomputing P and dP. */
+int fa_backward_dq(const void* q, const void* k, const void* v, const void* dO,
+                   const float* lse, const float* delta, void* dq,
+                   int B, int H, int n_q, int n_k, int d, float scale, int causal,
+                   int dtype, void* stream);
+
+/* Static text for a status code ("unknown status" for other values). */
+const char* fa_status_string(int status);
+
+/* Library interface version (major * 10000 + minor * 100 + patch). */
+int fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EXACT_ATTENTION_FA_H */

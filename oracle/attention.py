@@ -121,12 +121,13 @@ def attention_fwd(q, k, v, scale: float, causal: bool = False):
     return o, lse
 
 
-def attention_bwd(q, k, v, do, scale: float, causal: bool = False):
+def attention_bwd(q, k, v, do, scale: float, causal: bool = False, intermediates: bool = False):
     """Explicit backward pass from the oracle's own fp64 forward: (dQ, dK, dV).
 
     Uses the materialised P and O (no recomputation shortcut), then the chain
     rule listed in the module docstring.  Hidden positions have P = 0 and so
-    dS = 0.
+    dS = 0.  With ``intermediates=True`` a fourth element, the dict
+    {"p": P, "ds": dS}, is returned as well.
     """
     q = _f64(q)
     k = _f64(k)
@@ -140,6 +141,8 @@ def attention_bwd(q, k, v, do, scale: float, causal: bool = False):
     ds = p * (dp - dsum)
     dq = float(scale) * np.matmul(ds, k)
     dk = float(scale) * np.matmul(np.swapaxes(ds, -1, -2), q)
+    if intermediates:
+        return dq, dk, dv, {"p": p, "ds": ds}
     return dq, dk, dv
 
 

@@ -1,0 +1,129 @@
+"""Host-side checks of the C ABI: the library loads, exports every function
+include/fa.h declares, and rejects invalid arguments before launching
+anything.  Each call here fails validation on the host, so no GPU is needed
+and no kernel runs."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import exact_attention_05_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+# Fake, suitably aligned device addresses: never dereferenced, because every
+# call below fails validation first.
+P = ctypes.c_void_p(0x100000)
+P2 = ctypes.c_void_p(0x200000)
+MIS = ctypes.c_void_p(0x100008)  # 8-byte aligned only
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert {"fa_forward", "fa_backward", "fa_backward_workspace_size", "fa_status_string"} <= set(names)
+    L = fa.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", fa.library_path()], capture_output=True, text=True)
+    exported = set(re.findall(r"\bT (fa_[a-z_]+)\b", out.stdout))
+    assert set(names) <= exported
+
+
+def test_status_strings_cover_every_code():
+    seen = set()
+    for code in range(6):
+        s = fa.status_string(code)
+        assert s and s != "unknown status"
+        seen.add(s)
+    assert len(seen) == 6
+    assert fa.status_string(99) == "unknown status"
+    assert fa.status_string(-1) == "unknown status"
+
+
+def test_version():
+    assert fa.version() >= 10000
+
+
+def fwd(q=P, k=P, v=P, o=P2, lse=P2, B=1, H=1, n_q=8, n_k=8, d=64, scale=0.125, causal=0, dtype=1):
+    return fa.lib().fa_forward(q, k, v, o, lse, B, H, n_q, n_k, d, scale, causal, dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({"q": None}, fa.FA_ERR_INVALID_ARG),
+    ({"k": None}, fa.FA_ERR_INVALID_ARG),
+    ({"v": None}, fa.FA_ERR_INVALID_ARG),
+    ({"o": None}, fa.FA_ERR_INVALID_ARG),
+    ({"lse": None}, fa.FA_ERR_INVALID_ARG),
+    ({"B": 0}, fa.FA_ERR_INVALID_ARG),
+    ({"H": -1}, fa.FA_ERR_INVALID_ARG),
+    ({"n_q": 0}, fa.FA_ERR_INVALID_ARG),
+    ({"n_k": 0}, fa.FA_ERR_INVALID_ARG),
+    ({"d": 48}, fa.FA_ERR_UNSUPPORTED),
+    ({"d": 256}, fa.FA_ERR_UNSUPPORTED),
+    ({"dtype": 7}, fa.FA_ERR_UNSUPPORTED),
+    ({"causal": 2}, fa.FA_ERR_INVALID_ARG),
+    ({"scale": float("nan")}, fa.FA_ERR_INVALID_ARG),
+    ({"scale": float("inf")}, fa.FA_ERR_INVALID_ARG),
+    ({"scale": -0.5}, fa.FA_ERR_INVALID_ARG),
+    ({"q": MIS}, fa.FA_ERR_ALIGNMENT),
+    ({"o": MIS}, fa.FA_ERR_ALIGNMENT),
+    ({"lse": ctypes.c_void_p(0x100002)}, fa.FA_ERR_ALIGNMENT),
+    ({"B": 65536, "H": 65536}, fa.FA_ERR_INVALID_ARG),
+    ({"B": 1 << 20, "H": 64, "n_q": 1 << 20}, fa.FA_ERR_INVALID_ARG),
+])
+def test_forward_rejects_invalid_arguments(kw, code):
+    assert fwd(**kw) == code
+
+
+def test_workspace_size():
+    L = fa.lib()
+    assert L.fa_backward_workspace_size(2, 16, 4096, 4096, 128, 1) == 2 * 16 * 4096 * 4
+    assert L.fa_backward_workspace_size(1, 1, 3, 3, 64, 0) == 256
+    assert L.fa_backward_workspace_size(1, 1, 0, 3, 64, 0) == 0
+    assert L.fa_backward_workspace_size(1, 1, 3, 3, 40, 0) == 0
+
+
+def bwd(ws=P2, ws_bytes=1 << 20, B=1, H=1, n_q=8, n_k=8, d=64, scale=0.125, causal=0, dtype=1,
+        dq=P2, o=P):
+    return fa.lib().fa_backward(P, P, P, o, P, P, dq, P2, P2, ws, ws_bytes, B, H, n_q, n_k, d,
+                                scale, causal, dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({"ws": None}, fa.FA_ERR_WORKSPACE),
+    ({"ws_bytes": 8 * 4 - 1}, fa.FA_ERR_WORKSPACE),
+    ({"ws": ctypes.c_void_p(0x100010)}, fa.FA_ERR_ALIGNMENT),
+    ({"dq": None}, fa.FA_ERR_INVALID_ARG),
+    ({"o": MIS}, fa.FA_ERR_ALIGNMENT),
+    ({"d": 96}, fa.FA_ERR_UNSUPPORTED),
+    ({"causal": -1}, fa.FA_ERR_INVALID_ARG),
+    ({"n_k": 0}, fa.FA_ERR_INVALID_ARG),
+])
+def test_backward_rejects_invalid_arguments(kw, code):
+    assert bwd(**kw) == code
+
+
+def test_stage_entry_points_reject_invalid_arguments():
+    L = fa.lib()
+    assert L.fa_backward_preprocess(P, None, P2, 1, 1, 8, 64, 1, None) == fa.FA_ERR_INVALID_ARG
+    assert L.fa_backward_preprocess(P, P, P2, 1, 1, 8, 40, 1, None) == fa.FA_ERR_UNSUPPORTED
+    assert L.fa_backward_dkdv(P, P, P, P, P2, P2, None, P2, 1, 1, 8, 8, 64, 0.1, 0, 1, None) == fa.FA_ERR_INVALID_ARG
+    assert L.fa_backward_dkdv(P, P, P, P, P2, P2, P2, P2, 1, 1, 8, 8, 64, -0.1, 0, 1, None) == fa.FA_ERR_INVALID_ARG
+    assert L.fa_backward_dq(P, P, P, P, P2, P2, MIS, 1, 1, 8, 8, 64, 0.1, 0, 1, None) == fa.FA_ERR_ALIGNMENT
+    assert L.fa_backward_dq(P, P, P, P, P2, P2, P2, 1, 0, 8, 8, 64, 0.1, 0, 1, None) == fa.FA_ERR_INVALID_ARG
+
+
+def test_binding_validates_shapes_before_calling():
+    import torch
+    q = torch.zeros(1, 1, 8, 64)
+    with pytest.raises(ValueError):
+        fa.forward(q, q, q)  # CPU tensors are refused before any library call

@@ -1,0 +1,121 @@
+"""GPU parity of the recomputation backward pass against the fp64 oracle's
+explicit backward, through the C ABI."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import exact_attention_05_amd as fa
+import oracle
+import workloads
+from parity import RTOL_BF16_TERMS, assert_close, np64, require_gpu, tol_for
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return require_gpu()
+
+
+def gpu_fwd_bwd(dev, q, k, v, do, scale, causal):
+    qd, kd, vd, dod = (t.to(dev) for t in (q, k, v, do))
+    o, lse = fa.forward(qd, kd, vd, causal=causal, scale=scale)
+    dq, dk, dv = fa.backward(qd, kd, vd, o, dod, lse, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return o, lse, dq.cpu(), dk.cpu(), dv.cpu()
+
+
+def check_unit(tag, got, q, k, v, do, scale, causal, tol, rtol=0.0):
+    q64, k64, v64, do64 = np64(q), np64(k), np64(v), np64(do)
+    rq, rk, rv, mid = oracle.attention_bwd(q64, k64, v64, do64, scale, causal, intermediates=True)
+    ads, ap = np.abs(mid["ds"]), np.abs(mid["p"])
+    t = lambda x: np.swapaxes(x, -1, -2)  # noqa: E731
+    mags = (scale * ads @ np.abs(k64), scale * t(ads) @ np.abs(q64), t(ap) @ np.abs(do64))
+    for name, g, r, m in zip(("dQ", "dK", "dV"), got, (rq, rk, rv), mags):
+        assert_close(f"{name} {tag}", g, r, tol, rtol, mag=m)
+
+
+def test_c5_bwd_b2_h16_n4096_d128_causal(dev):
+    w = workloads.c5()
+    _, _, dq, dk, dv = gpu_fwd_bwd(dev, w.q, w.k, w.v, w.do, w.scale, True)
+    # Whole units (b, h) checked element by element against the fp64 oracle.
+    for b, h in ((0, 0), (0, 9), (1, 4), (1, 15)):
+        check_unit(f"c5 unit ({b},{h})", (dq[b, h], dk[b, h], dv[b, h]),
+                   w.q[b, h], w.k[b, h], w.v[b, h], w.do[b, h], w.scale, True, 2e-2)
+
+
+SHAPES = [(1, 1, 1, 1), (1, 2, 17, 17), (2, 1, 63, 65), (1, 1, 65, 63), (1, 2, 129, 129),
+          (1, 1, 257, 300), (1, 1, 300, 257), (1, 1, 5, 600), (1, 1, 600, 5), (1, 1, 1000, 1000)]
+
+
+@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_ragged_shapes(dev, shape, causal, dtype, d):
+    B, H, n_q, n_k = shape
+    q, k, v, do = workloads.random_qkv(2000 + n_q * 7 + n_k + d, B, H, n_q, n_k, d, dtype, with_do=True)
+    scale = 1 / math.sqrt(d)
+    _, _, dq, dk, dv = gpu_fwd_bwd(dev, q, k, v, do, scale, causal)
+    # With n_q >> n_k a key gathers gradient from hundreds of queries: the
+    # terms of dK reach sums near 20, beyond the O(1) scale of the 2e-2 bound.
+    tol = tol_for(dtype) if dtype == torch.bfloat16 else 2e-5
+    rtol = RTOL_BF16_TERMS if dtype == torch.bfloat16 else 0.0
+    check_unit(f"{shape} d{d} {dtype} causal={causal}", (dq, dk, dv), q, k, v, do, scale, causal, tol, rtol)
+
+
+def test_stages_compose_to_backward_bitwise(dev):
+    q, k, v, do = (t.to(dev) for t in workloads.random_qkv(31, 2, 3, 333, 333, 128, torch.bfloat16, with_do=True))
+    for causal in (False, True):
+        o, lse = fa.forward(q, k, v, causal=causal)
+        dq, dk, dv = fa.backward(q, k, v, o, do, lse, causal=causal)
+        delta = fa.backward_preprocess(o, do)
+        dk2, dv2 = fa.backward_dkdv(q, k, v, do, lse, delta, causal=causal)
+        dq2 = fa.backward_dq(q, k, v, do, lse, delta, causal=causal)
+        torch.cuda.synchronize()
+        assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2)
+        ref = (do.float() * o.float()).sum(-1)
+        assert_close("delta", delta, np64(ref), 1e-4)
+
+
+def test_backward_repeatable_bitwise(dev):
+    q, k, v, do = (t.to(dev) for t in workloads.random_qkv(32, 1, 4, 1024, 1024, 128, torch.bfloat16, with_do=True))
+    o, lse = fa.forward(q, k, v, causal=True)
+    a = fa.backward(q, k, v, o, do, lse, causal=True)
+    b = fa.backward(q, k, v, o, do, lse, causal=True)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_constant_values_give_zero_q_k_gradients(dev):
+    q, k, _, do = workloads.random_qkv(33, 1, 2, 200, 200, 64, torch.float32, with_do=True)
+    v = torch.full((1, 2, 200, 64), 0.75)
+    for causal in (False, True):
+        _, _, dq, dk, dv = gpu_fwd_bwd(dev, q, k, v, do, 0.125, causal)
+        assert_close("dQ (V const)", dq, np.zeros(dq.shape), 2e-5)
+        assert_close("dK (V const)", dk, np.zeros(dk.shape), 2e-5)
+
+
+def test_gradient_identities(dev):
+    # Key gradients sum to zero and value gradients sum to sum_i dO_i.
+    q, k, v, do = workloads.random_qkv(34, 1, 2, 500, 500, 64, torch.float32, with_do=True)
+    for causal in (False, True):
+        _, _, dq, dk, dv = gpu_fwd_bwd(dev, q, k, v, do, 0.125, causal)
+        assert_close("sum dK", dk.double().sum(2), np.zeros((1, 2, 64)), 1e-4)
+        assert_close("sum dV", dv.double().sum(2), np64(do.double().sum(2)), 1e-4)
+
+
+def test_writes_stay_in_bounds(dev):
+    B, H, n, d = 1, 2, 190, 64
+    q, k, v, do = (t.to(dev) for t in workloads.random_qkv(35, B, H, n, n, d, torch.bfloat16, with_do=True))
+    o, lse = fa.forward(q, k, v, causal=True)
+    pad = 4096
+    bufs = [torch.full((pad + B * H * n * d + pad,), 55.0, dtype=torch.bfloat16, device=dev) for _ in range(3)]
+    views = [b[pad:pad + B * H * n * d].view(B, H, n, d) for b in bufs]
+    fa.backward(q, k, v, o, do, lse, causal=True, dq=views[0], dk=views[1], dv=views[2])
+    torch.cuda.synchronize()
+    for b in bufs:
+        assert torch.all(b[:pad] == 55.0) and torch.all(b[-pad:] == 55.0)

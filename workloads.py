@@ -18,6 +18,8 @@ float32 draws):
   script's third part does.
 * ``c3``: (1, 32, 4096, 128) bf16, seed 3, scale 1/sqrt(128), both causal and
   non-causal.
+* ``c3_train``: ``c3`` plus dO drawn fourth from the seed-3 stream: one
+  forward + backward step (the bench workload).
 * ``c4``: (1, 32, 16384, 128) bf16, seed 4, causal, scale 1/sqrt(128); the
   256 checked rows are the first 256 entries of ``torch.randperm(32 * 16384)``
   under seed 4004, row r -> (h, i) = (r // 16384, r % 16384).
@@ -33,7 +35,7 @@ from dataclasses import dataclass
 
 import torch
 
-__all__ = ["Workload", "c1", "c2", "c3", "c4", "c4_rows", "c5", "random_qkv"]
+__all__ = ["Workload", "c1", "c2", "c3", "c3_train", "c4", "c4_rows", "c5", "random_qkv"]
 
 
 @dataclass
@@ -70,6 +72,16 @@ def c3(causal: bool = False) -> Workload:
     q, k, v = (t.to(torch.bfloat16) for t in _draw(gen, (1, 32, 4096, 128), 3))
     return Workload(f"c3 fwd bf16 B1 H32 n4096 d128 {'causal' if causal else 'noncausal'}",
                     q, k, v, 1.0 / math.sqrt(128), causal)
+
+
+def c3_train(causal: bool = False) -> Workload:
+    """``c3`` plus an output gradient dO, drawn fourth from the same stream
+    (q, k, v are identical to ``c3``'s): the input of one forward + backward
+    step at B=1, H=32, n=4096, d=128."""
+    gen = torch.Generator().manual_seed(3)
+    q, k, v, do = (t.to(torch.bfloat16) for t in _draw(gen, (1, 32, 4096, 128), 4))
+    return Workload(f"c3 fwd+bwd bf16 B1 H32 n4096 d128 {'causal' if causal else 'noncausal'}",
+                    q, k, v, 1.0 / math.sqrt(128), causal, do)
 
 
 def c4() -> Workload:
