@@ -47,6 +47,37 @@ __device__ __forceinline__ bf16x4 lds_read_tr16(const __bf16* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((FA_LDS bf16x4*)(const_cast<__bf16*>(p)));
 }
 
+// Direct global -> LDS copy of 16 bytes per lane: lane j's 16 bytes at
+// base + voffset land at LDS byte address lds_addr + 16 j.  Issued from
+// inline assembly so that the compiler does not treat the copy as an LDS
+// store aliasing every later LDS read (it would wait for the copy before the
+// first one); the caller therefore waits for the copies itself
+// (s_waitcnt vmcnt(0)) before they are read.  The instruction has no result
+// registers, and M0 is set and used inside the same block.
+#pragma clang diagnostic push
+// M0 is reserved; nothing else in these kernels keeps a value in it across
+// the copy (LDS reads and lane shuffles do not use M0 on gfx950).
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_dma16(uint32_t lds_addr, const void* base, uint32_t voffset) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "global_load_lds_dwordx4 %1, %2"
+      :
+      : "s"(lds_addr), "v"(voffset), "s"(base)
+      : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// s_waitcnt vmcnt(0): every vector-memory load of this wave has completed,
+// the LDS copies above included.  Written with the builtin so that the
+// compiler's own wait tracking knows that its earlier loads are done too.
+__device__ __forceinline__ void wait_lds_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+template <typename T>
+__device__ __forceinline__ uint32_t lds_address(const T* p) {
+  return (uint32_t)(uintptr_t)((FA_LDS const void*)p);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 

@@ -42,27 +42,239 @@ namespace {
 
 template <int D>
 struct Bf16FwdCfg {
-  static constexpr int kWaves = 4;
+  static constexpr int kWaves = 8;                 // two per SIMD
   static constexpr int kThreads = kWaves * 64;
-  static constexpr int kQB = 2;                    // 32-row query blocks per wave
-  static constexpr int kBM = kWaves * kQB * 32;    // query rows per workgroup
+  static constexpr int kBM = kWaves * 32;          // query rows per workgroup, 32 per wave
   static constexpr int kBN = 64;                   // keys per block
   static constexpr int kKB = kBN / 32;             // 32-key sub-blocks
   static constexpr int kDC = D / 16;               // 16-wide chunks of the head dim
   static constexpr int kDB = D / 32;               // 32-row blocks of O^T
-  static constexpr int kKStride = D + 8;           // LDS row pitch of K (elements)
-  static constexpr int kVStride = D + 16;          // LDS row pitch of V (elements)
+  static constexpr int kRowBytes = 2 * D;          // one K or V row in LDS
   static constexpr int kChunks = D / 8;            // 16-byte chunks per row
-  static constexpr int kLoads = kBN * kChunks / kThreads;
-  static_assert(kLoads * kThreads == kBN * kChunks, "tile load split");
+  static constexpr int kTileBytes = kBN * kRowBytes;
+  static constexpr int kDmaLoads = kTileBytes / 1024;   // 1 KiB wave loads per tile
+  static_assert(kDmaLoads * 1024 == kTileBytes, "tile load split");
 };
 
+// LDS tiles hold K or V rows unpadded; the 16-byte chunk c of row r sits at
+// chunk position c ^ (r mod chunks-per-row), so the 32 rows read together by
+// a matrix-core operand load fall into different banks.
+template <int D>
+__device__ __forceinline__ int swz(int row, int chunk) {
+  return row * Bf16FwdCfg<D>::kRowBytes + ((chunk ^ (row % Bf16FwdCfg<D>::kChunks)) << 4);
+}
+
+// Largest amount by which a row's scores may exceed the reference maximum
+// used for its exponentials, in log2 units: probabilities stay below 2^8, so
+// the reference (and the rescaling of the output) only changes when a block
+// raises the row maximum by more than this.
+constexpr float kLazyRescale = 8.0f;
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdArgs a, int n_qtiles) {
+  using C = Bf16FwdCfg<D>;
+  __shared__ __attribute__((aligned(1024))) char sk[2][C::kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char sv[2][C::kTileBytes];
+
+  const int work = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = work / n_qtiles;
+  int qt = work - bh * n_qtiles;
+  if (CAUSAL) qt = n_qtiles - 1 - qt;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+  const int q0 = qt * C::kBM;
+  const int qw = q0 + wave * 32;
+  const int qi = qw + l32;  // this lane's query (column of S^T)
+  const int n_q = a.n_q, n_k = a.n_k;
+  const float sl2 = a.scale_log2;
+
+  const __bf16* qp = static_cast<const __bf16*>(a.q) + (size_t)bh * n_q * D;
+  const __bf16* kp = static_cast<const __bf16*>(a.k) + (size_t)bh * n_k * D;
+  const __bf16* vp = static_cast<const __bf16*>(a.v) + (size_t)bh * n_k * D;
+
+  // Q fragments: B operand of S^T = K Q^T, kept for the whole pass.
+  bf16x8 qf[C::kDC];
+#pragma unroll
+  for (int c = 0; c < C::kDC; ++c) {
+    if (qi < n_q)
+      qf[c] = *reinterpret_cast<const bf16x8*>(qp + (size_t)qi * D + 16 * c + 8 * hi);
+    else
+      qf[c] = bf16x8{};
+  }
+
+  const int q_end = min(n_q, q0 + C::kBM);
+  const int k_end = CAUSAL ? min(n_k, q_end) : n_k;
+  const int ntiles = (k_end + C::kBN - 1) / C::kBN;
+
+  // Direct global -> LDS loads: lane j of 1 KiB load number L writes LDS
+  // bytes [1024 L + 16 j, +16) of the tile, which hold row `dma_row`,
+  // logical chunk `dma_chunk` of that tile.  Wave w issues loads w, w + 8, ...
+  constexpr int kMine = (C::kDmaLoads + C::kWaves - 1) / C::kWaves;
+  int dma_row[kMine], dma_col[kMine];
+#pragma unroll
+  for (int i = 0; i < kMine; ++i) {
+    const int L = wave + i * C::kWaves;
+    const int off = L * 1024 + 16 * lane;
+    dma_row[i] = off / C::kRowBytes;
+    dma_col[i] = (((off % C::kRowBytes) >> 4) ^ (dma_row[i] % C::kChunks)) * 16;  // bytes
+  }
+  const uint32_t sk_addr = lds_address(&sk[0][0]);
+  const uint32_t sv_addr = lds_address(&sv[0][0]);
+  auto load_tile = [&](int t, int buf) {
+    const int k0 = t * C::kBN;
+    const __bf16* kb_ = kp + (size_t)k0 * D;
+    const __bf16* vb_ = vp + (size_t)k0 * D;
+    const int last = n_k - 1 - k0;  // rows past the last key repeat it (masked later)
+#pragma unroll
+    for (int i = 0; i < kMine; ++i) {
+      const int L = wave + i * C::kWaves;
+      if (L < C::kDmaLoads) {
+        const uint32_t voff = (uint32_t)(min(dma_row[i], last) * C::kRowBytes + dma_col[i]);
+        const uint32_t dst = buf * C::kTileBytes + L * 1024;
+        lds_dma16(sk_addr + dst, kb_, voff);
+        lds_dma16(sv_addr + dst, vb_, voff);
+      }
+    }
+  };
+
+  f32x16 oacc[C::kDB];
+#pragma unroll
+  for (int db = 0; db < C::kDB; ++db) oacc[db] = f32x16{};
+  float m = -INFINITY, l = 0.f;
+
+  // Lane coordinates of the transposing V read (see fa_device.hpp).
+  const int grp = lane >> 4;
+  const int tr_row = (lane & 15) >> 2;
+  const int tr_col = 16 * (grp & 1) + 4 * (lane & 3);
+
+  load_tile(0, 0);
+  for (int t = 0; t < ntiles; ++t) {
+    const int buf = t & 1;
+    // Block t is complete in LDS once every wave's own loads have landed;
+    // after the barrier nobody reads buffer buf ^ 1 any more.
+    wait_lds_dma();
+    __syncthreads();
+    if (t + 1 < ntiles) load_tile(t + 1, buf ^ 1);
+    const char* ks = sk[buf];
+    const char* vs = sv[buf];
+    const int k0 = t * C::kBN;
+
+    // S^T = K Q^T for kBN keys x 32 queries.
+    f32x16 s[C::kKB];
+#pragma unroll
+    for (int kb = 0; kb < C::kKB; ++kb) s[kb] = f32x16{};
+#pragma unroll
+    for (int c = 0; c < C::kDC; ++c) {
+#pragma unroll
+      for (int kb = 0; kb < C::kKB; ++kb) {
+        const bf16x8 ka =
+            *reinterpret_cast<const bf16x8*>(ks + swz<D>(kb * 32 + l32, 2 * c + hi));
+        s[kb] = mfma_bf16(ka, qf[c], s[kb]);
+      }
+    }
+
+    const bool need_mask = (k0 + C::kBN > n_k) || (CAUSAL && k0 + C::kBN - 1 > qw);
+    uint32_t hide[C::kKB];
+    if (need_mask) {
+#pragma unroll
+      for (int kb = 0; kb < C::kKB; ++kb) {
+        uint32_t bits = 0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = k0 + kb * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
+          const bool h = key >= n_k || (CAUSAL && key > qi);
+          bits |= (h ? 1u : 0u) << i;
+        }
+        hide[kb] = bits;
+      }
+    }
+    // Row maximum of the block (raw scores), then the lazy reference update.
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < C::kKB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float x = (need_mask && ((hide[kb] >> i) & 1u)) ? -INFINITY : s[kb][i];
+        mx = fmaxf(mx, x);
+      }
+    mx = fmaxf(mx, swap_halves(mx));
+    const float mt = (mx == -INFINITY) ? -INFINITY : mx * sl2;
+    if (__builtin_amdgcn_ballot_w64(mt > m + kLazyRescale) != 0) {
+      const float m_new = fmaxf(m, mt);
+      const float ref = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = fast_exp2(m - ref);
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < C::kDB; ++db) oacc[db] *= alpha;
+      m = m_new;
+    }
+    const float ref = (m == -INFINITY) ? 0.f : m;
+    float rs = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < C::kKB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float p = fast_exp2(fmaf(s[kb][i], sl2, -ref));
+        if (need_mask && ((hide[kb] >> i) & 1u)) p = 0.f;
+        s[kb][i] = p;
+        rs += p;
+      }
+    l += rs;
+
+    // O^T += V^T P^T, 16 keys per matrix-core step.
+#pragma unroll
+    for (int kb = 0; kb < C::kKB; ++kb) {
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2) {
+        bf16x8 pb;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pb[e] = (__bf16)s[kb][8 * c2 + e];
+        const int key_a = kb * 32 + 16 * c2 + 4 * hi + tr_row;
+#pragma unroll
+        for (int db = 0; db < C::kDB; ++db) {
+          const int col = 32 * db + tr_col;
+          const int ca = swz<D>(key_a, col >> 3) + 2 * (col & 7);
+          const int cb = swz<D>(key_a + 8, col >> 3) + 2 * (col & 7);
+          const bf16x4 va = lds_read_tr16(reinterpret_cast<const __bf16*>(vs + ca));
+          const bf16x4 vb = lds_read_tr16(reinterpret_cast<const __bf16*>(vs + cb));
+          const bf16x8 vop = {va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]};
+          oacc[db] = mfma_bf16(vop, pb, oacc[db]);
+        }
+      }
+    }
+  }
+
+  // Epilogue: normalise, store O (bf16) and LSE (natural log).
+  const float lt = l + swap_halves(l);
+  const float inv = 1.f / lt;
+  if (qi < n_q) {
+    __bf16* op = static_cast<__bf16*>(a.o) + ((size_t)bh * n_q + qi) * D;
+#pragma unroll
+    for (int db = 0; db < C::kDB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        bf16x4 r;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r[e] = (__bf16)(oacc[db][4 * g4 + e] * inv);
+        *reinterpret_cast<bf16x4*>(op + 32 * db + 8 * g4 + 4 * hi) = r;
+      }
+    if (hi == 0) a.lse[(size_t)bh * n_q + qi] = (m + fast_log2(lt)) * kLn2;
+  }
+}
+
+// ------------------------------------------------------------------ fp32
+
 // Online-softmax update of one 32-query block held as S^T fragments
-// s[kb] (kb = 32-key sub-block).  Turns s into unnormalised probabilities
-// exp2(scale_log2 * s - m_new), updates the running max m and the lane's
-// partial running sum l, and returns the rescale factor for the old output.
-// With MASK, hidden entries (hide bit set) are left out of the max and get
-// probability 0 (this also covers scale == 0, where -inf * 0 would be NaN).
+// s[kb] (kb = 32-key sub-block), updating the reference maximum every block.
+// Turns s into unnormalised probabilities exp2(scale_log2 * s - m_new),
+// updates the running max m and the lane's partial running sum l, and
+// returns the rescale factor for the old output.  With MASK, hidden entries
+// (hide bit set) are left out of the max and get probability 0 (this also
+// covers scale == 0, where -inf * 0 would be NaN).
 template <int KB, bool MASK>
 __device__ __forceinline__ float softmax_block(f32x16 (&s)[KB], float& m, float& l,
                                                float scale_log2, const uint32_t* hide) {
@@ -93,194 +305,6 @@ __device__ __forceinline__ float softmax_block(f32x16 (&s)[KB], float& m, float&
   m = m_new;
   return alpha;
 }
-
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdArgs a, int n_qtiles) {
-  using C = Bf16FwdCfg<D>;
-  __shared__ __attribute__((aligned(16))) __bf16 sk[2][C::kBN * C::kKStride];
-  __shared__ __attribute__((aligned(16))) __bf16 sv[2][C::kBN * C::kVStride];
-
-  const int work = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = work / n_qtiles;
-  int qt = work - bh * n_qtiles;
-  if (CAUSAL) qt = n_qtiles - 1 - qt;
-
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6;
-  const int lane = tid & 63;
-  const int l32 = lane & 31;
-  const int hi = lane >> 5;
-  const int q0 = qt * C::kBM;
-  const int qw = q0 + wave * (C::kQB * 32);
-  const int n_q = a.n_q, n_k = a.n_k;
-
-  const __bf16* qp = static_cast<const __bf16*>(a.q) + (size_t)bh * n_q * D;
-  const __bf16* kp = static_cast<const __bf16*>(a.k) + (size_t)bh * n_k * D;
-  const __bf16* vp = static_cast<const __bf16*>(a.v) + (size_t)bh * n_k * D;
-
-  // Q fragments: B operand of S^T = K Q^T, kept for the whole pass.
-  bf16x8 qf[C::kQB][C::kDC];
-#pragma unroll
-  for (int qb = 0; qb < C::kQB; ++qb) {
-    const int row = qw + qb * 32 + l32;
-#pragma unroll
-    for (int c = 0; c < C::kDC; ++c) {
-      if (row < n_q)
-        qf[qb][c] = *reinterpret_cast<const bf16x8*>(qp + (size_t)row * D + 16 * c + 8 * hi);
-      else
-        qf[qb][c] = bf16x8{};
-    }
-  }
-
-  const int q_end = min(n_q, q0 + C::kBM);
-  const int k_end = CAUSAL ? min(n_k, q_end) : n_k;
-  const int ntiles = (k_end + C::kBN - 1) / C::kBN;
-
-  u32x4 kst[C::kLoads], vst[C::kLoads];
-  auto gload = [&](int t) {
-#pragma unroll
-    for (int i = 0; i < C::kLoads; ++i) {
-      const int idx = tid + i * C::kThreads;
-      const int row = idx / C::kChunks;
-      const int ch = idx - row * C::kChunks;
-      const int key = t * C::kBN + row;
-      if (key < n_k) {
-        kst[i] = *reinterpret_cast<const u32x4*>(kp + (size_t)key * D + ch * 8);
-        vst[i] = *reinterpret_cast<const u32x4*>(vp + (size_t)key * D + ch * 8);
-      } else {
-        kst[i] = u32x4{0u, 0u, 0u, 0u};
-        vst[i] = u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-  };
-  auto swrite = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < C::kLoads; ++i) {
-      const int idx = tid + i * C::kThreads;
-      const int row = idx / C::kChunks;
-      const int ch = idx - row * C::kChunks;
-      *reinterpret_cast<u32x4*>(&sk[buf][row * C::kKStride + ch * 8]) = kst[i];
-      *reinterpret_cast<u32x4*>(&sv[buf][row * C::kVStride + ch * 8]) = vst[i];
-    }
-  };
-
-  f32x16 oacc[C::kDB][C::kQB];
-#pragma unroll
-  for (int db = 0; db < C::kDB; ++db)
-#pragma unroll
-    for (int qb = 0; qb < C::kQB; ++qb) oacc[db][qb] = f32x16{};
-  float m[C::kQB], l[C::kQB];
-#pragma unroll
-  for (int qb = 0; qb < C::kQB; ++qb) { m[qb] = -INFINITY; l[qb] = 0.f; }
-
-  // Lane coordinates of the transposing V read (see fa_device.hpp).
-  const int grp = lane >> 4;
-  const int tr_row = (lane & 15) >> 2;
-  const int tr_col = 16 * (grp & 1) + 4 * (lane & 3);
-
-  gload(0);
-  swrite(0);
-  __syncthreads();
-
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < ntiles) gload(t + 1);
-    const int k0 = t * C::kBN;
-
-    // S^T = K Q^T for 64 keys x 64 queries.
-    f32x16 s[C::kQB][C::kKB];
-#pragma unroll
-    for (int qb = 0; qb < C::kQB; ++qb)
-#pragma unroll
-      for (int kb = 0; kb < C::kKB; ++kb) s[qb][kb] = f32x16{};
-#pragma unroll
-    for (int c = 0; c < C::kDC; ++c) {
-#pragma unroll
-      for (int kb = 0; kb < C::kKB; ++kb) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(
-            &sk[buf][(kb * 32 + l32) * C::kKStride + 16 * c + 8 * hi]);
-#pragma unroll
-        for (int qb = 0; qb < C::kQB; ++qb) s[qb][kb] = mfma_bf16(ka, qf[qb][c], s[qb][kb]);
-      }
-    }
-
-    const bool need_mask = (k0 + C::kBN > n_k) || (CAUSAL && k0 + C::kBN - 1 > qw);
-#pragma unroll
-    for (int qb = 0; qb < C::kQB; ++qb) {
-      float alpha;
-      if (need_mask) {
-        uint32_t hide[C::kKB];
-        const int qi = qw + qb * 32 + l32;
-#pragma unroll
-        for (int kb = 0; kb < C::kKB; ++kb) {
-          uint32_t bits = 0;
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = k0 + kb * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
-            const bool h = key >= n_k || (CAUSAL && key > qi);
-            bits |= (h ? 1u : 0u) << i;
-          }
-          hide[kb] = bits;
-        }
-        alpha = softmax_block<C::kKB, true>(s[qb], m[qb], l[qb], a.scale_log2, hide);
-      } else {
-        alpha = softmax_block<C::kKB, false>(s[qb], m[qb], l[qb], a.scale_log2, nullptr);
-      }
-#pragma unroll
-      for (int db = 0; db < C::kDB; ++db) oacc[db][qb] *= alpha;
-    }
-
-    // O^T += V^T P^T, 16 keys per matrix-core step.
-#pragma unroll
-    for (int kb = 0; kb < C::kKB; ++kb) {
-#pragma unroll
-      for (int c2 = 0; c2 < 2; ++c2) {
-        bf16x8 pb[C::kQB];
-#pragma unroll
-        for (int qb = 0; qb < C::kQB; ++qb) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) pb[qb][e] = (__bf16)s[qb][kb][8 * c2 + e];
-        }
-        const int key_a = kb * 32 + 16 * c2 + 4 * hi + tr_row;
-#pragma unroll
-        for (int db = 0; db < C::kDB; ++db) {
-          const int col = 32 * db + tr_col;
-          const bf16x4 va = lds_read_tr16(&sv[buf][key_a * C::kVStride + col]);
-          const bf16x4 vb = lds_read_tr16(&sv[buf][(key_a + 8) * C::kVStride + col]);
-          const bf16x8 vop = {va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]};
-#pragma unroll
-          for (int qb = 0; qb < C::kQB; ++qb) oacc[db][qb] = mfma_bf16(vop, pb[qb], oacc[db][qb]);
-        }
-      }
-    }
-
-    if (t + 1 < ntiles) swrite(buf ^ 1);
-    __syncthreads();
-  }
-
-  // Epilogue: normalise, store O (bf16) and LSE (natural log).
-#pragma unroll
-  for (int qb = 0; qb < C::kQB; ++qb) {
-    const float lt = l[qb] + swap_halves(l[qb]);
-    const float inv = 1.f / lt;
-    const int qi = qw + qb * 32 + l32;
-    if (qi < n_q) {
-      __bf16* op = static_cast<__bf16*>(a.o) + ((size_t)bh * n_q + qi) * D;
-#pragma unroll
-      for (int db = 0; db < C::kDB; ++db)
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          bf16x4 r;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) r[e] = (__bf16)(oacc[db][qb][4 * g4 + e] * inv);
-          *reinterpret_cast<bf16x4*>(op + 32 * db + 8 * g4 + 4 * hi) = r;
-        }
-      if (hi == 0) a.lse[(size_t)bh * n_q + qi] = (m[qb] + fast_log2(lt)) * kLn2;
-    }
-  }
-}
-
-// ------------------------------------------------------------------ fp32
 
 template <int D>
 struct F32FwdCfg {
@@ -429,24 +453,27 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdArgs a, int n_qtiles) {
 }
 
 template <typename Kernel>
-hipError_t launch(Kernel kernel, int grid, const FwdArgs& a, int n_qtiles, hipStream_t stream) {
+hipError_t launch(Kernel kernel, int grid, int block, const FwdArgs& a, int n_qtiles,
+                  hipStream_t stream) {
   FwdArgs args = a;
   int nq = n_qtiles;
   void* params[] = {&args, &nq};
-  return hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3(grid), dim3(256), params, 0,
+  return hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3(grid), dim3(block), params, 0,
                          stream);
 }
 
 template <int D, bool CAUSAL>
 hipError_t fwd_bf16_t(const FwdArgs& a, hipStream_t stream) {
   const int n_qtiles = (a.n_q + Bf16FwdCfg<D>::kBM - 1) / Bf16FwdCfg<D>::kBM;
-  return launch(fwd_bf16_kernel<D, CAUSAL>, n_qtiles * a.BH, a, n_qtiles, stream);
+  return launch(fwd_bf16_kernel<D, CAUSAL>, n_qtiles * a.BH, Bf16FwdCfg<D>::kThreads, a, n_qtiles,
+                stream);
 }
 
 template <int D, bool CAUSAL>
 hipError_t fwd_f32_t(const FwdArgs& a, hipStream_t stream) {
   const int n_qtiles = (a.n_q + F32FwdCfg<D>::kBM - 1) / F32FwdCfg<D>::kBM;
-  return launch(fwd_f32_kernel<D, CAUSAL>, n_qtiles * a.BH, a, n_qtiles, stream);
+  return launch(fwd_f32_kernel<D, CAUSAL>, n_qtiles * a.BH, F32FwdCfg<D>::kThreads, a, n_qtiles,
+                stream);
 }
 
 }  // namespace
