@@ -38,6 +38,10 @@ def compile_flags() -> list[str]:
         "-O3",
         "-std=c++17",
         "-fPIC",
+        # NaN inputs are not supported (they propagate unchecked), so the
+        # compiler need not quiet NaNs before every max; infinities are still
+        # honoured (the masks use -inf).
+        "-fno-honor-nans",
         "-Wall",
         "-Wno-unused-function",
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -36,6 +36,7 @@
 #include "fa_device.hpp"
 
 #include <cmath>
+#include <type_traits>
 
 namespace fa {
 namespace {
@@ -151,9 +152,15 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdArgs a, int n_qtiles) 
   const int tr_row = (lane & 15) >> 2;
   const int tr_col = 16 * (grp & 1) + 4 * (lane & 3);
 
-  load_tile(0, 0);
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
+  // One key block: wait for it, start the next block's copy, then
+  // S^T = K Q^T, softmax, O^T += V^T P^T.  MASK selects the variant with the
+  // causal / key-tail mask; BUF (0, 1, or -1 for "t % 2 at run time") names
+  // the LDS buffer, so that with a fixed buffer every LDS address is a
+  // per-lane register plus an immediate.
+  auto block = [&](auto mask_tag, auto buf_tag, int t) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    constexpr int BUFC = decltype(buf_tag)::value;
+    const int buf = BUFC >= 0 ? BUFC : (t & 1);
     // Block t is complete in LDS once every wave's own loads have landed;
     // after the barrier nobody reads buffer buf ^ 1 any more.
     wait_lds_dma();
@@ -177,30 +184,23 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdArgs a, int n_qtiles) 
       }
     }
 
-    const bool need_mask = (k0 + C::kBN > n_k) || (CAUSAL && k0 + C::kBN - 1 > qw);
-    uint32_t hide[C::kKB];
-    if (need_mask) {
+    if constexpr (MASK) {
+      // Hidden entries (key past the end, or after the query when causal)
+      // leave the maximum alone and get probability 0.
 #pragma unroll
-      for (int kb = 0; kb < C::kKB; ++kb) {
-        uint32_t bits = 0;
+      for (int kb = 0; kb < C::kKB; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = k0 + kb * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
-          const bool h = key >= n_k || (CAUSAL && key > qi);
-          bits |= (h ? 1u : 0u) << i;
+          if (key >= n_k || (CAUSAL && key > qi)) s[kb][i] = -INFINITY;
         }
-        hide[kb] = bits;
-      }
     }
     // Row maximum of the block (raw scores), then the lazy reference update.
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < C::kKB; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float x = (need_mask && ((hide[kb] >> i) & 1u)) ? -INFINITY : s[kb][i];
-        mx = fmaxf(mx, x);
-      }
+      for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(s[kb][i], s[kb][i + 1]));
     mx = fmaxf(mx, swap_halves(mx));
     const float mt = (mx == -INFINITY) ? -INFINITY : mx * sl2;
     if (__builtin_amdgcn_ballot_w64(mt > m + kLazyRescale) != 0) {
@@ -213,26 +213,39 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdArgs a, int n_qtiles) 
       m = m_new;
     }
     const float ref = (m == -INFINITY) ? 0.f : m;
-    float rs = 0.f;
+
+    // P = exp2(scale_log2 * S - ref), rounded to bf16 as the B operand of
+    // the P V product.  The row sum l adds the unrounded float values: the
+    // LSE needs them (a sum of bf16-rounded terms is off by up to 2^-9).
+    bf16x8 pb[C::kKB][2];
+    float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
     for (int kb = 0; kb < C::kKB; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float p = fast_exp2(fmaf(s[kb][i], sl2, -ref));
-        if (need_mask && ((hide[kb] >> i) & 1u)) p = 0.f;
-        s[kb][i] = p;
-        rs += p;
+      for (int c2 = 0; c2 < 2; ++c2) {
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          float p0 = fast_exp2(fmaf(s[kb][8 * c2 + e], sl2, -ref));
+          float p1 = fast_exp2(fmaf(s[kb][8 * c2 + e + 1], sl2, -ref));
+          if constexpr (MASK) {
+            // exp2(-inf) is 0 already unless the scale is 0.
+            if (s[kb][8 * c2 + e] == -INFINITY) p0 = 0.f;
+            if (s[kb][8 * c2 + e + 1] == -INFINITY) p1 = 0.f;
+          }
+          const bf16x2 pp = to_bf16x2(p0, p1);
+          pb[kb][c2][e] = pp[0];
+          pb[kb][c2][e + 1] = pp[1];
+          rs0 += p0;
+          rs1 += p1;
+        }
       }
-    l += rs;
+    l += rs0 + rs1;
 
     // O^T += V^T P^T, 16 keys per matrix-core step.
 #pragma unroll
     for (int kb = 0; kb < C::kKB; ++kb) {
 #pragma unroll
       for (int c2 = 0; c2 < 2; ++c2) {
-        bf16x8 pb;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pb[e] = (__bf16)s[kb][8 * c2 + e];
         const int key_a = kb * 32 + 16 * c2 + 4 * hi + tr_row;
 #pragma unroll
         for (int db = 0; db < C::kDB; ++db) {
@@ -242,11 +255,25 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdArgs a, int n_qtiles) 
           const bf16x4 va = lds_read_tr16(reinterpret_cast<const __bf16*>(vs + ca));
           const bf16x4 vb = lds_read_tr16(reinterpret_cast<const __bf16*>(vs + cb));
           const bf16x8 vop = {va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]};
-          oacc[db] = mfma_bf16(vop, pb, oacc[db]);
+          oacc[db] = mfma_bf16(vop, pb[kb][c2], oacc[db]);
         }
       }
     }
+  };
+
+  // Leading blocks that need no mask for any row of the workgroup, two at a
+  // time with fixed buffers; the rest (key tail, causal diagonal) masked.
+  const int n_full = min(ntiles, (CAUSAL ? min(q0 + 1, n_k) : n_k) / C::kBN);
+  using F = std::false_type;
+  using T = std::true_type;
+  load_tile(0, 0);
+  int t = 0;
+  for (; t + 1 < n_full; t += 2) {
+    block(F{}, std::integral_constant<int, 0>{}, t);
+    block(F{}, std::integral_constant<int, 1>{}, t + 1);
   }
+  for (; t < n_full; ++t) block(F{}, std::integral_constant<int, -1>{}, t);
+  for (; t < ntiles; ++t) block(T{}, std::integral_constant<int, -1>{}, t);
 
   // Epilogue: normalise, store O (bf16) and LSE (natural log).
   const float lt = l + swap_halves(l);
