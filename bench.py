@@ -68,7 +68,7 @@ def kernel_bytes(B, H, n, d, e=2):
     r = B * H * n * 4
     return {
         "fwd": 3 * t + t + r,                     # read q k v, write o lse
-        "bwd_preprocess": 2 * t + r,              # read o dO, write delta
+        "bwd_preprocess": 2 * t + 3 * r,          # read o dO lse, write delta and lse*log2(e)
         "bwd_dkdv": 4 * t + 2 * r + 2 * t,        # read q k v dO lse delta, write dk dv
         "bwd_dq": 4 * t + 2 * r + t,              # read q k v dO lse delta, write dq
     }
@@ -155,7 +155,7 @@ def main(argv=None):
     q, k, v, do = (t.to(dev).contiguous() for t in (w.q, w.k, w.v, w.do))
     o = torch.empty_like(q)
     lse = torch.empty((B, H, n), dtype=torch.float32, device=dev)
-    delta = torch.empty((B, H, n), dtype=torch.float32, device=dev)
+    ws = fa.backward_workspace(B, H, n, n, d, q.dtype, dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     causal = args.causal
 
@@ -167,13 +167,13 @@ def main(argv=None):
         fa.forward(q, k, v, causal=causal, scale=w.scale, out=o, lse=lse)
         if ev is not None:
             ev[1].record()
-        fa.backward_preprocess(o, do, delta)
+        fa.backward_preprocess(o, do, lse, ws)
         if ev is not None:
             ev[2].record()
-        fa.backward_dkdv(q, k, v, do, lse, delta, causal=causal, scale=w.scale, dk=dk, dv=dv)
+        fa.backward_dkdv(q, k, v, do, ws, causal=causal, scale=w.scale, dk=dk, dv=dv)
         if ev is not None:
             ev[3].record()
-        fa.backward_dq(q, k, v, do, lse, delta, causal=causal, scale=w.scale, dq=dq)
+        fa.backward_dq(q, k, v, do, ws, causal=causal, scale=w.scale, dq=dq)
         if ev is not None:
             ev[4].record()
 

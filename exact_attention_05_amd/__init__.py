@@ -18,10 +18,12 @@ from .binding import (  # noqa: F401
     backward_dkdv,
     backward_dq,
     backward_preprocess,
+    backward_workspace,
     backward_workspace_size,
     forward,
     lib,
     library_path,
     status_string,
     version,
+    workspace_delta,
 )

@@ -16,8 +16,8 @@ import torch
 __all__ = [
     "FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_WORKSPACE", "FA_ERR_LAUNCH",
     "FA_ERR_ALIGNMENT", "FA_DTYPE_FP32", "FA_DTYPE_BF16", "FaError", "library_path", "lib",
-    "forward", "backward", "backward_workspace_size", "backward_preprocess", "backward_dkdv",
-    "backward_dq", "status_string", "version",
+    "forward", "backward", "backward_workspace_size", "backward_workspace", "workspace_delta",
+    "backward_preprocess", "backward_dkdv", "backward_dq", "status_string", "version",
 ]
 
 FA_OK = 0
@@ -60,11 +60,11 @@ def lib() -> ctypes.CDLL:
         L.fa_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
                                   i, i, i, i, i, f, i, i, vp]
         L.fa_backward.restype = i
-        L.fa_backward_preprocess.argtypes = [vp, vp, vp, i, i, i, i, i, vp]
+        L.fa_backward_preprocess.argtypes = [vp, vp, vp, vp, sz, i, i, i, i, i, vp]
         L.fa_backward_preprocess.restype = i
-        L.fa_backward_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp]
+        L.fa_backward_dkdv.argtypes = [vp, vp, vp, vp, vp, sz, vp, vp, i, i, i, i, i, f, i, i, vp]
         L.fa_backward_dkdv.restype = i
-        L.fa_backward_dq.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp]
+        L.fa_backward_dq.argtypes = [vp, vp, vp, vp, vp, sz, vp, i, i, i, i, i, f, i, i, vp]
         L.fa_backward_dq.restype = i
         L.fa_status_string.argtypes = [i]
         L.fa_status_string.restype = ctypes.c_char_p
@@ -167,45 +167,63 @@ def backward(q, k, v, o, do, lse, causal: bool = False, scale: float | None = No
     _check_like("dq", dq, q)
     _check_like("dk", dk, k)
     _check_like("dv", dv, v)
-    ws_bytes = backward_workspace_size(B, H, n_q, n_k, d, q.dtype)
     if workspace is None:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+        workspace = backward_workspace(B, H, n_q, n_k, d, q.dtype, q.device)
     st = lib().fa_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq),
-                           _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                           _ptr(dk), _ptr(dv), *_ws(workspace),
                            B, H, n_q, n_k, d, _scale(scale, d), int(bool(causal)),
                            _DTYPES[q.dtype], _stream(q.device))
     _check(st, "fa_backward")
     return dq, dk, dv
 
 
-def backward_preprocess(o, do, delta=None):
-    """delta = rowsum(do * o) in float32, (B, H, n_q)."""
+def backward_workspace(B, H, n_q, n_k, d, dtype: torch.dtype, device) -> torch.Tensor:
+    """A device buffer of fa_backward_workspace_size bytes (256-byte aligned)."""
+    n = backward_workspace_size(B, H, n_q, n_k, d, dtype)
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def _ws(workspace):
+    return _ptr(workspace), workspace.numel() * workspace.element_size()
+
+
+def workspace_delta(workspace: torch.Tensor, B: int, H: int, n_q: int) -> torch.Tensor:
+    """View of the row sums D = rowsum(dO * O) that stage 1 writes at the start
+    of the workspace, as a float32 (B, H, n_q) tensor."""
+    return workspace[: B * H * n_q * 4].view(torch.float32).view(B, H, n_q)
+
+
+def backward_preprocess(o, do, lse, workspace=None):
+    """Stage 1: writes D = rowsum(do * o) and LSE * log2(e) into the workspace
+    (allocated if not given) and returns it."""
     B, H, n_q, d = o.shape
     _check_like("do", do, o)
-    if delta is None:
-        delta = torch.empty((B, H, n_q), dtype=torch.float32, device=o.device)
-    st = lib().fa_backward_preprocess(_ptr(o), _ptr(do), _ptr(delta), B, H, n_q, d,
+    if workspace is None:
+        workspace = backward_workspace(B, H, n_q, n_q, d, o.dtype, o.device)
+    st = lib().fa_backward_preprocess(_ptr(o), _ptr(do), _ptr(lse), *_ws(workspace), B, H, n_q, d,
                                       _DTYPES[o.dtype], _stream(o.device))
     _check(st, "fa_backward_preprocess")
-    return delta
+    return workspace
 
 
-def backward_dkdv(q, k, v, do, lse, delta, causal=False, scale=None, dk=None, dv=None):
+def backward_dkdv(q, k, v, do, workspace, causal=False, scale=None, dk=None, dv=None):
+    """Stage 2: dK and dV from the workspace of stage 1."""
     B, H, n_q, n_k, d = _check_qkv(q, k, v)
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
-    st = lib().fa_backward_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(delta),
+    st = lib().fa_backward_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(do), *_ws(workspace),
                                 _ptr(dk), _ptr(dv), B, H, n_q, n_k, d, _scale(scale, d),
                                 int(bool(causal)), _DTYPES[q.dtype], _stream(q.device))
     _check(st, "fa_backward_dkdv")
     return dk, dv
 
 
-def backward_dq(q, k, v, do, lse, delta, causal=False, scale=None, dq=None):
+def backward_dq(q, k, v, do, workspace, causal=False, scale=None, dq=None):
+    """Stage 3: dQ from the workspace of stage 1."""
     B, H, n_q, n_k, d = _check_qkv(q, k, v)
     dq = torch.empty_like(q) if dq is None else dq
-    st = lib().fa_backward_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(delta),
-                              _ptr(dq), B, H, n_q, n_k, d, _scale(scale, d), int(bool(causal)),
+    st = lib().fa_backward_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(do), *_ws(workspace), _ptr(dq),
+                              B, H, n_q, n_k, d, _scale(scale, d), int(bool(causal)),
                               _DTYPES[q.dtype], _stream(q.device))
     _check(st, "fa_backward_dq")
     return dq

@@ -38,10 +38,11 @@ def compile_flags() -> list[str]:
         "-O3",
         "-std=c++17",
         "-fPIC",
-        # NaN inputs are not supported (they propagate unchecked), so the
-        # compiler need not quiet NaNs before every max; infinities are still
-        # honoured (the masks use -inf).
-        "-fno-honor-nans",
+        # Device code only: NaN inputs are not supported (they propagate
+        # unchecked), so the compiler need not quiet NaNs before every max;
+        # infinities are still honoured (the masks use -inf).  Host code keeps
+        # full IEEE semantics for argument validation.
+        "-Xarch_device", "-fno-honor-nans",
         "-Wall",
         "-Wno-unused-function",
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

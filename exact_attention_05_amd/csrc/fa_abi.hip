@@ -8,6 +8,7 @@
 #include <climits>
 #include <cmath>
 #include <cstdint>
+#include <cstring>
 
 namespace {
 
@@ -26,8 +27,16 @@ int check_sizes(int B, int H, int n_q, int n_k, int d, int dtype) {
   return FA_OK;
 }
 
+// Finite test on the bit pattern: the library is built without NaN semantics
+// (-fno-honor-nans), under which std::isfinite may be folded to true.
+bool finite_bits(float x) {
+  uint32_t u;
+  std::memcpy(&u, &x, sizeof(u));
+  return ((u >> 23) & 0xFFu) != 0xFFu;
+}
+
 int check_scale_causal(float scale, int causal) {
-  if (!std::isfinite(scale) || scale < 0.f) return FA_ERR_INVALID_ARG;
+  if (!finite_bits(scale) || scale < 0.f) return FA_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
   return FA_OK;
 }
@@ -52,16 +61,29 @@ int first_error(T... s) {
   return r;
 }
 
-size_t delta_bytes(int B, int H, int n_q) {
-  const size_t raw = (size_t)B * (size_t)H * (size_t)n_q * sizeof(float);
+// Backward workspace: two float32 (B,H,n_q) row vectors, D then LSE*log2(e),
+// each followed by at least 16 bytes of slack (16-byte copies of a vector's
+// last entries may read up to 12 bytes past it) and rounded up to 256 bytes.
+size_t ws_half_bytes(int B, int H, int n_q) {
+  const size_t raw = (size_t)B * (size_t)H * (size_t)n_q * sizeof(float) + 16;
   return (raw + 255) / 256 * 256;
+}
+size_t ws_bytes(int B, int H, int n_q) { return 2 * ws_half_bytes(B, H, n_q); }
+
+int check_workspace(const void* ws, size_t bytes, int B, int H, int n_q) {
+  if (ws == nullptr || bytes < ws_bytes(B, H, n_q)) return FA_ERR_WORKSPACE;
+  if (!aligned(ws, 256)) return FA_ERR_ALIGNMENT;
+  return FA_OK;
 }
 
 fa::BwdArgs make_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
-                     const float* lse, float* delta, void* dq, void* dk, void* dv, int B, int H,
+                     const float* lse, const void* ws, void* dq, void* dk, void* dv, int B, int H,
                      int n_q, int n_k, float scale) {
   fa::BwdArgs a;
-  a.q = q; a.k = k; a.v = v; a.o = o; a.dO = dO; a.lse = lse; a.delta = delta;
+  a.q = q; a.k = k; a.v = v; a.o = o; a.dO = dO; a.lse = lse;
+  char* w = static_cast<char*>(const_cast<void*>(ws));
+  a.delta = reinterpret_cast<float*>(w);
+  a.lse2 = w ? reinterpret_cast<float*>(w + ws_half_bytes(B, H, n_q)) : nullptr;
   a.dq = dq; a.dk = dk; a.dv = dv;
   a.BH = B * H; a.n_q = n_q; a.n_k = n_k;
   a.scale = scale;
@@ -107,44 +129,46 @@ int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse,
 
 size_t fa_backward_workspace_size(int B, int H, int n_q, int n_k, int d, int dtype) {
   if (check_sizes(B, H, n_q, n_k, d, dtype) != FA_OK) return 0;
-  return delta_bytes(B, H, n_q);
+  return ws_bytes(B, H, n_q);
 }
 
-int fa_backward_preprocess(const void* o, const void* dO, float* delta, int B, int H, int n_q,
-                           int d, int dtype, void* stream) {
+int fa_backward_preprocess(const void* o, const void* dO, const float* lse, void* workspace,
+                           size_t workspace_bytes, int B, int H, int n_q, int d, int dtype,
+                           void* stream) {
   int st = first_error(check_sizes(B, H, n_q, 1, d, dtype), check_tensor(o), check_tensor(dO),
-                       check_rowvec(delta));
+                       check_rowvec(lse), check_workspace(workspace, workspace_bytes, B, H, n_q));
   if (st != FA_OK) return st;
-  fa::BwdArgs a = make_bwd(nullptr, nullptr, nullptr, o, dO, nullptr, delta, nullptr, nullptr,
+  fa::BwdArgs a = make_bwd(nullptr, nullptr, nullptr, o, dO, lse, workspace, nullptr, nullptr,
                            nullptr, B, H, n_q, 1, 0.f);
   return status_of(fa::launch_bwd_preprocess(a, d, dtype == FA_DTYPE_BF16,
                                              static_cast<hipStream_t>(stream)));
 }
 
 int fa_backward_dkdv(const void* q, const void* k, const void* v, const void* dO,
-                     const float* lse, const float* delta, void* dk, void* dv, int B, int H,
-                     int n_q, int n_k, int d, float scale, int causal, int dtype, void* stream) {
+                     const void* workspace, size_t workspace_bytes, void* dk, void* dv, int B,
+                     int H, int n_q, int n_k, int d, float scale, int causal, int dtype,
+                     void* stream) {
   int st = first_error(check_sizes(B, H, n_q, n_k, d, dtype), check_scale_causal(scale, causal),
                        check_tensor(q), check_tensor(k), check_tensor(v), check_tensor(dO),
-                       check_rowvec(lse), check_rowvec(delta), check_tensor(dk),
+                       check_workspace(workspace, workspace_bytes, B, H, n_q), check_tensor(dk),
                        check_tensor(dv));
   if (st != FA_OK) return st;
-  fa::BwdArgs a = make_bwd(q, k, v, nullptr, dO, lse, const_cast<float*>(delta), nullptr, dk, dv,
-                           B, H, n_q, n_k, scale);
+  fa::BwdArgs a = make_bwd(q, k, v, nullptr, dO, nullptr, workspace, nullptr, dk, dv, B, H, n_q,
+                           n_k, scale);
   hipStream_t s = static_cast<hipStream_t>(stream);
   return status_of(dtype == FA_DTYPE_BF16 ? fa::launch_bwd_dkdv_bf16(a, d, causal != 0, s)
                                           : fa::launch_bwd_dkdv_f32(a, d, causal != 0, s));
 }
 
-int fa_backward_dq(const void* q, const void* k, const void* v, const void* dO, const float* lse,
-                   const float* delta, void* dq, int B, int H, int n_q, int n_k, int d,
-                   float scale, int causal, int dtype, void* stream) {
+int fa_backward_dq(const void* q, const void* k, const void* v, const void* dO,
+                   const void* workspace, size_t workspace_bytes, void* dq, int B, int H, int n_q,
+                   int n_k, int d, float scale, int causal, int dtype, void* stream) {
   int st = first_error(check_sizes(B, H, n_q, n_k, d, dtype), check_scale_causal(scale, causal),
                        check_tensor(q), check_tensor(k), check_tensor(v), check_tensor(dO),
-                       check_rowvec(lse), check_rowvec(delta), check_tensor(dq));
+                       check_workspace(workspace, workspace_bytes, B, H, n_q), check_tensor(dq));
   if (st != FA_OK) return st;
-  fa::BwdArgs a = make_bwd(q, k, v, nullptr, dO, lse, const_cast<float*>(delta), dq, nullptr,
-                           nullptr, B, H, n_q, n_k, scale);
+  fa::BwdArgs a = make_bwd(q, k, v, nullptr, dO, nullptr, workspace, dq, nullptr, nullptr, B, H,
+                           n_q, n_k, scale);
   hipStream_t s = static_cast<hipStream_t>(stream);
   return status_of(dtype == FA_DTYPE_BF16 ? fa::launch_bwd_dq_bf16(a, d, causal != 0, s)
                                           : fa::launch_bwd_dq_f32(a, d, causal != 0, s));
@@ -159,10 +183,9 @@ int fa_backward(const void* q, const void* k, const void* v, const void* o, cons
                        check_tensor(dO), check_rowvec(lse), check_tensor(dq), check_tensor(dk),
                        check_tensor(dv));
   if (st != FA_OK) return st;
-  if (workspace == nullptr || workspace_bytes < delta_bytes(B, H, n_q)) return FA_ERR_WORKSPACE;
-  if (!aligned(workspace, 256)) return FA_ERR_ALIGNMENT;
-  float* delta = static_cast<float*>(workspace);
-  fa::BwdArgs a = make_bwd(q, k, v, o, dO, lse, delta, dq, dk, dv, B, H, n_q, n_k, scale);
+  st = check_workspace(workspace, workspace_bytes, B, H, n_q);
+  if (st != FA_OK) return st;
+  fa::BwdArgs a = make_bwd(q, k, v, o, dO, lse, workspace, dq, dk, dv, B, H, n_q, n_k, scale);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool bf16 = dtype == FA_DTYPE_BF16;
   hipError_t e = fa::launch_bwd_preprocess(a, d, bf16, s);

@@ -10,36 +10,52 @@
 //   dQ  = scale dS K                  (stage 3, one workgroup per query block)
 //
 // Stages 2 and 3 both recompute S and dP, so no atomics are needed and the
-// result is bitwise repeatable.
+// result is bitwise repeatable.  Stage 1 also stores LSE_i * log2(e) next to
+// D_i in the workspace, so the later stages exponentiate base 2 with a single
+// fused multiply-add and can copy both rows straight into LDS.
 //
-// Stage 2 (dK, dV): each wave owns 32 keys and keeps their K and V rows in
-// registers as matrix-core B operands for the whole pass.  Query blocks of
-// 64 rows (Q, dO, LSE, D) stream through double-buffered LDS.  S = Q K^T and
-// dP = dO V^T land in the accumulator layout with one key per lane, which is
-// the B-operand layout needed for dV^T += dO^T P and dK^T += Q^T dS; the
-// dO^T and Q^T A operands come from LDS through ds_read_b64_tr_b16.
+// bf16 stage 2 (dK, dV): 8 waves (two per SIMD); each wave owns 32 keys and
+// keeps their K and V rows in registers as matrix-core B operands for the
+// whole pass.  Query blocks of 64 rows (Q, dO, and the two row vectors)
+// stream through double-buffered LDS by direct global -> LDS copies.
+// S = Q K^T and dP = dO V^T land in the accumulator layout with one key per
+// lane, which is the B-operand layout needed for dV^T += dO^T P and
+// dK^T += Q^T dS; the dO^T and Q^T A operands come from the same LDS tiles
+// through the transposing read.
 //
-// Stage 3 (dQ): mirrors the forward kernel.  Each wave owns 32 queries and
-// keeps Q and dO in registers; key blocks of 64 rows (K, V) stream through
-// LDS.  S^T = K Q^T and dP^T = V dO^T put one query per lane, so LSE_i and
-// D_i are one register each, and dQ^T += K^T dS^T takes K^T through the
-// transposing LDS read.
+// bf16 stage 3 (dQ): mirrors the forward kernel.  8 waves own 32 queries
+// each and keep Q and dO in registers; key blocks of 64 rows (K, V) stream
+// through LDS.  S^T = K Q^T and dP^T = V dO^T put one query per lane, so
+// LSE_i and D_i are one register each, and dQ^T += K^T dS^T reads K^T
+// through the transposing read.
+//
+// In both, blocks that need no mask for any row of the workgroup run
+// through a separate code path, two at a time with fixed LDS buffers.
 #include "fa_internal.hpp"
 #include "fa_device.hpp"
+#include "fa_tiles.hpp"
 
 #include <cmath>
+#include <type_traits>
 
 namespace fa {
 namespace {
 
+using F = std::false_type;
+using T = std::true_type;
+template <int B>
+using Buf = std::integral_constant<int, B>;
+
 // ------------------------------------------------------------ stage 1
 
-template <int D, typename T>
-__global__ __launch_bounds__(256) void bwd_preprocess_kernel(const T* __restrict__ o,
-                                                            const T* __restrict__ dO,
+template <int D, typename TT>
+__global__ __launch_bounds__(256) void bwd_preprocess_kernel(const TT* __restrict__ o,
+                                                            const TT* __restrict__ dO,
+                                                            const float* __restrict__ lse,
                                                             float* __restrict__ delta,
+                                                            float* __restrict__ lse2,
                                                             long rows) {
-  constexpr int kVec = 16 / sizeof(T);        // elements per 16-byte load
+  constexpr int kVec = 16 / sizeof(TT);       // elements per 16-byte load
   constexpr int kLanesPerRow = D / kVec;      // 4 .. 32
   constexpr int kRowsPerBlock = 256 / kLanesPerRow;
   const int tid = threadIdx.x;
@@ -47,9 +63,9 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(const T* __restrict
   const int part = tid % kLanesPerRow;
   float acc = 0.f;
   if (row < rows) {
-    const T* op = o + row * D + part * kVec;
-    const T* gp = dO + row * D + part * kVec;
-    if constexpr (sizeof(T) == 2) {
+    const TT* op = o + row * D + part * kVec;
+    const TT* gp = dO + row * D + part * kVec;
+    if constexpr (sizeof(TT) == 2) {
       const bf16x8 x = *reinterpret_cast<const bf16x8*>(op);
       const bf16x8 y = *reinterpret_cast<const bf16x8*>(gp);
 #pragma unroll
@@ -63,206 +79,235 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(const T* __restrict
   }
 #pragma unroll
   for (int off = kLanesPerRow / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
-  if (row < rows && part == 0) delta[row] = acc;
+  if (row < rows && part == 0) {
+    delta[row] = acc;
+    lse2[row] = lse[row] * kLog2e;
+  }
 }
 
 // ------------------------------------------------------ stage 2 (bf16)
 
 template <int D>
 struct DkdvCfg {
-  static constexpr int kWaves = 4;
+  static constexpr int kWaves = 4;               // one per SIMD: 512 registers each
   static constexpr int kThreads = kWaves * 64;
-  static constexpr int kBK = kWaves * 32;        // keys per workgroup
-  static constexpr int kBQ = 64;                 // queries per block
+  static constexpr int kKW = 1;                  // 32-key column blocks per wave
+  static constexpr int kBK = kWaves * kKW * 32;  // keys per workgroup
+  static constexpr int kBQ = 64;                 // queries per streamed block
   static constexpr int kQS = kBQ / 32;           // 32-query sub-blocks
   static constexpr int kDC = D / 16;
   static constexpr int kDB = D / 32;
-  static constexpr int kStride = D + 16;         // LDS pitch (elements) of Q and dO
-  static constexpr int kChunks = D / 8;
-  static constexpr int kLoads = kBQ * kChunks / kThreads;
-  static_assert(kLoads * kThreads == kBQ * kChunks, "tile load split");
+  using QT = Tile<D, kBQ>;                       // one Q or dO block in LDS
+  static constexpr int kRowVecBytes = kBQ * 4;   // one block of LSE2 or D
 };
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256) void bwd_dkdv_bf16_kernel(BwdArgs a, int n_ktiles) {
   using C = DkdvCfg<D>;
-  __shared__ __attribute__((aligned(16))) __bf16 sq[2][C::kBQ * C::kStride];
-  __shared__ __attribute__((aligned(16))) __bf16 sdo[2][C::kBQ * C::kStride];
+  __shared__ __attribute__((aligned(1024))) char sq[2][C::QT::kBytes];
+  __shared__ __attribute__((aligned(1024))) char sdo[2][C::QT::kBytes];
   __shared__ __attribute__((aligned(16))) float slse[2][C::kBQ];
   __shared__ __attribute__((aligned(16))) float sdel[2][C::kBQ];
 
+  // The workgroups with the first keys see the most query blocks under the
+  // causal mask; they come first in the natural order.
   const int work = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = work / n_ktiles;
   const int kt = work - bh * n_ktiles;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int hi = lane >> 5;
   const int n_q = a.n_q, n_k = a.n_k;
+  const float sl2 = a.scale_log2;
   const int k0 = kt * C::kBK;
-  const int key = k0 + wave * 32 + l32;  // this lane's key (column of S)
+  const int kw = k0 + wave * (C::kKW * 32);  // this wave's first key
 
   const __bf16* qp = static_cast<const __bf16*>(a.q) + (size_t)bh * n_q * D;
   const __bf16* dop = static_cast<const __bf16*>(a.dO) + (size_t)bh * n_q * D;
   const __bf16* kp = static_cast<const __bf16*>(a.k) + (size_t)bh * n_k * D;
   const __bf16* vp = static_cast<const __bf16*>(a.v) + (size_t)bh * n_k * D;
-  const float* lsep = a.lse + (size_t)bh * n_q;
+  const float* lsep = a.lse2 + (size_t)bh * n_q;
   const float* delp = a.delta + (size_t)bh * n_q;
 
-  bf16x8 kf[C::kDC], vf[C::kDC];
+  // K and V rows of this lane's keys (kw + 32 kb + l32) stay in registers as
+  // the B operands of S = Q K^T and dP = dO V^T.
+  bf16x8 kf[C::kKW][C::kDC], vf[C::kKW][C::kDC];
 #pragma unroll
-  for (int c = 0; c < C::kDC; ++c) {
-    if (key < n_k) {
-      kf[c] = *reinterpret_cast<const bf16x8*>(kp + (size_t)key * D + 16 * c + 8 * hi);
-      vf[c] = *reinterpret_cast<const bf16x8*>(vp + (size_t)key * D + 16 * c + 8 * hi);
-    } else {
-      kf[c] = bf16x8{};
-      vf[c] = bf16x8{};
+  for (int kb = 0; kb < C::kKW; ++kb) {
+    const int key = kw + 32 * kb + l32;
+#pragma unroll
+    for (int c = 0; c < C::kDC; ++c) {
+      kf[kb][c] = key < n_k
+                      ? *reinterpret_cast<const bf16x8*>(kp + (size_t)key * D + 16 * c + 8 * hi)
+                      : bf16x8{};
+      vf[kb][c] = key < n_k
+                      ? *reinterpret_cast<const bf16x8*>(vp + (size_t)key * D + 16 * c + 8 * hi)
+                      : bf16x8{};
     }
   }
 
   // Query blocks that can see any key of this workgroup.
   const int qb_first = CAUSAL ? (k0 / C::kBQ) : 0;
-  const int qb_end = (n_q + C::kBQ - 1) / C::kBQ;
-  const int nblocks = (CAUSAL && k0 >= n_q) ? 0 : max(0, qb_end - qb_first);
+  const int nblocks = (CAUSAL && k0 >= n_q) ? 0 : (n_q + C::kBQ - 1) / C::kBQ - qb_first;
 
-  u32x4 qst[C::kLoads], dost[C::kLoads];
-  float lse_st = 0.f, del_st = 0.f;
-  auto gload = [&](int b) {
-    const int qbase = (qb_first + b) * C::kBQ;
+  TileDma<D, C::kBQ, C::kWaves> dma;
+  dma.init(wave, lane);
+  const uint32_t sq_addr = lds_address(&sq[0][0]);
+  const uint32_t sdo_addr = lds_address(&sdo[0][0]);
+  const uint32_t slse_addr = lds_address(&slse[0][0]);
+  const uint32_t sdel_addr = lds_address(&sdel[0][0]);
+  auto load_block = [&](int b, int buf) {
+    const int q0 = (qb_first + b) * C::kBQ;
+    const int valid = n_q - q0;
+    dma.load(qp + (size_t)q0 * D, valid, sq_addr + buf * C::QT::kBytes);
+    dma.load(dop + (size_t)q0 * D, valid, sdo_addr + buf * C::QT::kBytes);
+    // The two row vectors, 16 lanes x 16 bytes each, copied by the last two
+    // waves.  Lane j copies entries 4j .. 4j+3 when entry 4j exists; the up
+    // to three entries read past the last query lie in the next row vector
+    // or in the workspace's slack (their rows are masked).  Lanes whose
+    // entries are all past the end copy entries 0 .. 3 instead.
+    if (wave >= C::kWaves - 2 && lane < C::kBQ / 4) {
+      const float* src = (wave == C::kWaves - 1 ? lsep : delp) + q0;
+      const uint32_t dst = (wave == C::kWaves - 1 ? slse_addr : sdel_addr) + buf * C::kRowVecBytes;
+      lds_dma16(dst, src, (uint32_t)((4 * lane < valid ? 4 * lane : 0) * 4));
+    }
+  };
+
+  f32x16 dk[C::kKW][C::kDB], dv[C::kKW][C::kDB];
 #pragma unroll
-    for (int i = 0; i < C::kLoads; ++i) {
-      const int idx = tid + i * C::kThreads;
-      const int row = idx / C::kChunks;
-      const int ch = idx - row * C::kChunks;
-      const int qi = qbase + row;
-      if (qi < n_q) {
-        qst[i] = *reinterpret_cast<const u32x4*>(qp + (size_t)qi * D + ch * 8);
-        dost[i] = *reinterpret_cast<const u32x4*>(dop + (size_t)qi * D + ch * 8);
-      } else {
-        qst[i] = u32x4{0u, 0u, 0u, 0u};
-        dost[i] = u32x4{0u, 0u, 0u, 0u};
+  for (int kb = 0; kb < C::kKW; ++kb)
+#pragma unroll
+    for (int db = 0; db < C::kDB; ++db) { dk[kb][db] = f32x16{}; dv[kb][db] = f32x16{}; }
+
+  // P and dS of one 32-query sub-block from S and dP (element i of this
+  // lane is query row r0 + 8(i/4) + 4 hi + i%4 of the block), rounded to
+  // bf16 in the order the B operand of the dV / dK products wants.  With
+  // MASK, hidden pairs (query past n_q, key past n_k, key after query when
+  // causal) get P = dS = 0.
+  auto probs = [&](auto mask_tag, const f32x16 (&s)[C::kKW], const f32x16 (&dp)[C::kKW],
+                   const float* lrow, const float* drow, int qbase, int r0,
+                   bf16x8 (&pb)[C::kKW][2], bf16x8 (&dsb)[C::kKW][2]) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int r = r0 + 8 * g4 + 4 * hi;
+      const f32x4 lv = *reinterpret_cast<const f32x4*>(&lrow[r]);
+      const f32x4 dv4 = *reinterpret_cast<const f32x4*>(&drow[r]);
+#pragma unroll
+      for (int kb = 0; kb < C::kKW; ++kb) {
+        const int key = kw + 32 * kb + l32;
+#pragma unroll
+        for (int e = 0; e < 4; e += 2) {
+          const int i = 4 * g4 + e;
+          float p0 = fast_exp2(fmaf(s[kb][i], sl2, -lv[e]));
+          float p1 = fast_exp2(fmaf(s[kb][i + 1], sl2, -lv[e + 1]));
+          if constexpr (MASK) {
+            const int q = qbase + r + e;
+            if (q >= n_q || key >= n_k || (CAUSAL && key > q)) p0 = 0.f;
+            if (q + 1 >= n_q || key >= n_k || (CAUSAL && key > q + 1)) p1 = 0.f;
+          }
+          const bf16x2 pp = to_bf16x2(p0, p1);
+          const bf16x2 dd = to_bf16x2(p0 * (dp[kb][i] - dv4[e]), p1 * (dp[kb][i + 1] - dv4[e + 1]));
+          const int slot = 4 * (g4 & 1) + e;
+          pb[kb][g4 >> 1][slot] = pp[0];
+          pb[kb][g4 >> 1][slot + 1] = pp[1];
+          dsb[kb][g4 >> 1][slot] = dd[0];
+          dsb[kb][g4 >> 1][slot + 1] = dd[1];
+        }
       }
     }
-    if (tid < C::kBQ) {
-      const int qi = qbase + tid;
-      lse_st = (qi < n_q) ? lsep[qi] * kLog2e : 0.f;
-      del_st = (qi < n_q) ? delp[qi] : 0.f;
-    }
-  };
-  auto swrite = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < C::kLoads; ++i) {
-      const int idx = tid + i * C::kThreads;
-      const int row = idx / C::kChunks;
-      const int ch = idx - row * C::kChunks;
-      *reinterpret_cast<u32x4*>(&sq[buf][row * C::kStride + ch * 8]) = qst[i];
-      *reinterpret_cast<u32x4*>(&sdo[buf][row * C::kStride + ch * 8]) = dost[i];
-    }
-    if (tid < C::kBQ) {
-      slse[buf][tid] = lse_st;
-      sdel[buf][tid] = del_st;
-    }
   };
 
-  f32x16 dk[C::kDB], dv[C::kDB];
-#pragma unroll
-  for (int db = 0; db < C::kDB; ++db) { dk[db] = f32x16{}; dv[db] = f32x16{}; }
-
-  const int grp = lane >> 4;
-  const int tr_row = (lane & 15) >> 2;
-  const int tr_col = 16 * (grp & 1) + 4 * (lane & 3);
-
-  if (nblocks > 0) {
-    gload(0);
-    swrite(0);
+  // Blocks needing the mask: the causal diagonal (query blocks starting
+  // before the workgroup's last key), a ragged last query block, or every
+  // block when the workgroup's keys run past n_k.  One loop body serves all
+  // blocks; only the probability step branches on the mask, so the
+  // accumulators stay in one set of registers.
+  int b_lo = 0, b_hi = nblocks;
+  if (CAUSAL) {
+    const int first_clear = k0 + C::kBK - 1;  // first query row that sees every key here
+    b_lo = min(nblocks, max(0, (first_clear - qb_first * C::kBQ + C::kBQ - 1) / C::kBQ));
   }
-  __syncthreads();
+  if (n_q % C::kBQ != 0) b_hi = nblocks - 1;
+  if (k0 + C::kBK > n_k) b_lo = b_hi = nblocks;
+  b_hi = max(b_hi, b_lo);
 
+  if (nblocks > 0) load_block(0, 0);
   for (int b = 0; b < nblocks; ++b) {
     const int buf = b & 1;
-    if (b + 1 < nblocks) gload(b + 1);
+    wait_lds_dma();
+    __syncthreads();
+    if (b + 1 < nblocks) load_block(b + 1, buf ^ 1);
+    const char* qt = sq[buf];
+    const char* gt = sdo[buf];
+    const float* lrow = slse[buf];
+    const float* drow = sdel[buf];
     const int qbase = (qb_first + b) * C::kBQ;
+    const bool masked = b < b_lo || b >= b_hi;
 
 #pragma unroll
     for (int qs = 0; qs < C::kQS; ++qs) {
-      const int qrow0 = qbase + qs * 32;
-      // Skip sub-blocks entirely above this wave's keys (all hidden).
-      if (CAUSAL && qrow0 + 31 < k0 + wave * 32) continue;
-      f32x16 s = f32x16{}, dp = f32x16{};
+      const int r0 = qs * 32;
+      // Sub-blocks entirely before this wave's first key are all hidden.
+      if (CAUSAL && qbase + r0 + 31 < kw) continue;
+      f32x16 s[C::kKW], dp[C::kKW];
+#pragma unroll
+      for (int kb = 0; kb < C::kKW; ++kb) { s[kb] = f32x16{}; dp[kb] = f32x16{}; }
 #pragma unroll
       for (int c = 0; c < C::kDC; ++c) {
-        const int off = (qs * 32 + l32) * C::kStride + 16 * c + 8 * hi;
-        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&sq[buf][off]);
-        const bf16x8 ga = *reinterpret_cast<const bf16x8*>(&sdo[buf][off]);
-        s = mfma_bf16(qa, kf[c], s);
-        dp = mfma_bf16(ga, vf[c], dp);
-      }
-      // P and dS; element i is query row qrow0 + 8*(i/4) + 4*hi + (i%4).
-      f32x16 p, ds;
+        const bf16x8 qa = C::QT::read_rows(qt, r0, c, lane);
+        const bf16x8 ga = C::QT::read_rows(gt, r0, c, lane);
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int r0 = qs * 32 + 8 * g4 + 4 * hi;
-        const f32x4 lv = *reinterpret_cast<const f32x4*>(&slse[buf][r0]);
-        const f32x4 dv4 = *reinterpret_cast<const f32x4*>(&sdel[buf][r0]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 4 * g4 + e;
-          const int qi = qbase + r0 + e;
-          float pv = fast_exp2(fmaf(s[i], a.scale_log2, -lv[e]));
-          const bool hide = qi >= n_q || key >= n_k || (CAUSAL && key > qi);
-          pv = hide ? 0.f : pv;
-          p[i] = pv;
-          ds[i] = pv * (dp[i] - dv4[e]);
+        for (int kb = 0; kb < C::kKW; ++kb) {
+          s[kb] = mfma_bf16(qa, kf[kb][c], s[kb]);
+          dp[kb] = mfma_bf16(ga, vf[kb][c], dp[kb]);
         }
       }
-      // dV^T += dO^T P and dK^T += Q^T dS, 16 queries per step.
+      bf16x8 pb[C::kKW][2], dsb[C::kKW][2];
+      if (masked)
+        probs(T{}, s, dp, lrow, drow, qbase, r0, pb, dsb);
+      else
+        probs(F{}, s, dp, lrow, drow, qbase, r0, pb, dsb);
+      // dV^T += dO^T P and dK^T += Q^T dS, 16 queries per step; the dO^T and
+      // Q^T operands serve both key blocks.
 #pragma unroll
-      for (int c2 = 0; c2 < 2; ++c2) {
-        bf16x8 pb, dsb;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          pb[e] = (__bf16)p[8 * c2 + e];
-          dsb[e] = (__bf16)ds[8 * c2 + e];
-        }
-        const int ra = qs * 32 + 16 * c2 + 4 * hi + tr_row;
+      for (int c2 = 0; c2 < 2; ++c2)
 #pragma unroll
         for (int db = 0; db < C::kDB; ++db) {
-          const int col = 32 * db + tr_col;
-          const bf16x4 ga = lds_read_tr16(&sdo[buf][ra * C::kStride + col]);
-          const bf16x4 gb = lds_read_tr16(&sdo[buf][(ra + 8) * C::kStride + col]);
-          const bf16x8 gop = {ga[0], ga[1], ga[2], ga[3], gb[0], gb[1], gb[2], gb[3]};
-          dv[db] = mfma_bf16(gop, pb, dv[db]);
-          const bf16x4 qa = lds_read_tr16(&sq[buf][ra * C::kStride + col]);
-          const bf16x4 qb2 = lds_read_tr16(&sq[buf][(ra + 8) * C::kStride + col]);
-          const bf16x8 qop = {qa[0], qa[1], qa[2], qa[3], qb2[0], qb2[1], qb2[2], qb2[3]};
-          dk[db] = mfma_bf16(qop, dsb, dk[db]);
+          const bf16x8 gtr = C::QT::read_cols_tr(gt, r0 + 16 * c2, 32 * db, lane);
+          const bf16x8 qtr = C::QT::read_cols_tr(qt, r0 + 16 * c2, 32 * db, lane);
+#pragma unroll
+          for (int kb = 0; kb < C::kKW; ++kb) {
+            dv[kb][db] = mfma_bf16(gtr, pb[kb][c2], dv[kb][db]);
+            dk[kb][db] = mfma_bf16(qtr, dsb[kb][c2], dk[kb][db]);
+          }
         }
-      }
     }
-
-    if (b + 1 < nblocks) swrite(buf ^ 1);
-    __syncthreads();
   }
 
-  if (key < n_k) {
-    __bf16* dkp = static_cast<__bf16*>(a.dk) + ((size_t)bh * n_k + key) * D;
-    __bf16* dvp = static_cast<__bf16*>(a.dv) + ((size_t)bh * n_k + key) * D;
 #pragma unroll
-    for (int db = 0; db < C::kDB; ++db)
+  for (int kb = 0; kb < C::kKW; ++kb) {
+    const int key = kw + 32 * kb + l32;
+    if (key < n_k) {
+      __bf16* dkp = static_cast<__bf16*>(a.dk) + ((size_t)bh * n_k + key) * D;
+      __bf16* dvp = static_cast<__bf16*>(a.dv) + ((size_t)bh * n_k + key) * D;
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        bf16x4 rk, rv;
+      for (int db = 0; db < C::kDB; ++db)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          rk[e] = (__bf16)(dk[db][4 * g4 + e] * a.scale);
-          rv[e] = (__bf16)dv[db][4 * g4 + e];
+        for (int g4 = 0; g4 < 4; ++g4) {
+          bf16x4 rk, rv;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            rk[e] = (__bf16)(dk[kb][db][4 * g4 + e] * a.scale);
+            rv[e] = (__bf16)dv[kb][db][4 * g4 + e];
+          }
+          *reinterpret_cast<bf16x4*>(dkp + 32 * db + 8 * g4 + 4 * hi) = rk;
+          *reinterpret_cast<bf16x4*>(dvp + 32 * db + 8 * g4 + 4 * hi) = rv;
         }
-        *reinterpret_cast<bf16x4*>(dkp + 32 * db + 8 * g4 + 4 * hi) = rk;
-        *reinterpret_cast<bf16x4*>(dvp + 32 * db + 8 * g4 + 4 * hi) = rv;
-      }
+    }
   }
 }
 
@@ -270,24 +315,21 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16_kernel(BwdArgs a, int n_kti
 
 template <int D>
 struct DqCfg {
-  static constexpr int kWaves = 4;
+  static constexpr int kWaves = 8;
   static constexpr int kThreads = kWaves * 64;
-  static constexpr int kBM = kWaves * 32;        // queries per workgroup
+  static constexpr int kBM = kWaves * 32;        // queries per workgroup, 32 per wave
   static constexpr int kBN = 64;                 // keys per block
   static constexpr int kKB = kBN / 32;
   static constexpr int kDC = D / 16;
   static constexpr int kDB = D / 32;
-  static constexpr int kStride = D + 16;
-  static constexpr int kChunks = D / 8;
-  static constexpr int kLoads = kBN * kChunks / kThreads;
-  static_assert(kLoads * kThreads == kBN * kChunks, "tile load split");
+  using KV = Tile<D, kBN>;
 };
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void bwd_dq_bf16_kernel(BwdArgs a, int n_qtiles) {
+__global__ __launch_bounds__(512) void bwd_dq_bf16_kernel(BwdArgs a, int n_qtiles) {
   using C = DqCfg<D>;
-  __shared__ __attribute__((aligned(16))) __bf16 sk[2][C::kBN * C::kStride];
-  __shared__ __attribute__((aligned(16))) __bf16 sv[2][C::kBN * C::kStride];
+  __shared__ __attribute__((aligned(1024))) char sk[2][C::KV::kBytes];
+  __shared__ __attribute__((aligned(1024))) char sv[2][C::KV::kBytes];
 
   const int work = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = work / n_qtiles;
@@ -295,11 +337,12 @@ __global__ __launch_bounds__(256) void bwd_dq_bf16_kernel(BwdArgs a, int n_qtile
   if (CAUSAL) qt = n_qtiles - 1 - qt;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int hi = lane >> 5;
   const int n_q = a.n_q, n_k = a.n_k;
+  const float sl2 = a.scale_log2;
   const int q0 = qt * C::kBM;
   const int qw = q0 + wave * 32;
   const int qi = qw + l32;  // this lane's query (column of S^T)
@@ -320,97 +363,78 @@ __global__ __launch_bounds__(256) void bwd_dq_bf16_kernel(BwdArgs a, int n_qtile
       gf[c] = bf16x8{};
     }
   }
-  const float lse2 = (qi < n_q) ? a.lse[(size_t)bh * n_q + qi] * kLog2e : 0.f;
+  // Rows past n_q have zero Q and dO, so their (unstored) dQ stays finite.
+  const float lse2 = (qi < n_q) ? a.lse2[(size_t)bh * n_q + qi] : 0.f;
   const float dlt = (qi < n_q) ? a.delta[(size_t)bh * n_q + qi] : 0.f;
 
   const int q_end = min(n_q, q0 + C::kBM);
   const int k_end = CAUSAL ? min(n_k, q_end) : n_k;
   const int ntiles = (k_end + C::kBN - 1) / C::kBN;
 
-  u32x4 kst[C::kLoads], vst[C::kLoads];
-  auto gload = [&](int t) {
-#pragma unroll
-    for (int i = 0; i < C::kLoads; ++i) {
-      const int idx = tid + i * C::kThreads;
-      const int row = idx / C::kChunks;
-      const int ch = idx - row * C::kChunks;
-      const int kj = t * C::kBN + row;
-      if (kj < n_k) {
-        kst[i] = *reinterpret_cast<const u32x4*>(kp + (size_t)kj * D + ch * 8);
-        vst[i] = *reinterpret_cast<const u32x4*>(vp + (size_t)kj * D + ch * 8);
-      } else {
-        kst[i] = u32x4{0u, 0u, 0u, 0u};
-        vst[i] = u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-  };
-  auto swrite = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < C::kLoads; ++i) {
-      const int idx = tid + i * C::kThreads;
-      const int row = idx / C::kChunks;
-      const int ch = idx - row * C::kChunks;
-      *reinterpret_cast<u32x4*>(&sk[buf][row * C::kStride + ch * 8]) = kst[i];
-      *reinterpret_cast<u32x4*>(&sv[buf][row * C::kStride + ch * 8]) = vst[i];
-    }
+  TileDma<D, C::kBN, C::kWaves> dma;
+  dma.init(wave, lane);
+  const uint32_t sk_addr = lds_address(&sk[0][0]);
+  const uint32_t sv_addr = lds_address(&sv[0][0]);
+  auto load_tile = [&](int t, int buf) {
+    const int k0 = t * C::kBN;
+    dma.load(kp + (size_t)k0 * D, n_k - k0, sk_addr + buf * C::KV::kBytes);
+    dma.load(vp + (size_t)k0 * D, n_k - k0, sv_addr + buf * C::KV::kBytes);
   };
 
   f32x16 dq[C::kDB];
 #pragma unroll
   for (int db = 0; db < C::kDB; ++db) dq[db] = f32x16{};
 
-  const int grp = lane >> 4;
-  const int tr_row = (lane & 15) >> 2;
-  const int tr_col = 16 * (grp & 1) + 4 * (lane & 3);
-
-  gload(0);
-  swrite(0);
-  __syncthreads();
-
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < ntiles) gload(t + 1);
+  auto block = [&](auto mask_tag, auto buf_tag, int t) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    constexpr int BUFC = decltype(buf_tag)::value;
+    const int buf = BUFC >= 0 ? BUFC : (t & 1);
+    wait_lds_dma();
+    __syncthreads();
+    if (t + 1 < ntiles) load_tile(t + 1, buf ^ 1);
+    const char* ks = sk[buf];
+    const char* vs = sv[buf];
     const int k0 = t * C::kBN;
 #pragma unroll
     for (int kb = 0; kb < C::kKB; ++kb) {
-      if (CAUSAL && k0 + kb * 32 > qw + 31) continue;  // all keys hidden from this wave
+      if (MASK && CAUSAL && k0 + kb * 32 > qw + 31) continue;  // every key hidden from this wave
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
       for (int c = 0; c < C::kDC; ++c) {
-        const int off = (kb * 32 + l32) * C::kStride + 16 * c + 8 * hi;
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&sk[buf][off]);
-        const bf16x8 va = *reinterpret_cast<const bf16x8*>(&sv[buf][off]);
-        s = mfma_bf16(ka, qf[c], s);
-        dp = mfma_bf16(va, gf[c], dp);
+        s = mfma_bf16(C::KV::read_rows(ks, kb * 32, c, lane), qf[c], s);
+        dp = mfma_bf16(C::KV::read_rows(vs, kb * 32, c, lane), gf[c], dp);
       }
-      f32x16 ds;
+      bf16x8 dsb[2];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int kj = k0 + kb * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
-        float pv = fast_exp2(fmaf(s[i], a.scale_log2, -lse2));
-        const bool hide = qi >= n_q || kj >= n_k || (CAUSAL && kj > qi);
-        pv = hide ? 0.f : pv;
-        ds[i] = pv * (dp[i] - dlt);
-      }
-#pragma unroll
-      for (int c2 = 0; c2 < 2; ++c2) {
-        bf16x8 dsb;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) dsb[e] = (__bf16)ds[8 * c2 + e];
-        const int ra = kb * 32 + 16 * c2 + 4 * hi + tr_row;
-#pragma unroll
-        for (int db = 0; db < C::kDB; ++db) {
-          const int col = 32 * db + tr_col;
-          const bf16x4 x = lds_read_tr16(&sk[buf][ra * C::kStride + col]);
-          const bf16x4 y = lds_read_tr16(&sk[buf][(ra + 8) * C::kStride + col]);
-          const bf16x8 kop = {x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
-          dq[db] = mfma_bf16(kop, dsb, dq[db]);
+      for (int i = 0; i < 16; i += 2) {
+        float p0 = fast_exp2(fmaf(s[i], sl2, -lse2));
+        float p1 = fast_exp2(fmaf(s[i + 1], sl2, -lse2));
+        if constexpr (MASK) {
+          const int kj = k0 + kb * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
+          if (kj >= n_k || (CAUSAL && kj > qi)) p0 = 0.f;
+          if (kj + 1 >= n_k || (CAUSAL && kj + 1 > qi)) p1 = 0.f;
         }
+        const bf16x2 dd = to_bf16x2(p0 * (dp[i] - dlt), p1 * (dp[i + 1] - dlt));
+        dsb[i >> 3][i & 7] = dd[0];
+        dsb[i >> 3][(i & 7) + 1] = dd[1];
       }
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+        for (int db = 0; db < C::kDB; ++db)
+          dq[db] = mfma_bf16(C::KV::read_cols_tr(ks, kb * 32 + 16 * c2, 32 * db, lane), dsb[c2], dq[db]);
     }
-    if (t + 1 < ntiles) swrite(buf ^ 1);
-    __syncthreads();
+  };
+
+  const int n_full = min(ntiles, (CAUSAL ? min(q0 + 1, n_k) : n_k) / C::kBN);
+  load_tile(0, 0);
+  int t = 0;
+  for (; t + 1 < n_full; t += 2) {
+    block(F{}, Buf<0>{}, t);
+    block(F{}, Buf<1>{}, t + 1);
   }
+  for (; t < n_full; ++t) block(F{}, Buf<0>{}, t);
+  for (; t < ntiles; ++t) block(T{}, Buf<-1>{}, t);
 
   if (qi < n_q) {
     __bf16* dqp = static_cast<__bf16*>(a.dq) + ((size_t)bh * n_q + qi) * D;
@@ -471,7 +495,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_f32_kernel(BwdArgs a, int n_ktil
   const float* dop = static_cast<const float*>(a.dO) + (size_t)bh * n_q * D;
   const float* kp = static_cast<const float*>(a.k) + (size_t)bh * n_k * D;
   const float* vp = static_cast<const float*>(a.v) + (size_t)bh * n_k * D;
-  const float* lsep = a.lse + (size_t)bh * n_q;
+  const float* lsep = a.lse2 + (size_t)bh * n_q;
   const float* delp = a.delta + (size_t)bh * n_q;
 
   // K and V rows of this lane's key, as B operands (d = 2c + hi).
@@ -506,7 +530,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_f32_kernel(BwdArgs a, int n_ktil
     }
     if (tid < C::kBS) {
       const int qi = qbase + tid;
-      lse_st = (qi < n_q) ? lsep[qi] * kLog2e : 0.f;
+      lse_st = (qi < n_q) ? lsep[qi] : 0.f;
       del_st = (qi < n_q) ? delp[qi] : 0.f;
     }
   };
@@ -626,7 +650,7 @@ __global__ __launch_bounds__(256) void bwd_dq_f32_kernel(BwdArgs a, int n_qtiles
     qreg[c] = (qi < n_q) ? qp[(size_t)qi * D + 2 * c + hi] : 0.f;
     greg[c] = (qi < n_q) ? dop[(size_t)qi * D + 2 * c + hi] : 0.f;
   }
-  const float lse2 = (qi < n_q) ? a.lse[(size_t)bh * n_q + qi] * kLog2e : 0.f;
+  const float lse2 = (qi < n_q) ? a.lse2[(size_t)bh * n_q + qi] : 0.f;
   const float dlt = (qi < n_q) ? a.delta[(size_t)bh * n_q + qi] : 0.f;
 
   const int q_end = min(n_q, q0 + C::kBlk);
@@ -725,22 +749,24 @@ hipError_t launch_raw(const void* kernel, int grid, int block, void** params, hi
 
 template <int D, bool CAUSAL>
 hipError_t dkdv_bf16_t(const BwdArgs& a, hipStream_t s) {
-  const int n_ktiles = (a.n_k + DkdvCfg<D>::kBK - 1) / DkdvCfg<D>::kBK;
+  using C = DkdvCfg<D>;
+  const int n_ktiles = (a.n_k + C::kBK - 1) / C::kBK;
   BwdArgs args = a;
   int nt = n_ktiles;
   void* params[] = {&args, &nt};
   return launch_raw(reinterpret_cast<const void*>(bwd_dkdv_bf16_kernel<D, CAUSAL>),
-                    n_ktiles * a.BH, 256, params, s);
+                    n_ktiles * a.BH, C::kThreads, params, s);
 }
 
 template <int D, bool CAUSAL>
 hipError_t dq_bf16_t(const BwdArgs& a, hipStream_t s) {
-  const int n_qtiles = (a.n_q + DqCfg<D>::kBM - 1) / DqCfg<D>::kBM;
+  using C = DqCfg<D>;
+  const int n_qtiles = (a.n_q + C::kBM - 1) / C::kBM;
   BwdArgs args = a;
   int nt = n_qtiles;
   void* params[] = {&args, &nt};
   return launch_raw(reinterpret_cast<const void*>(bwd_dq_bf16_kernel<D, CAUSAL>),
-                    n_qtiles * a.BH, 256, params, s);
+                    n_qtiles * a.BH, C::kThreads, params, s);
 }
 
 template <int D, bool CAUSAL>
@@ -750,7 +776,7 @@ hipError_t dkdv_f32_t(const BwdArgs& a, hipStream_t s) {
   int nt = n_ktiles;
   void* params[] = {&args, &nt};
   return launch_raw(reinterpret_cast<const void*>(bwd_dkdv_f32_kernel<D, CAUSAL>),
-                    n_ktiles * a.BH, 256, params, s);
+                    n_ktiles * a.BH, F32BwdCfg<D>::kThreads, params, s);
 }
 
 template <int D, bool CAUSAL>
@@ -760,20 +786,22 @@ hipError_t dq_f32_t(const BwdArgs& a, hipStream_t s) {
   int nt = n_qtiles;
   void* params[] = {&args, &nt};
   return launch_raw(reinterpret_cast<const void*>(bwd_dq_f32_kernel<D, CAUSAL>),
-                    n_qtiles * a.BH, 256, params, s);
+                    n_qtiles * a.BH, F32BwdCfg<D>::kThreads, params, s);
 }
 
-template <int D, typename T>
+template <int D, typename TT>
 hipError_t preprocess_t(const BwdArgs& a, hipStream_t s) {
-  constexpr int kRowsPerBlock = 256 / (D / (16 / sizeof(T)));
+  constexpr int kRowsPerBlock = 256 / (D / (16 / sizeof(TT)));
   const long rows = (long)a.BH * a.n_q;
   const long grid = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
-  const T* o = static_cast<const T*>(a.o);
-  const T* g = static_cast<const T*>(a.dO);
+  const TT* o = static_cast<const TT*>(a.o);
+  const TT* g = static_cast<const TT*>(a.dO);
+  const float* lse = a.lse;
   float* delta = a.delta;
+  float* lse2 = a.lse2;
   long r = rows;
-  void* params[] = {&o, &g, &delta, &r};
-  return hipLaunchKernel(reinterpret_cast<const void*>(bwd_preprocess_kernel<D, T>),
+  void* params[] = {&o, &g, &lse, &delta, &lse2, &r};
+  return hipLaunchKernel(reinterpret_cast<const void*>(bwd_preprocess_kernel<D, TT>),
                          dim3((unsigned)grid), dim3(256), params, 0, s);
 }
 

@@ -34,6 +34,7 @@
 // 4 waves x 32 query rows and 32-key blocks; probabilities stay in fp32.
 #include "fa_internal.hpp"
 #include "fa_device.hpp"
+#include "fa_tiles.hpp"
 
 #include <cmath>
 #include <type_traits>
@@ -50,20 +51,8 @@ struct Bf16FwdCfg {
   static constexpr int kKB = kBN / 32;             // 32-key sub-blocks
   static constexpr int kDC = D / 16;               // 16-wide chunks of the head dim
   static constexpr int kDB = D / 32;               // 32-row blocks of O^T
-  static constexpr int kRowBytes = 2 * D;          // one K or V row in LDS
-  static constexpr int kChunks = D / 8;            // 16-byte chunks per row
-  static constexpr int kTileBytes = kBN * kRowBytes;
-  static constexpr int kDmaLoads = kTileBytes / 1024;   // 1 KiB wave loads per tile
-  static_assert(kDmaLoads * 1024 == kTileBytes, "tile load split");
+  using KV = Tile<D, kBN>;                         // one K or V block in LDS
 };
-
-// LDS tiles hold K or V rows unpadded; the 16-byte chunk c of row r sits at
-// chunk position c ^ (r mod chunks-per-row), so the 32 rows read together by
-// a matrix-core operand load fall into different banks.
-template <int D>
-__device__ __forceinline__ int swz(int row, int chunk) {
-  return row * Bf16FwdCfg<D>::kRowBytes + ((chunk ^ (row % Bf16FwdCfg<D>::kChunks)) << 4);
-}
 
 // Largest amount by which a row's scores may exceed the reference maximum
 // used for its exponentials, in log2 units: probabilities stay below 2^8, so
@@ -74,8 +63,8 @@ constexpr float kLazyRescale = 8.0f;
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdArgs a, int n_qtiles) {
   using C = Bf16FwdCfg<D>;
-  __shared__ __attribute__((aligned(1024))) char sk[2][C::kTileBytes];
-  __shared__ __attribute__((aligned(1024))) char sv[2][C::kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char sk[2][C::KV::kBytes];
+  __shared__ __attribute__((aligned(1024))) char sv[2][C::KV::kBytes];
 
   const int work = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = work / n_qtiles;
@@ -111,46 +100,20 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdArgs a, int n_qtiles) 
   const int k_end = CAUSAL ? min(n_k, q_end) : n_k;
   const int ntiles = (k_end + C::kBN - 1) / C::kBN;
 
-  // Direct global -> LDS loads: lane j of 1 KiB load number L writes LDS
-  // bytes [1024 L + 16 j, +16) of the tile, which hold row `dma_row`,
-  // logical chunk `dma_chunk` of that tile.  Wave w issues loads w, w + 8, ...
-  constexpr int kMine = (C::kDmaLoads + C::kWaves - 1) / C::kWaves;
-  int dma_row[kMine], dma_col[kMine];
-#pragma unroll
-  for (int i = 0; i < kMine; ++i) {
-    const int L = wave + i * C::kWaves;
-    const int off = L * 1024 + 16 * lane;
-    dma_row[i] = off / C::kRowBytes;
-    dma_col[i] = (((off % C::kRowBytes) >> 4) ^ (dma_row[i] % C::kChunks)) * 16;  // bytes
-  }
+  TileDma<D, C::kBN, C::kWaves> dma;
+  dma.init(wave, lane);
   const uint32_t sk_addr = lds_address(&sk[0][0]);
   const uint32_t sv_addr = lds_address(&sv[0][0]);
   auto load_tile = [&](int t, int buf) {
     const int k0 = t * C::kBN;
-    const __bf16* kb_ = kp + (size_t)k0 * D;
-    const __bf16* vb_ = vp + (size_t)k0 * D;
-    const int last = n_k - 1 - k0;  // rows past the last key repeat it (masked later)
-#pragma unroll
-    for (int i = 0; i < kMine; ++i) {
-      const int L = wave + i * C::kWaves;
-      if (L < C::kDmaLoads) {
-        const uint32_t voff = (uint32_t)(min(dma_row[i], last) * C::kRowBytes + dma_col[i]);
-        const uint32_t dst = buf * C::kTileBytes + L * 1024;
-        lds_dma16(sk_addr + dst, kb_, voff);
-        lds_dma16(sv_addr + dst, vb_, voff);
-      }
-    }
+    dma.load(kp + (size_t)k0 * D, n_k - k0, sk_addr + buf * C::KV::kBytes);
+    dma.load(vp + (size_t)k0 * D, n_k - k0, sv_addr + buf * C::KV::kBytes);
   };
 
   f32x16 oacc[C::kDB];
 #pragma unroll
   for (int db = 0; db < C::kDB; ++db) oacc[db] = f32x16{};
   float m = -INFINITY, l = 0.f;
-
-  // Lane coordinates of the transposing V read (see fa_device.hpp).
-  const int grp = lane >> 4;
-  const int tr_row = (lane & 15) >> 2;
-  const int tr_col = 16 * (grp & 1) + 4 * (lane & 3);
 
   // One key block: wait for it, start the next block's copy, then
   // S^T = K Q^T, softmax, O^T += V^T P^T.  MASK selects the variant with the
@@ -178,9 +141,7 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdArgs a, int n_qtiles) 
     for (int c = 0; c < C::kDC; ++c) {
 #pragma unroll
       for (int kb = 0; kb < C::kKB; ++kb) {
-        const bf16x8 ka =
-            *reinterpret_cast<const bf16x8*>(ks + swz<D>(kb * 32 + l32, 2 * c + hi));
-        s[kb] = mfma_bf16(ka, qf[c], s[kb]);
+        s[kb] = mfma_bf16(C::KV::read_rows(ks, kb * 32, c, lane), qf[c], s[kb]);
       }
     }
 
@@ -243,22 +204,13 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdArgs a, int n_qtiles) 
 
     // O^T += V^T P^T, 16 keys per matrix-core step.
 #pragma unroll
-    for (int kb = 0; kb < C::kKB; ++kb) {
+    for (int kb = 0; kb < C::kKB; ++kb)
 #pragma unroll
-      for (int c2 = 0; c2 < 2; ++c2) {
-        const int key_a = kb * 32 + 16 * c2 + 4 * hi + tr_row;
+      for (int c2 = 0; c2 < 2; ++c2)
 #pragma unroll
-        for (int db = 0; db < C::kDB; ++db) {
-          const int col = 32 * db + tr_col;
-          const int ca = swz<D>(key_a, col >> 3) + 2 * (col & 7);
-          const int cb = swz<D>(key_a + 8, col >> 3) + 2 * (col & 7);
-          const bf16x4 va = lds_read_tr16(reinterpret_cast<const __bf16*>(vs + ca));
-          const bf16x4 vb = lds_read_tr16(reinterpret_cast<const __bf16*>(vs + cb));
-          const bf16x8 vop = {va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]};
-          oacc[db] = mfma_bf16(vop, pb[kb][c2], oacc[db]);
-        }
-      }
-    }
+        for (int db = 0; db < C::kDB; ++db)
+          oacc[db] = mfma_bf16(C::KV::read_cols_tr(vs, kb * 32 + 16 * c2, 32 * db, lane),
+                               pb[kb][c2], oacc[db]);
   };
 
   // Leading blocks that need no mask for any row of the workgroup, two at a

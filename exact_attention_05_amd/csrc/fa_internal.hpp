@@ -28,8 +28,9 @@ struct BwdArgs {
   const void* v;
   const void* o;
   const void* dO;
-  const float* lse;
-  float* delta;     // (B,H,n_q) float32 row sums of dO * O
+  const float* lse;  // (B,H,n_q) natural-log LSE saved by the forward pass
+  float* delta;     // workspace: (B,H,n_q) float32 row sums of dO * O
+  float* lse2;      // workspace: (B,H,n_q) float32 LSE * log2(e)
   void* dq;
   void* dk;
   void* dv;

@@ -1,0 +1,91 @@
+// LDS tiles of bf16 rows (K, V, Q or dO blocks) for the gfx950 kernels:
+// layout, direct global -> LDS filling, and the two operand reads the matrix
+// cores need.
+//
+// Layout: a tile is ROWS rows of D bf16 values, unpadded (2*D bytes per
+// row).  The 16-byte chunk c of row r is stored at chunk position
+// c ^ (r mod D/8): 32 rows read at the same logical chunk by one
+// matrix-core operand load then fall into different LDS banks.
+//
+// Filling: the tile is copied with global_load_lds_dwordx4, 1 KiB per wave
+// instruction (lane j writes bytes [16 j, 16 j + 16) of its KiB).  Wave w of
+// a WAVES-wave workgroup issues KiB number w, w + WAVES, ...  Rows past the
+// last valid row repeat the last valid row, so nothing outside the tensor is
+// read; callers mask those rows.
+#pragma once
+
+#include "fa_device.hpp"
+
+namespace fa {
+
+template <int D, int ROWS>
+struct Tile {
+  static constexpr int kRowBytes = 2 * D;
+  static constexpr int kChunks = D / 8;            // 16-byte chunks per row
+  static constexpr int kBytes = ROWS * kRowBytes;
+  static constexpr int kKiB = kBytes / 1024;
+  static_assert(kKiB * 1024 == kBytes, "a tile is a whole number of KiB");
+
+  // Byte offset of (row, 16-byte logical chunk) within the tile.
+  __device__ static __forceinline__ int offset(int row, int chunk) {
+    return row * kRowBytes + ((chunk ^ (row % kChunks)) << 4);
+  }
+
+  // A-operand read for v_mfma_f32_32x32x16_bf16 from rows row0 .. row0+31:
+  // lane l gets row row0 + l%32, columns 16c + 8(l/32) .. +7.
+  __device__ static __forceinline__ bf16x8 read_rows(const char* tile, int row0, int c, int lane) {
+    return *reinterpret_cast<const bf16x8*>(tile + offset(row0 + (lane & 31), 2 * c + (lane >> 5)));
+  }
+
+  // A-operand read of the TRANSPOSED tile for v_mfma_f32_32x32x16_bf16:
+  // operand rows are tile columns col0 .. col0+31, operand k-slots are tile
+  // rows.  Lane l gets columns col0 + l%32 of tile rows
+  //   r0 + 4(l/32) + 0..3  and  r0 + 8 + 4(l/32) + 0..3,
+  // i.e. the 16-row chunk r0 .. r0+15 in the order the 32x32 accumulator
+  // layout lists its rows (element i of lane l is row 8(i/4) + 4(l/32) + i%4),
+  // so an accumulator converted to bf16 can be the matching B operand.
+  __device__ static __forceinline__ bf16x8 read_cols_tr(const char* tile, int r0, int col0, int lane) {
+    const int row = r0 + 4 * (lane >> 5) + ((lane & 15) >> 2);
+    const int col = col0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    const int byte_in_chunk = 2 * (col & 7);
+    const bf16x4 a = lds_read_tr16(reinterpret_cast<const __bf16*>(tile + offset(row, col >> 3) + byte_in_chunk));
+    const bf16x4 b = lds_read_tr16(reinterpret_cast<const __bf16*>(tile + offset(row + 8, col >> 3) + byte_in_chunk));
+    return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  }
+};
+
+// Per-lane state for filling Tile<D, ROWS> tiles by direct copies.
+template <int D, int ROWS, int WAVES>
+struct TileDma {
+  using T = Tile<D, ROWS>;
+  static constexpr int kMine = (T::kKiB + WAVES - 1) / WAVES;  // KiB copies per wave
+  int row[kMine];
+  int col_bytes[kMine];
+  int wave;
+
+  __device__ __forceinline__ void init(int wave_, int lane) {
+    wave = wave_;
+#pragma unroll
+    for (int i = 0; i < kMine; ++i) {
+      const int off = (wave + i * WAVES) * 1024 + 16 * lane;
+      row[i] = off / T::kRowBytes;
+      col_bytes[i] = (((off % T::kRowBytes) >> 4) ^ (row[i] % T::kChunks)) * 16;
+    }
+  }
+
+  // Copy rows [0, ROWS) starting at `src` (row 0 of the tile in global
+  // memory, rows of D bf16) into the tile at LDS byte address `lds`.  Rows at
+  // or past `valid` repeat row valid - 1 (valid >= 1).
+  __device__ __forceinline__ void load(const __bf16* src, int valid, uint32_t lds) const {
+#pragma unroll
+    for (int i = 0; i < kMine; ++i) {
+      const int L = wave + i * WAVES;
+      if (L < T::kKiB) {
+        const uint32_t voff = (uint32_t)(min(row[i], valid - 1) * T::kRowBytes + col_bytes[i]);
+        lds_dma16(lds + L * 1024, src, voff);
+      }
+    }
+  }
+};
+
+}  // namespace fa

@@ -33,14 +33,15 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  * Layout   q, o, dO, dq: contiguous (B, H, n_q, d); k, v, dk, dv: contiguous
- *          (B, H, n_k, d); lse and delta: contiguous (B, H, n_q) float32.
+ *          (B, H, n_k, d); lse: contiguous (B, H, n_q) float32.
  *          Rows are row-major with d innermost.
  * dtype    FA_DTYPE_BF16: q, k, v, o, dO, dq, dk, dv hold bfloat16 and all
  *          accumulation is float32; results are rounded to nearest-even.
  *          FA_DTYPE_FP32: those tensors hold float32 and every product runs
- *          on float32 matrix cores.  lse and delta are always float32.
+ *          on float32 matrix cores.  lse is always float32.
  * Pointers All tensor pointers are device pointers.  q, k, v, o, dO, dq, dk,
- *          dv must be 16-byte aligned; lse and delta 4-byte aligned.
+ *          dv must be 16-byte aligned, lse 4-byte aligned, the backward
+ *          workspace 256-byte aligned.
  * Ownership The caller owns every buffer.  The library allocates and frees
  *          nothing, never synchronises, and does not modify inputs.  Outputs
  *          are fully overwritten (never accumulated into) and must not alias
@@ -88,9 +89,10 @@ int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse,
                int B, int H, int n_q, int n_k, int d, float scale, int causal,
                int dtype, void* stream);
 
-/* Bytes of device workspace fa_backward needs for these sizes (the float32
- * row sums D, B*H*n_q*4 bytes rounded up to 256).  Returns 0 for invalid or
- * unsupported sizes. */
+/* Bytes of device workspace the backward pass needs for these sizes: two
+ * float32 (B,H,n_q) row vectors (the row sums D and LSE * log2(e)), each
+ * padded to a multiple of 256 bytes with at least 16 bytes of slack.
+ * Returns 0 for invalid or unsupported sizes. */
 size_t fa_backward_workspace_size(int B, int H, int n_q, int n_k, int d, int dtype);
 
 /* Backward pass from the saved o and lse of fa_forward (same q, k, v, scale,
@@ -104,22 +106,25 @@ int fa_backward(const void* q, const void* k, const void* v, const void* o,
                 int B, int H, int n_q, int n_k, int d, float scale, int causal,
                 int dtype, void* stream);
 
-/* Backward stage 1: delta_i = sum_c dO_ic * o_ic in float32, (B,H,n_q).
- * The row term D of the softmax gradient, taken from the saved output. */
-int fa_backward_preprocess(const void* o, const void* dO, float* delta,
+/* Backward stage 1: writes into `workspace` the float32 row sums
+ * D_i = sum_c dO_ic * o_ic (the row term of the softmax gradient, from the
+ * saved output) and LSE_i * log2(e).  Workspace as for fa_backward. */
+int fa_backward_preprocess(const void* o, const void* dO, const float* lse,
+                           void* workspace, size_t workspace_bytes,
                            int B, int H, int n_q, int d, int dtype, void* stream);
 
-/* Backward stage 2: dk and dv.  One pass over the query blocks for every key
- * block, recomputing P from lse, with dV = P^T dO and dK = scale dS^T Q. */
+/* Backward stage 2: dk and dv, from the workspace of stage 1.  One pass over
+ * the query blocks for every key block, recomputing P from the saved LSE,
+ * with dV = P^T dO and dK = scale dS^T Q. */
 int fa_backward_dkdv(const void* q, const void* k, const void* v, const void* dO,
-                     const float* lse, const float* delta, void* dk, void* dv,
+                     const void* workspace, size_t workspace_bytes, void* dk, void* dv,
                      int B, int H, int n_q, int n_k, int d, float scale, int causal,
                      int dtype, void* stream);
 
-/* Backward stage 3: dq = scale dS K.  One pass over the key blocks for every
- * query block, recomputing P and dP. */
+/* Backward stage 3: dq = scale dS K, from the workspace of stage 1.  One
+ * pass over the key blocks for every query block, recomputing P and dP. */
 int fa_backward_dq(const void* q, const void* k, const void* v, const void* dO,
-                   const float* lse, const float* delta, void* dq,
+                   const void* workspace, size_t workspace_bytes, void* dq,
                    int B, int H, int n_q, int n_k, int d, float scale, int causal,
                    int dtype, void* stream);
 

@@ -86,8 +86,11 @@ def test_forward_rejects_invalid_arguments(kw, code):
 
 def test_workspace_size():
     L = fa.lib()
-    assert L.fa_backward_workspace_size(2, 16, 4096, 4096, 128, 1) == 2 * 16 * 4096 * 4
-    assert L.fa_backward_workspace_size(1, 1, 3, 3, 64, 0) == 256
+    # two float32 row vectors, each with >= 16 bytes of slack, 256-byte multiples
+    assert L.fa_backward_workspace_size(2, 16, 4096, 4096, 128, 1) == 2 * (2 * 16 * 4096 * 4 + 256)
+    assert L.fa_backward_workspace_size(1, 1, 3, 3, 64, 0) == 512
+    assert L.fa_backward_workspace_size(1, 1, 60, 3, 64, 0) == 512
+    assert L.fa_backward_workspace_size(1, 1, 61, 3, 64, 0) == 1024
     assert L.fa_backward_workspace_size(1, 1, 0, 3, 64, 0) == 0
     assert L.fa_backward_workspace_size(1, 1, 3, 3, 40, 0) == 0
 
@@ -100,7 +103,7 @@ def bwd(ws=P2, ws_bytes=1 << 20, B=1, H=1, n_q=8, n_k=8, d=64, scale=0.125, caus
 
 @pytest.mark.parametrize("kw,code", [
     ({"ws": None}, fa.FA_ERR_WORKSPACE),
-    ({"ws_bytes": 8 * 4 - 1}, fa.FA_ERR_WORKSPACE),
+    ({"ws_bytes": 511}, fa.FA_ERR_WORKSPACE),
     ({"ws": ctypes.c_void_p(0x100010)}, fa.FA_ERR_ALIGNMENT),
     ({"dq": None}, fa.FA_ERR_INVALID_ARG),
     ({"o": MIS}, fa.FA_ERR_ALIGNMENT),
@@ -114,12 +117,17 @@ def test_backward_rejects_invalid_arguments(kw, code):
 
 def test_stage_entry_points_reject_invalid_arguments():
     L = fa.lib()
-    assert L.fa_backward_preprocess(P, None, P2, 1, 1, 8, 64, 1, None) == fa.FA_ERR_INVALID_ARG
-    assert L.fa_backward_preprocess(P, P, P2, 1, 1, 8, 40, 1, None) == fa.FA_ERR_UNSUPPORTED
-    assert L.fa_backward_dkdv(P, P, P, P, P2, P2, None, P2, 1, 1, 8, 8, 64, 0.1, 0, 1, None) == fa.FA_ERR_INVALID_ARG
-    assert L.fa_backward_dkdv(P, P, P, P, P2, P2, P2, P2, 1, 1, 8, 8, 64, -0.1, 0, 1, None) == fa.FA_ERR_INVALID_ARG
-    assert L.fa_backward_dq(P, P, P, P, P2, P2, MIS, 1, 1, 8, 8, 64, 0.1, 0, 1, None) == fa.FA_ERR_ALIGNMENT
-    assert L.fa_backward_dq(P, P, P, P, P2, P2, P2, 1, 0, 8, 8, 64, 0.1, 0, 1, None) == fa.FA_ERR_INVALID_ARG
+    W = 1 << 20
+    assert L.fa_backward_preprocess(P, None, P2, P2, W, 1, 1, 8, 64, 1, None) == fa.FA_ERR_INVALID_ARG
+    assert L.fa_backward_preprocess(P, P, P2, P2, W, 1, 1, 8, 40, 1, None) == fa.FA_ERR_UNSUPPORTED
+    assert L.fa_backward_preprocess(P, P, P2, P2, 100, 1, 1, 8, 64, 1, None) == fa.FA_ERR_WORKSPACE
+    assert L.fa_backward_preprocess(P, P, P2, ctypes.c_void_p(0x200080), W, 1, 1, 8, 64, 1, None) == fa.FA_ERR_ALIGNMENT
+    assert L.fa_backward_dkdv(P, P, P, P, P2, W, None, P2, 1, 1, 8, 8, 64, 0.1, 0, 1, None) == fa.FA_ERR_INVALID_ARG
+    assert L.fa_backward_dkdv(P, P, P, P, P2, W, P2, P2, 1, 1, 8, 8, 64, -0.1, 0, 1, None) == fa.FA_ERR_INVALID_ARG
+    assert L.fa_backward_dkdv(P, P, P, P, None, W, P2, P2, 1, 1, 8, 8, 64, 0.1, 0, 1, None) == fa.FA_ERR_WORKSPACE
+    assert L.fa_backward_dq(P, P, P, P, P2, W, MIS, 1, 1, 8, 8, 64, 0.1, 0, 1, None) == fa.FA_ERR_ALIGNMENT
+    assert L.fa_backward_dq(P, P, P, P, P2, W, P2, 1, 0, 8, 8, 64, 0.1, 0, 1, None) == fa.FA_ERR_INVALID_ARG
+    assert L.fa_backward_dq(P, P, P, P, P2, 0, P2, 1, 1, 8, 8, 64, 0.1, 0, 1, None) == fa.FA_ERR_WORKSPACE
 
 
 def test_binding_validates_shapes_before_calling():

@@ -71,13 +71,13 @@ def test_stages_compose_to_backward_bitwise(dev):
     for causal in (False, True):
         o, lse = fa.forward(q, k, v, causal=causal)
         dq, dk, dv = fa.backward(q, k, v, o, do, lse, causal=causal)
-        delta = fa.backward_preprocess(o, do)
-        dk2, dv2 = fa.backward_dkdv(q, k, v, do, lse, delta, causal=causal)
-        dq2 = fa.backward_dq(q, k, v, do, lse, delta, causal=causal)
+        ws = fa.backward_preprocess(o, do, lse)
+        dk2, dv2 = fa.backward_dkdv(q, k, v, do, ws, causal=causal)
+        dq2 = fa.backward_dq(q, k, v, do, ws, causal=causal)
         torch.cuda.synchronize()
         assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2)
         ref = (do.float() * o.float()).sum(-1)
-        assert_close("delta", delta, np64(ref), 1e-4)
+        assert_close("delta", fa.workspace_delta(ws, *q.shape[:3]), np64(ref), 1e-4)
 
 
 def test_backward_repeatable_bitwise(dev):
