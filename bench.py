@@ -134,6 +134,9 @@ def main(argv=None):
     ap.add_argument("--causal", action="store_true", help="causal mask (default: non-causal)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle CPU work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibration-copy", action="store_true",
+                    help="after the timed steps, run one elementwise copy of 512 MiB (fp32 x*1 into "
+                         "a second buffer) so that a counter run sees a kernel of known traffic")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -188,6 +191,13 @@ def main(argv=None):
         step(events[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+
+    if args.calibration_copy:
+        src = torch.ones(1 << 27, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     per_stage = {s: 0.0 for s in stages}
     step_ms = []
