@@ -81,11 +81,21 @@ def load_traffic(kernel: str):
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    src = os.path.join(ROOT, KERNEL_SOURCES[kernel])
-    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    if rec.get("source_sha256") != digest:
+    if rec.get("source_sha256") != kernel_source_digest(kernel):
         return None
     return rec.get("bytes_per_launch")
+
+
+def kernel_source_digest(kernel: str) -> str:
+    """sha256 over the kernel's .hip file and every header it can include."""
+    csrc = os.path.join(ROOT, "exact_attention_05_amd", "csrc")
+    h = hashlib.sha256()
+    files = [os.path.join(ROOT, KERNEL_SOURCES[kernel])]
+    files += sorted(os.path.join(csrc, f) for f in os.listdir(csrc) if f.endswith(".hpp"))
+    files.append(os.path.join(ROOT, "include", "fa.h"))
+    for f in files:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
 
 
 def cpu_baseline(w, budget_s: float):

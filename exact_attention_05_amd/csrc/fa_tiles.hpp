@@ -3,10 +3,20 @@
 // cores need.
 //
 // Layout: a tile is ROWS rows of D bf16 values, unpadded (2*D bytes per
-// row).  The 16-byte chunk c of row r is stored at chunk position
-// c ^ (r mod D/8): 32 rows read at the same logical chunk by one
-// matrix-core operand load then fall into different LDS banks.
-//
+// row).  The 16-byte chunk c of row r is stored at chunk position c ^ f(r).
+// The LDS serves 256 bytes (64 banks x 4 bytes) per clock: 16 lanes of a
+// 16-byte row read, 32 lanes of an 8-byte transposing read.  f keeps both
+// reads free of bank conflicts:
+//  * row read: 16 consecutive rows, one logical chunk each, must occupy
+//    distinct banks;
+//  * transposing read: two 16-lane groups read the same 4 aligned rows, the
+//    first the chunk pair {b, b+1}, the second {b+2, b+3} (b a multiple of
+//    4); the 8 (row, pair) combinations must occupy distinct banks.
+// For D = 128 (one 256-byte row spans all banks) f(r) = 4 (r mod 4) +
+// (r/4 mod 4): a permutation over any 16 aligned rows, and 4 aligned rows
+// differ in chunk bits 2-3 while sharing bits 0-1.  For D = 64 two rows
+// share the banks and f(r) = 4 (r/2 mod 2) + (r/4 mod 4); for D = 32 four
+// rows share them and f(r) = r/4 mod 4.
 // Filling: the tile is copied with global_load_lds_dwordx4, 1 KiB per wave
 // instruction (lane j writes bytes [16 j, 16 j + 16) of its KiB).  Wave w of
 // a WAVES-wave workgroup issues KiB number w, w + WAVES, ...  Rows past the
@@ -26,9 +36,16 @@ struct Tile {
   static constexpr int kKiB = kBytes / 1024;
   static_assert(kKiB * 1024 == kBytes, "a tile is a whole number of KiB");
 
+  // Chunk permutation of row `row` (see the layout note above).
+  __device__ static __forceinline__ int swizzle(int row) {
+    if constexpr (D == 128) return 4 * (row & 3) + ((row >> 2) & 3);
+    else if constexpr (D == 64) return 4 * ((row >> 1) & 1) + ((row >> 2) & 3);
+    else return (row >> 2) & 3;
+  }
+
   // Byte offset of (row, 16-byte logical chunk) within the tile.
   __device__ static __forceinline__ int offset(int row, int chunk) {
-    return row * kRowBytes + ((chunk ^ (row % kChunks)) << 4);
+    return row * kRowBytes + ((chunk ^ swizzle(row)) << 4);
   }
 
   // A-operand read for v_mfma_f32_32x32x16_bf16 from rows row0 .. row0+31:
@@ -69,7 +86,7 @@ struct TileDma {
     for (int i = 0; i < kMine; ++i) {
       const int off = (wave + i * WAVES) * 1024 + 16 * lane;
       row[i] = off / T::kRowBytes;
-      col_bytes[i] = (((off % T::kRowBytes) >> 4) ^ (row[i] % T::kChunks)) * 16;
+      col_bytes[i] = (((off % T::kRowBytes) >> 4) ^ T::swizzle(row[i])) * 16;
     }
   }
 
