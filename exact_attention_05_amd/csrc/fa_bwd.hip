@@ -189,7 +189,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16_kernel(BwdArgs a, int n_kti
   // causal) get P = dS = 0.
   auto probs = [&](auto mask_tag, const f32x16 (&s)[C::kKW], const f32x16 (&dp)[C::kKW],
                    const float* lrow, const float* drow, int qbase, int r0,
-                   bf16x8 (&pb)[C::kKW][2], bf16x8 (&dsb)[C::kKW][2]) {
+                   u32x4 (&pb)[C::kKW][2], u32x4 (&dsb)[C::kKW][2]) {
     constexpr bool MASK = decltype(mask_tag)::value;
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
@@ -209,13 +209,10 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16_kernel(BwdArgs a, int n_kti
             if (q >= n_q || key >= n_k || (CAUSAL && key > q)) p0 = 0.f;
             if (q + 1 >= n_q || key >= n_k || (CAUSAL && key > q + 1)) p1 = 0.f;
           }
-          const bf16x2 pp = to_bf16x2(p0, p1);
-          const bf16x2 dd = to_bf16x2(p0 * (dp[kb][i] - dv4[e]), p1 * (dp[kb][i + 1] - dv4[e + 1]));
-          const int slot = 4 * (g4 & 1) + e;
-          pb[kb][g4 >> 1][slot] = pp[0];
-          pb[kb][g4 >> 1][slot + 1] = pp[1];
-          dsb[kb][g4 >> 1][slot] = dd[0];
-          dsb[kb][g4 >> 1][slot + 1] = dd[1];
+          const int slot = (4 * (g4 & 1) + e) >> 1;  // packed bf16 pair index
+          pb[kb][g4 >> 1][slot] = pack_bf16x2(p0, p1);
+          dsb[kb][g4 >> 1][slot] =
+              pack_bf16x2(p0 * (dp[kb][i] - dv4[e]), p1 * (dp[kb][i + 1] - dv4[e + 1]));
         }
       }
     }
@@ -266,7 +263,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16_kernel(BwdArgs a, int n_kti
           dp[kb] = mfma_bf16(ga, vf[kb][c], dp[kb]);
         }
       }
-      bf16x8 pb[C::kKW][2], dsb[C::kKW][2];
+      u32x4 pb[C::kKW][2], dsb[C::kKW][2];
       if (masked)
         probs(T{}, s, dp, lrow, drow, qbase, r0, pb, dsb);
       else
@@ -281,8 +278,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16_kernel(BwdArgs a, int n_kti
           const bf16x8 qtr = C::QT::read_cols_tr(qt, r0 + 16 * c2, 32 * db, lane);
 #pragma unroll
           for (int kb = 0; kb < C::kKW; ++kb) {
-            dv[kb][db] = mfma_bf16(gtr, pb[kb][c2], dv[kb][db]);
-            dk[kb][db] = mfma_bf16(qtr, dsb[kb][c2], dk[kb][db]);
+            dv[kb][db] = mfma_bf16(gtr, bf16x8_of(pb[kb][c2]), dv[kb][db]);
+            dk[kb][db] = mfma_bf16(qtr, bf16x8_of(dsb[kb][c2]), dk[kb][db]);
           }
         }
     }
@@ -404,7 +401,7 @@ __global__ __launch_bounds__(512) void bwd_dq_bf16_kernel(BwdArgs a, int n_qtile
         s = mfma_bf16(C::KV::read_rows(ks, kb * 32, c, lane), qf[c], s);
         dp = mfma_bf16(C::KV::read_rows(vs, kb * 32, c, lane), gf[c], dp);
       }
-      bf16x8 dsb[2];
+      u32x4 dsb[2];
 #pragma unroll
       for (int i = 0; i < 16; i += 2) {
         float p0 = fast_exp2(fmaf(s[i], sl2, -lse2));
@@ -414,15 +411,14 @@ __global__ __launch_bounds__(512) void bwd_dq_bf16_kernel(BwdArgs a, int n_qtile
           if (kj >= n_k || (CAUSAL && kj > qi)) p0 = 0.f;
           if (kj + 1 >= n_k || (CAUSAL && kj + 1 > qi)) p1 = 0.f;
         }
-        const bf16x2 dd = to_bf16x2(p0 * (dp[i] - dlt), p1 * (dp[i + 1] - dlt));
-        dsb[i >> 3][i & 7] = dd[0];
-        dsb[i >> 3][(i & 7) + 1] = dd[1];
+        dsb[i >> 3][(i & 7) >> 1] = pack_bf16x2(p0 * (dp[i] - dlt), p1 * (dp[i + 1] - dlt));
       }
 #pragma unroll
       for (int c2 = 0; c2 < 2; ++c2)
 #pragma unroll
         for (int db = 0; db < C::kDB; ++db)
-          dq[db] = mfma_bf16(C::KV::read_cols_tr(ks, kb * 32 + 16 * c2, 32 * db, lane), dsb[c2], dq[db]);
+          dq[db] = mfma_bf16(C::KV::read_cols_tr(ks, kb * 32 + 16 * c2, 32 * db, lane),
+                             bf16x8_of(dsb[c2]), dq[db]);
     }
   };
 

@@ -94,6 +94,13 @@ __device__ __forceinline__ bf16x2 to_bf16x2(float a, float b) {
   return r;
 }
 
+// Two floats rounded to bf16 (RNE) in one 32-bit register, a in the low half:
+// one v_cvt_pk_bf16_f32.  Four such words form an 8 x bf16 operand.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, to_bf16x2(a, b));
+}
+__device__ __forceinline__ bf16x8 bf16x8_of(const u32x4& w) { return __builtin_bit_cast(bf16x8, w); }
+
 __device__ __forceinline__ bf16x8 to_bf16x8(const float* x) {
   bf16x8 r;
 #pragma unroll

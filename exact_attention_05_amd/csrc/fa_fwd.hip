@@ -133,6 +133,11 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdArgs a, int n_qtiles) 
     const char* vs = sv[buf];
     const int k0 = t * C::kBN;
 
+    // Matrix-core phases run at raised wave priority, the softmax at normal
+    // priority: of the two waves on a SIMD, the one still issuing matrix
+    // operations wins the issue port, so one wave's softmax overlaps the
+    // other's products instead of both waves alternating in lock step.
+    __builtin_amdgcn_s_setprio(1);
     // S^T = K Q^T for kBN keys x 32 queries.
     f32x16 s[C::kKB];
 #pragma unroll
@@ -145,6 +150,7 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdArgs a, int n_qtiles) 
       }
     }
 
+    __builtin_amdgcn_s_setprio(0);
     if constexpr (MASK) {
       // Hidden entries (key past the end, or after the query when causal)
       // leave the maximum alone and get probability 0.
@@ -178,7 +184,7 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdArgs a, int n_qtiles) 
     // P = exp2(scale_log2 * S - ref), rounded to bf16 as the B operand of
     // the P V product.  The row sum l adds the unrounded float values: the
     // LSE needs them (a sum of bf16-rounded terms is off by up to 2^-9).
-    bf16x8 pb[C::kKB][2];
+    u32x4 pw[C::kKB][2];
     float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
     for (int kb = 0; kb < C::kKB; ++kb)
@@ -193,9 +199,7 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdArgs a, int n_qtiles) 
             if (s[kb][8 * c2 + e] == -INFINITY) p0 = 0.f;
             if (s[kb][8 * c2 + e + 1] == -INFINITY) p1 = 0.f;
           }
-          const bf16x2 pp = to_bf16x2(p0, p1);
-          pb[kb][c2][e] = pp[0];
-          pb[kb][c2][e + 1] = pp[1];
+          pw[kb][c2][e >> 1] = pack_bf16x2(p0, p1);
           rs0 += p0;
           rs1 += p1;
         }
@@ -203,6 +207,7 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdArgs a, int n_qtiles) 
     l += rs0 + rs1;
 
     // O^T += V^T P^T, 16 keys per matrix-core step.
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int kb = 0; kb < C::kKB; ++kb)
 #pragma unroll
@@ -210,7 +215,8 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdArgs a, int n_qtiles) 
 #pragma unroll
         for (int db = 0; db < C::kDB; ++db)
           oacc[db] = mfma_bf16(C::KV::read_cols_tr(vs, kb * 32 + 16 * c2, 32 * db, lane),
-                               pb[kb][c2], oacc[db]);
+                               bf16x8_of(pw[kb][c2]), oacc[db]);
+    __builtin_amdgcn_s_setprio(0);
   };
 
   // Leading blocks that need no mask for any row of the workgroup, two at a
