@@ -51,9 +51,14 @@ def compile_flags() -> list[str]:
     ]
 
 
+# Per-source code-generation options (none at present).
+FILE_FLAGS: dict[str, list[str]] = {}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(OBJ_DIR, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *compile_flags(), "-c", src, "-o", obj]
+    extra = FILE_FLAGS.get(os.path.basename(src), [])
+    cmd = [hipcc(), *compile_flags(), *extra, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     # hipcc's host pass does not know the packed-fp32 feature and says so;
     # that note is expected, anything else is shown.

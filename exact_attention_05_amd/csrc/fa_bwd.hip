@@ -91,14 +91,16 @@ template <int D>
 struct DkdvCfg {
   static constexpr int kWaves = 4;               // one per SIMD: 512 registers each
   static constexpr int kThreads = kWaves * 64;
-  static constexpr int kKW = 1;                  // 32-key column blocks per wave
-  static constexpr int kBK = kWaves * kKW * 32;  // keys per workgroup
-  static constexpr int kBQ = 64;                 // queries per streamed block
-  static constexpr int kQS = kBQ / 32;           // 32-query sub-blocks
+  static constexpr int kBK = kWaves * 32;        // keys per workgroup, 32 per wave
+  static constexpr int kBQ = 64;                 // queries per streamed stage
   static constexpr int kDC = D / 16;
   static constexpr int kDB = D / 32;
-  using QT = Tile<D, kBQ>;                       // one Q or dO block in LDS
-  static constexpr int kRowVecBytes = kBQ * 4;   // one block of LSE2 or D
+  static constexpr int kS1 = kDC;                // steps of region 1 (Q / dO row fragments)
+  static constexpr int kS2 = 2 * kDB;            // steps of region 2 (dO^T / Q^T fragments)
+  static constexpr int kAhead = 4;               // fragments read ahead of their products
+  static constexpr int kRing = kAhead + 1;
+  using QT = Tile<D, kBQ>;                       // one Q or dO stage in LDS
+  static constexpr int kRowVecBytes = kBQ * 4;   // one stage of LSE2 or D
 };
 
 template <int D, bool CAUSAL>
@@ -123,7 +125,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16_kernel(BwdArgs a, int n_kti
   const int n_q = a.n_q, n_k = a.n_k;
   const float sl2 = a.scale_log2;
   const int k0 = kt * C::kBK;
-  const int kw = k0 + wave * (C::kKW * 32);  // this wave's first key
+  const int key = k0 + wave * 32 + l32;  // this lane's key (a column of S)
 
   const __bf16* qp = static_cast<const __bf16*>(a.q) + (size_t)bh * n_q * D;
   const __bf16* dop = static_cast<const __bf16*>(a.dO) + (size_t)bh * n_q * D;
@@ -132,24 +134,18 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16_kernel(BwdArgs a, int n_kti
   const float* lsep = a.lse2 + (size_t)bh * n_q;
   const float* delp = a.delta + (size_t)bh * n_q;
 
-  // K and V rows of this lane's keys (kw + 32 kb + l32) stay in registers as
-  // the B operands of S = Q K^T and dP = dO V^T.
-  bf16x8 kf[C::kKW][C::kDC], vf[C::kKW][C::kDC];
+  // The lane's K and V rows stay in registers as the B operands of
+  // S = Q K^T and dP = dO V^T.
+  bf16x8 kf[C::kDC], vf[C::kDC];
 #pragma unroll
-  for (int kb = 0; kb < C::kKW; ++kb) {
-    const int key = kw + 32 * kb + l32;
-#pragma unroll
-    for (int c = 0; c < C::kDC; ++c) {
-      kf[kb][c] = key < n_k
-                      ? *reinterpret_cast<const bf16x8*>(kp + (size_t)key * D + 16 * c + 8 * hi)
+  for (int c = 0; c < C::kDC; ++c) {
+    kf[c] = key < n_k ? *reinterpret_cast<const bf16x8*>(kp + (size_t)key * D + 16 * c + 8 * hi)
                       : bf16x8{};
-      vf[kb][c] = key < n_k
-                      ? *reinterpret_cast<const bf16x8*>(vp + (size_t)key * D + 16 * c + 8 * hi)
+    vf[c] = key < n_k ? *reinterpret_cast<const bf16x8*>(vp + (size_t)key * D + 16 * c + 8 * hi)
                       : bf16x8{};
-    }
   }
 
-  // Query blocks that can see any key of this workgroup.
+  // Query stages that can see any key of this workgroup.
   const int qb_first = CAUSAL ? (k0 / C::kBQ) : 0;
   const int nblocks = (CAUSAL && k0 >= n_q) ? 0 : (n_q + C::kBQ - 1) / C::kBQ - qb_first;
 
@@ -159,7 +155,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16_kernel(BwdArgs a, int n_kti
   const uint32_t sdo_addr = lds_address(&sdo[0][0]);
   const uint32_t slse_addr = lds_address(&slse[0][0]);
   const uint32_t sdel_addr = lds_address(&sdel[0][0]);
-  auto load_block = [&](int b, int buf) {
+  auto load_block = [&](int b, int buf) __attribute__((always_inline)) {
     const int q0 = (qb_first + b) * C::kBQ;
     const int valid = n_q - q0;
     dma.load(qp + (size_t)q0 * D, valid, sq_addr + buf * C::QT::kBytes);
@@ -176,53 +172,135 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16_kernel(BwdArgs a, int n_kti
     }
   };
 
-  f32x16 dk[C::kKW][C::kDB], dv[C::kKW][C::kDB];
-#pragma unroll
-  for (int kb = 0; kb < C::kKW; ++kb)
-#pragma unroll
-    for (int db = 0; db < C::kDB; ++db) { dk[kb][db] = f32x16{}; dv[kb][db] = f32x16{}; }
+  // Stage buffer 1 starts as zeros: the first iteration's output update
+  // reads it with zero probabilities.
+  for (int i = tid; i < C::QT::kBytes / 16; i += C::kThreads) {
+    reinterpret_cast<u32x4*>(sq[1])[i] = u32x4{};
+    reinterpret_cast<u32x4*>(sdo[1])[i] = u32x4{};
+  }
 
-  // P and dS of one 32-query sub-block from S and dP (element i of this
-  // lane is query row r0 + 8(i/4) + 4 hi + i%4 of the block), rounded to
-  // bf16 in the order the B operand of the dV / dK products wants.  With
-  // MASK, hidden pairs (query past n_q, key past n_k, key after query when
-  // causal) get P = dS = 0.
-  auto probs = [&](auto mask_tag, const f32x16 (&s)[C::kKW], const f32x16 (&dp)[C::kKW],
-                   const float* lrow, const float* drow, int qbase, int r0,
-                   u32x4 (&pb)[C::kKW][2], u32x4 (&dsb)[C::kKW][2]) {
-    constexpr bool MASK = decltype(mask_tag)::value;
+  f32x16 dk[C::kDB], dv[C::kDB];
 #pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      const int r = r0 + 8 * g4 + 4 * hi;
-      const f32x4 lv = *reinterpret_cast<const f32x4*>(&lrow[r]);
-      const f32x4 dv4 = *reinterpret_cast<const f32x4*>(&drow[r]);
+  for (int db = 0; db < C::kDB; ++db) { dk[db] = f32x16{}; dv[db] = f32x16{}; }
+  f32x16 s, dp;             // S and dP of the current 32-query sub-block
+  f32x4 lv[4], dl[4];       // LSE2 and D of the lane's 16 query rows of that sub-block
+  float ex[16], dd[16];     // its probabilities and dP - D (element i: row 8(i/4) + 4 hi + i%4)
+  u32x4 pb[2], dsb[2];      // P and dS of the previous sub-block as bf16 pairs
 #pragma unroll
-      for (int kb = 0; kb < C::kKW; ++kb) {
-        const int key = kw + 32 * kb + l32;
-#pragma unroll
-        for (int e = 0; e < 4; e += 2) {
-          const int i = 4 * g4 + e;
-          float p0 = fast_exp2(fmaf(s[kb][i], sl2, -lv[e]));
-          float p1 = fast_exp2(fmaf(s[kb][i + 1], sl2, -lv[e + 1]));
-          if constexpr (MASK) {
-            const int q = qbase + r + e;
-            if (q >= n_q || key >= n_k || (CAUSAL && key > q)) p0 = 0.f;
-            if (q + 1 >= n_q || key >= n_k || (CAUSAL && key > q + 1)) p1 = 0.f;
-          }
-          const int slot = (4 * (g4 & 1) + e) >> 1;  // packed bf16 pair index
-          pb[kb][g4 >> 1][slot] = pack_bf16x2(p0, p1);
-          dsb[kb][g4 >> 1][slot] =
-              pack_bf16x2(p0 * (dp[kb][i] - dv4[e]), p1 * (dp[kb][i + 1] - dv4[e + 1]));
-        }
-      }
+  for (int i = 0; i < 16; ++i) { ex[i] = 0.f; dd[i] = 0.f; }
+  bf16x8 fa[C::kRing], fb[C::kRing];
+
+  // Probability step for element i of the current sub-block (section
+  // "Recomputation": P = exp(scale S - LSE), and dP - D for dS = P o (dP - D)).
+  // With MASK, hidden pairs (query past n_q, key past n_k, key after query
+  // when causal) get P = 0.
+  auto stage_a = [&](auto mask_tag, int i, int qrow0) __attribute__((always_inline)) {
+    const int g4 = i >> 2, e = i & 3;
+    float p = fast_exp2(fmaf(s[i], sl2, -lv[g4][e]));
+    if constexpr (decltype(mask_tag)::value) {
+      const int q = qrow0 + 8 * g4 + 4 * hi + e;
+      if (q >= n_q || key >= n_k || (CAUSAL && key > q)) p = 0.f;
     }
+    ex[i] = p;
+    dd[i] = dp[i] - dl[g4][e];
+  };
+  // dS for key pair pr (elements 2 pr, 2 pr + 1) and both rounded to bf16 in
+  // the order of the B operand of dV^T += dO^T P and dK^T += Q^T dS.
+  auto stage_b = [&](int pr) __attribute__((always_inline)) {
+    const float d0 = ex[2 * pr] * dd[2 * pr], d1 = ex[2 * pr + 1] * dd[2 * pr + 1];
+    pb[pr >> 2][pr & 3] = pack_bf16x2(ex[2 * pr], ex[2 * pr + 1]);
+    dsb[pr >> 2][pr & 3] = pack_bf16x2(d0, d1);
+  };
+  auto step_order = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);       // fragment reads
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       // product
+    __builtin_amdgcn_sched_group_barrier(0x2 | 0x400, 4, 0); // vector work
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       // product
+    __builtin_amdgcn_sched_group_barrier(0x2 | 0x400, 64, 0);
+    __builtin_amdgcn_sched_barrier(0);
   };
 
-  // Blocks needing the mask: the causal diagonal (query blocks starting
-  // before the workgroup's last key), a ragged last query block, or every
-  // block when the workgroup's keys run past n_k.  One loop body serves all
-  // blocks; only the probability step branches on the mask, so the
-  // accumulators stay in one set of registers.
+  // Iteration over one 32-query sub-block (rows R0 of stage buffer BUF),
+  // software-pipelined with the sub-block before it (rows RP of buffer BP):
+  //   region 1: S, dP of this sub-block   with dS and bf16 rounding of the previous
+  //   region 2: dV, dK of the previous one with P, dP - D of this one
+  // qrow0 is the absolute index of row R0.
+  auto iteration = [&](auto mask_tag, auto buf_tag, auto r0_tag, auto bp_tag, auto rp_tag, int qrow0)
+      __attribute__((always_inline)) {
+    constexpr int BUF = decltype(buf_tag)::value, R0 = decltype(r0_tag)::value;
+    constexpr int BP = decltype(bp_tag)::value, RP = decltype(rp_tag)::value;
+    const char* qt = sq[BUF];
+    const char* gt = sdo[BUF];
+    s = f32x16{};
+    dp = f32x16{};
+    static_for<0, (C::kS1 < C::kAhead ? C::kS1 : C::kAhead)>([&](auto i) __attribute__((always_inline)) {
+      fa[decltype(i)::value] = C::QT::read_rows(qt, R0, decltype(i)::value, lane);
+      fb[decltype(i)::value] = C::QT::read_rows(gt, R0, decltype(i)::value, lane);
+    });
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      lv[g4] = *reinterpret_cast<const f32x4*>(&slse[BUF][R0 + 8 * g4 + 4 * hi]);
+      dl[g4] = *reinterpret_cast<const f32x4*>(&sdel[BUF][R0 + 8 * g4 + 4 * hi]);
+    }
+    static_for<0, C::kS1>([&](auto c_tag) __attribute__((always_inline)) {
+      constexpr int c = decltype(c_tag)::value;
+      if constexpr (c + C::kAhead < C::kS1) {
+        fa[(c + C::kAhead) % C::kRing] = C::QT::read_rows(qt, R0, c + C::kAhead, lane);
+        fb[(c + C::kAhead) % C::kRing] = C::QT::read_rows(gt, R0, c + C::kAhead, lane);
+      }
+      s = mfma_bf16(fa[c % C::kRing], kf[c], s);
+      dp = mfma_bf16(fb[c % C::kRing], vf[c], dp);
+      static_for<c * 8 / C::kS1, (c + 1) * 8 / C::kS1>([&](auto pr) __attribute__((always_inline)) {
+        stage_b(decltype(pr)::value);
+      });
+      if constexpr (c == C::kS1 - 1) {
+        static_for<0, (C::kS2 < C::kAhead ? C::kS2 : C::kAhead)>([&](auto i) __attribute__((always_inline)) {
+          constexpr int f = decltype(i)::value;
+          fa[f] = C::QT::read_cols_tr(sdo[BP], RP + 16 * (f / C::kDB), 32 * (f % C::kDB), lane);
+          fb[f] = C::QT::read_cols_tr(sq[BP], RP + 16 * (f / C::kDB), 32 * (f % C::kDB), lane);
+        });
+      }
+      step_order();
+    });
+    static_for<0, C::kS2>([&](auto f_tag) __attribute__((always_inline)) {
+      constexpr int f = decltype(f_tag)::value;
+      constexpr int c2 = f / C::kDB, db = f % C::kDB;
+      if constexpr (f + C::kAhead < C::kS2) {
+        constexpr int g = f + C::kAhead;
+        fa[g % C::kRing] = C::QT::read_cols_tr(sdo[BP], RP + 16 * (g / C::kDB), 32 * (g % C::kDB), lane);
+        fb[g % C::kRing] = C::QT::read_cols_tr(sq[BP], RP + 16 * (g / C::kDB), 32 * (g % C::kDB), lane);
+      }
+      dv[db] = mfma_bf16(fa[f % C::kRing], bf16x8_of(pb[c2]), dv[db]);
+      dk[db] = mfma_bf16(fb[f % C::kRing], bf16x8_of(dsb[c2]), dk[db]);
+      static_for<f * 16 / C::kS2, (f + 1) * 16 / C::kS2>([&](auto i) __attribute__((always_inline)) {
+        stage_a(mask_tag, decltype(i)::value, qrow0);
+      });
+      step_order();
+    });
+  };
+
+  // One 64-query stage in buffer BUF: its two sub-blocks, the first paired
+  // with the second sub-block of the previous stage (buffer BUF ^ 1).  The
+  // stage was copied during the previous stage; after the first sub-block
+  // every wave is past the previous stage, whose buffer then takes the next.
+  auto do_stage = [&](auto mask_tag, auto buf_tag, int b) __attribute__((always_inline)) {
+    constexpr int BUF = decltype(buf_tag)::value;
+    using IB = std::integral_constant<int, BUF>;
+    using IP = std::integral_constant<int, BUF ^ 1>;
+    using R0 = std::integral_constant<int, 0>;
+    using R32 = std::integral_constant<int, 32>;
+    const int qrow0 = (qb_first + b) * C::kBQ;
+    wait_lds_dma();
+    phase_barrier();
+    iteration(mask_tag, IB{}, R0{}, IP{}, R32{}, qrow0);
+    phase_barrier();
+    if (b + 1 < nblocks) load_block(b + 1, BUF ^ 1);
+    iteration(mask_tag, IB{}, R32{}, IB{}, R0{}, qrow0 + 32);
+  };
+
+  // Stages needing the mask: the causal diagonal (query stages starting
+  // before the workgroup's last key), a ragged last stage, or every stage
+  // when the workgroup's keys run past n_k.
   int b_lo = 0, b_hi = nblocks;
   if (CAUSAL) {
     const int first_clear = k0 + C::kBK - 1;  // first query row that sees every key here
@@ -232,79 +310,106 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16_kernel(BwdArgs a, int n_kti
   if (k0 + C::kBK > n_k) b_lo = b_hi = nblocks;
   b_hi = max(b_hi, b_lo);
 
-  if (nblocks > 0) load_block(0, 0);
-  for (int b = 0; b < nblocks; ++b) {
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  const bool any_masked = b_lo > 0 || b_hi < nblocks;
+
+  // A masked stage, without the pipeline (they are few: the causal diagonal
+  // and ragged ends): per sub-block S and dP, masked P and dS, then the dV
+  // and dK products.  The next stage is started at once, since nothing here
+  // reads the other buffer.
+  auto masked_stage = [&](int b) __attribute__((always_inline)) {
     const int buf = b & 1;
     wait_lds_dma();
-    __syncthreads();
+    phase_barrier();
     if (b + 1 < nblocks) load_block(b + 1, buf ^ 1);
     const char* qt = sq[buf];
     const char* gt = sdo[buf];
-    const float* lrow = slse[buf];
-    const float* drow = sdel[buf];
-    const int qbase = (qb_first + b) * C::kBQ;
-    const bool masked = b < b_lo || b >= b_hi;
-
-#pragma unroll
-    for (int qs = 0; qs < C::kQS; ++qs) {
-      const int r0 = qs * 32;
-      // Sub-blocks entirely before this wave's first key are all hidden.
-      if (CAUSAL && qbase + r0 + 31 < kw) continue;
-      f32x16 s[C::kKW], dp[C::kKW];
-#pragma unroll
-      for (int kb = 0; kb < C::kKW; ++kb) { s[kb] = f32x16{}; dp[kb] = f32x16{}; }
+#pragma unroll 1
+    for (int r0 = 0; r0 < C::kBQ; r0 += 32) {
+      s = f32x16{};
+      dp = f32x16{};
 #pragma unroll
       for (int c = 0; c < C::kDC; ++c) {
-        const bf16x8 qa = C::QT::read_rows(qt, r0, c, lane);
-        const bf16x8 ga = C::QT::read_rows(gt, r0, c, lane);
-#pragma unroll
-        for (int kb = 0; kb < C::kKW; ++kb) {
-          s[kb] = mfma_bf16(qa, kf[kb][c], s[kb]);
-          dp[kb] = mfma_bf16(ga, vf[kb][c], dp[kb]);
-        }
+        s = mfma_bf16(C::QT::read_rows(qt, r0, c, lane), kf[c], s);
+        dp = mfma_bf16(C::QT::read_rows(gt, r0, c, lane), vf[c], dp);
       }
-      u32x4 pb[C::kKW][2], dsb[C::kKW][2];
-      if (masked)
-        probs(T{}, s, dp, lrow, drow, qbase, r0, pb, dsb);
-      else
-        probs(F{}, s, dp, lrow, drow, qbase, r0, pb, dsb);
-      // dV^T += dO^T P and dK^T += Q^T dS, 16 queries per step; the dO^T and
-      // Q^T operands serve both key blocks.
 #pragma unroll
-      for (int c2 = 0; c2 < 2; ++c2)
+      for (int g4 = 0; g4 < 4; ++g4) {
+        lv[g4] = *reinterpret_cast<const f32x4*>(&slse[buf][r0 + 8 * g4 + 4 * hi]);
+        dl[g4] = *reinterpret_cast<const f32x4*>(&sdel[buf][r0 + 8 * g4 + 4 * hi]);
+      }
+      const int qrow0 = (qb_first + b) * C::kBQ + r0;
+      static_for<0, 16>([&](auto i) __attribute__((always_inline)) { stage_a(T{}, decltype(i)::value, qrow0); });
+      static_for<0, 8>([&](auto pr) __attribute__((always_inline)) { stage_b(decltype(pr)::value); });
 #pragma unroll
-        for (int db = 0; db < C::kDB; ++db) {
-          const bf16x8 gtr = C::QT::read_cols_tr(gt, r0 + 16 * c2, 32 * db, lane);
-          const bf16x8 qtr = C::QT::read_cols_tr(qt, r0 + 16 * c2, 32 * db, lane);
-#pragma unroll
-          for (int kb = 0; kb < C::kKW; ++kb) {
-            dv[kb][db] = mfma_bf16(gtr, bf16x8_of(pb[kb][c2]), dv[kb][db]);
-            dk[kb][db] = mfma_bf16(qtr, bf16x8_of(dsb[kb][c2]), dk[kb][db]);
-          }
-        }
+      for (int f = 0; f < C::kS2; ++f) {
+        const int c2 = f / C::kDB, db = f % C::kDB;
+        dv[db] = mfma_bf16(C::QT::read_cols_tr(gt, r0 + 16 * c2, 32 * db, lane), bf16x8_of(pb[c2]), dv[db]);
+        dk[db] = mfma_bf16(C::QT::read_cols_tr(qt, r0 + 16 * c2, 32 * db, lane), bf16x8_of(dsb[c2]), dk[db]);
+      }
     }
+  };
+
+  // dS of the last pipelined sub-block (rows 32..63 of buffer BUF), then
+  // its dV and dK products.
+  auto finish = [&](auto buf_tag) __attribute__((always_inline)) {
+    constexpr int BUF = decltype(buf_tag)::value;
+    static_for<0, 8>([&](auto pr) __attribute__((always_inline)) { stage_b(decltype(pr)::value); });
+#pragma unroll
+    for (int f = 0; f < C::kS2; ++f) {
+      const int c2 = f / C::kDB, db = f % C::kDB;
+      dv[db] = mfma_bf16(C::QT::read_cols_tr(sdo[BUF], 32 + 16 * c2, 32 * db, lane), bf16x8_of(pb[c2]), dv[db]);
+      dk[db] = mfma_bf16(C::QT::read_cols_tr(sq[BUF], 32 + 16 * c2, 32 * db, lane), bf16x8_of(dsb[c2]), dk[db]);
+    }
+  };
+
+  if (nblocks > 0) {
+    load_block(0, 0);
+    int b = 0;
+    if (any_masked)
+      for (; b < b_lo; ++b) masked_stage(b);
+    // Unmasked stages [b, b_hi) through the pipeline, in pairs with fixed
+    // buffers; its state starts empty (zero probabilities for the "previous"
+    // sub-block of the first iteration).
+    if (b < b_hi) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) { ex[i] = 0.f; dd[i] = 0.f; }
+      if (b & 1) {
+        do_stage(F{}, B1{}, b);
+        ++b;
+      }
+      for (; b + 1 < b_hi; b += 2) {
+        do_stage(F{}, B0{}, b);
+        do_stage(F{}, B1{}, b + 1);
+      }
+      if (b < b_hi) {
+        do_stage(F{}, B0{}, b);
+        ++b;
+      }
+      if ((b - 1) & 1) finish(B1{});
+      else finish(B0{});
+    }
+    if (any_masked)
+      for (; b < nblocks; ++b) masked_stage(b);
   }
 
+  if (key < n_k) {
+    __bf16* dkp = static_cast<__bf16*>(a.dk) + ((size_t)bh * n_k + key) * D;
+    __bf16* dvp = static_cast<__bf16*>(a.dv) + ((size_t)bh * n_k + key) * D;
 #pragma unroll
-  for (int kb = 0; kb < C::kKW; ++kb) {
-    const int key = kw + 32 * kb + l32;
-    if (key < n_k) {
-      __bf16* dkp = static_cast<__bf16*>(a.dk) + ((size_t)bh * n_k + key) * D;
-      __bf16* dvp = static_cast<__bf16*>(a.dv) + ((size_t)bh * n_k + key) * D;
+    for (int db = 0; db < C::kDB; ++db)
 #pragma unroll
-      for (int db = 0; db < C::kDB; ++db)
+      for (int g4 = 0; g4 < 4; ++g4) {
+        bf16x4 rk, rv;
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          bf16x4 rk, rv;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            rk[e] = (__bf16)(dk[kb][db][4 * g4 + e] * a.scale);
-            rv[e] = (__bf16)dv[kb][db][4 * g4 + e];
-          }
-          *reinterpret_cast<bf16x4*>(dkp + 32 * db + 8 * g4 + 4 * hi) = rk;
-          *reinterpret_cast<bf16x4*>(dvp + 32 * db + 8 * g4 + 4 * hi) = rv;
+        for (int e = 0; e < 4; ++e) {
+          rk[e] = (__bf16)(dk[db][4 * g4 + e] * a.scale);
+          rv[e] = (__bf16)dv[db][4 * g4 + e];
         }
-    }
+        *reinterpret_cast<bf16x4*>(dkp + 32 * db + 8 * g4 + 4 * hi) = rk;
+        *reinterpret_cast<bf16x4*>(dvp + 32 * db + 8 * g4 + 4 * hi) = rv;
+      }
   }
 }
 

@@ -20,6 +20,7 @@
 
 #include <hip/hip_runtime.h>
 #include <cstdint>
+#include <type_traits>
 
 namespace fa {
 
@@ -59,6 +60,12 @@ __device__ __forceinline__ bf16x4 lds_read_tr16(const __bf16* p) {
 // the copy (LDS reads and lane shuffles do not use M0 on gfx950).
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void lds_dma16(uint32_t lds_addr, const void* base, uint32_t voffset) {
+  // Both scalar operands are wave-uniform; the read-first-lane makes that
+  // visible to the compiler where its divergence analysis cannot prove it.
+  lds_addr = __builtin_amdgcn_readfirstlane(lds_addr);
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  base = (const void*)(uintptr_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
+                                  (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b));
   asm volatile(
       "s_mov_b32 m0, %0\n\t"
       "global_load_lds_dwordx4 %1, %2"
@@ -72,6 +79,28 @@ __device__ __forceinline__ void lds_dma16(uint32_t lds_addr, const void* base, u
 // the LDS copies above included.  Written with the builtin so that the
 // compiler's own wait tracking knows that its earlier loads are done too.
 __device__ __forceinline__ void wait_lds_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Workgroup barrier that leaves vector-memory loads (the LDS copies above)
+// in flight.  It waits only for this wave's own LDS reads (lgkmcnt(0)), so
+// that a buffer read before the barrier may be refilled after it; the asm
+// statement's memory clobber keeps the compiler from moving memory accesses
+// across it and the scheduling barriers keep every instruction on its side.
+__device__ __forceinline__ void phase_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  asm volatile("s_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Calls f(std::integral_constant<int, I>{}) for I = BEGIN .. END-1, so that
+// the index is a compile-time constant in the body.
+template <int BEGIN, int END, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (BEGIN < END) {
+    f(std::integral_constant<int, BEGIN>{});
+    static_for<BEGIN + 1, END>(f);
+  }
+}
 
 template <typename T>
 __device__ __forceinline__ uint32_t lds_address(const T* p) {

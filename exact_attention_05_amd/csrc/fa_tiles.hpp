@@ -71,23 +71,25 @@ struct Tile {
   }
 };
 
-// Per-lane state for filling Tile<D, ROWS> tiles by direct copies.
+// Per-lane state for filling Tile<D, ROWS> tiles by direct copies.  The
+// KiB blocks of one wave lie WAVES KiB apart, a whole number of 16-row
+// swizzle periods, so every copy of a lane uses the same chunk position and
+// only its row advances.
 template <int D, int ROWS, int WAVES>
 struct TileDma {
   using T = Tile<D, ROWS>;
   static constexpr int kMine = (T::kKiB + WAVES - 1) / WAVES;  // KiB copies per wave
-  int row[kMine];
-  int col_bytes[kMine];
+  static constexpr int kRowStep = WAVES * 1024 / T::kRowBytes;  // rows between a lane's copies
+  static_assert(kRowStep % 16 == 0, "a wave's copies must be whole swizzle periods apart");
+  int row0;       // tile row of the lane's first copy
+  int col_bytes;  // byte offset of its 16-byte chunk within a row (swizzled)
   int wave;
 
   __device__ __forceinline__ void init(int wave_, int lane) {
     wave = wave_;
-#pragma unroll
-    for (int i = 0; i < kMine; ++i) {
-      const int off = (wave + i * WAVES) * 1024 + 16 * lane;
-      row[i] = off / T::kRowBytes;
-      col_bytes[i] = (((off % T::kRowBytes) >> 4) ^ T::swizzle(row[i])) * 16;
-    }
+    const int off = wave * 1024 + 16 * lane;
+    row0 = off / T::kRowBytes;
+    col_bytes = (((off % T::kRowBytes) >> 4) ^ T::swizzle(row0)) * 16;
   }
 
   // Copy rows [0, ROWS) starting at `src` (row 0 of the tile in global
@@ -97,8 +99,21 @@ struct TileDma {
 #pragma unroll
     for (int i = 0; i < kMine; ++i) {
       const int L = wave + i * WAVES;
-      if (L < T::kKiB) {
-        const uint32_t voff = (uint32_t)(min(row[i], valid - 1) * T::kRowBytes + col_bytes[i]);
+      if (T::kKiB % WAVES == 0 || L < T::kKiB) {
+        const uint32_t voff = (uint32_t)(min(row0 + i * kRowStep, valid - 1) * T::kRowBytes + col_bytes);
+        lds_dma16(lds + L * 1024, src, voff);
+      }
+    }
+  }
+
+  // The same for a tile whose ROWS rows all exist: the per-lane offsets do
+  // not depend on the tile.
+  __device__ __forceinline__ void load_full(const __bf16* src, uint32_t lds) const {
+#pragma unroll
+    for (int i = 0; i < kMine; ++i) {
+      const int L = wave + i * WAVES;
+      if (T::kKiB % WAVES == 0 || L < T::kKiB) {
+        const uint32_t voff = (uint32_t)((row0 + i * kRowStep) * T::kRowBytes + col_bytes);
         lds_dma16(lds + L * 1024, src, voff);
       }
     }
