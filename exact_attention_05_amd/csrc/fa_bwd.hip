@@ -203,13 +203,19 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16_kernel(BwdArgs a, int n_kti
     }
     ex[i] = p;
     dd[i] = dp[i] - dl[g4][e];
+    pin(ex[i]);
+    pin(dd[i]);
   };
   // dS for key pair pr (elements 2 pr, 2 pr + 1) and both rounded to bf16 in
   // the order of the B operand of dV^T += dO^T P and dK^T += Q^T dS.
   auto stage_b = [&](int pr) __attribute__((always_inline)) {
     const float d0 = ex[2 * pr] * dd[2 * pr], d1 = ex[2 * pr + 1] * dd[2 * pr + 1];
-    pb[pr >> 2][pr & 3] = pack_bf16x2(ex[2 * pr], ex[2 * pr + 1]);
-    dsb[pr >> 2][pr & 3] = pack_bf16x2(d0, d1);
+    uint32_t wp = pack_bf16x2(ex[2 * pr], ex[2 * pr + 1]);
+    uint32_t wd = pack_bf16x2(d0, d1);
+    pin(wp);
+    pin(wd);
+    pb[pr >> 2][pr & 3] = wp;
+    dsb[pr >> 2][pr & 3] = wd;
   };
   auto step_order = [&]() __attribute__((always_inline)) {
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);       // fragment reads

@@ -92,6 +92,12 @@ __device__ __forceinline__ void phase_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// Fixes the point where x is computed: the compiler may not sink its
+// computation past this statement (towards a later use) nor hoist it above
+// an earlier one.  Emits no instruction.
+__device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin(uint32_t& x) { asm volatile("" : "+v"(x)); }
+
 // Calls f(std::integral_constant<int, I>{}) for I = BEGIN .. END-1, so that
 // the index is a compile-time constant in the body.
 template <int BEGIN, int END, typename F>
