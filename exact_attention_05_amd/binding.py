@@ -66,6 +66,11 @@ def lib() -> ctypes.CDLL:
         L.fa_backward_dkdv.restype = i
         L.fa_backward_dq.argtypes = [vp, vp, vp, vp, vp, sz, vp, i, i, i, i, i, f, i, i, vp]
         L.fa_backward_dq.restype = i
+        L.fa_forward_gqa.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp]
+        L.fa_forward_gqa.restype = i
+        L.fa_backward_gqa.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
+                                      i, i, i, i, i, i, f, i, i, vp]
+        L.fa_backward_gqa.restype = i
         L.fa_status_string.argtypes = [i]
         L.fa_status_string.restype = ctypes.c_char_p
         L.fa_version.argtypes = []
@@ -112,10 +117,11 @@ def _check_qkv(q, k, v):
     if not (q.device == k.device == v.device):
         raise ValueError("q, k, v must be on one device")
     B, H, n_q, d = q.shape
-    if k.shape[:2] != (B, H) or v.shape[:2] != (B, H) or k.shape[3] != d or v.shape[3] != d:
+    if k.shape != v.shape or k.shape[0] != B or k.shape[3] != d:
         raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
-    if k.shape[2] != v.shape[2]:
-        raise ValueError("k and v must have the same number of rows")
+    h_kv = k.shape[1]
+    if h_kv < 1 or H % h_kv != 0:
+        raise ValueError(f"k and v have {h_kv} heads, which must divide q's {H}")
     return B, H, n_q, k.shape[2], d
 
 
@@ -124,7 +130,9 @@ def _scale(scale, d):
 
 
 def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None):
-    """O, LSE = attention(q, k, v).  q: (B,H,n_q,d); k, v: (B,H,n_k,d).
+    """O, LSE = attention(q, k, v).  q: (B,H,n_q,d); k, v: (B,H_kv,n_k,d) with H_kv
+    dividing H (H_kv < H shares each K/V head among H/H_kv consecutive query
+    heads: grouped-query or, with H_kv = 1, multi-query attention).
 
     Returns O (q's dtype, (B,H,n_q,d)) and LSE (float32, (B,H,n_q)).
     ``scale`` defaults to 1/sqrt(d).
@@ -138,9 +146,16 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None,
         raise ValueError("out must be a contiguous tensor like q")
     if lse.shape != (B, H, n_q) or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.device != q.device:
         raise ValueError("lse must be a contiguous float32 (B, H, n_q) tensor")
-    st = lib().fa_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, n_q, n_k, d,
-                          _scale(scale, d), int(bool(causal)), _DTYPES[q.dtype], _stream(q.device))
-    _check(st, "fa_forward")
+    h_kv = k.shape[1]
+    if h_kv == H:
+        st = lib().fa_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, n_q, n_k, d,
+                              _scale(scale, d), int(bool(causal)), _DTYPES[q.dtype], _stream(q.device))
+        _check(st, "fa_forward")
+    else:
+        st = lib().fa_forward_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, h_kv, n_q,
+                                  n_k, d, _scale(scale, d), int(bool(causal)), _DTYPES[q.dtype],
+                                  _stream(q.device))
+        _check(st, "fa_forward_gqa")
     return out, lse
 
 
@@ -155,7 +170,7 @@ def _check_like(name, t, ref):
 
 def backward(q, k, v, o, do, lse, causal: bool = False, scale: float | None = None,
              dq=None, dk=None, dv=None, workspace=None):
-    """dQ, dK, dV from the saved o and lse of ``forward``."""
+    """dQ, dK, dV from the saved o and lse of ``forward``; dK, dV have k's shape."""
     B, H, n_q, n_k, d = _check_qkv(q, k, v)
     _check_like("o", o, q)
     _check_like("do", do, q)
@@ -169,11 +184,19 @@ def backward(q, k, v, o, do, lse, causal: bool = False, scale: float | None = No
     _check_like("dv", dv, v)
     if workspace is None:
         workspace = backward_workspace(B, H, n_q, n_k, d, q.dtype, q.device)
-    st = lib().fa_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq),
-                           _ptr(dk), _ptr(dv), *_ws(workspace),
-                           B, H, n_q, n_k, d, _scale(scale, d), int(bool(causal)),
-                           _DTYPES[q.dtype], _stream(q.device))
-    _check(st, "fa_backward")
+    h_kv = k.shape[1]
+    if h_kv == H:
+        st = lib().fa_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq),
+                               _ptr(dk), _ptr(dv), *_ws(workspace),
+                               B, H, n_q, n_k, d, _scale(scale, d), int(bool(causal)),
+                               _DTYPES[q.dtype], _stream(q.device))
+        _check(st, "fa_backward")
+    else:
+        st = lib().fa_backward_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse),
+                                   _ptr(dq), _ptr(dk), _ptr(dv), *_ws(workspace),
+                                   B, H, h_kv, n_q, n_k, d, _scale(scale, d), int(bool(causal)),
+                                   _DTYPES[q.dtype], _stream(q.device))
+        _check(st, "fa_backward_gqa")
     return dq, dk, dv
 
 
@@ -206,9 +229,16 @@ def backward_preprocess(o, do, lse, workspace=None):
     return workspace
 
 
+def _require_mha(q, k, where):
+    if k.shape[1] != q.shape[1]:
+        raise ValueError(f"{where}: the stage entry points take one K/V head per query head; "
+                         "use backward() for shared K/V heads")
+
+
 def backward_dkdv(q, k, v, do, workspace, causal=False, scale=None, dk=None, dv=None):
     """Stage 2: dK and dV from the workspace of stage 1."""
     B, H, n_q, n_k, d = _check_qkv(q, k, v)
+    _require_mha(q, k, "backward_dkdv")
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
     st = lib().fa_backward_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(do), *_ws(workspace),
@@ -221,6 +251,7 @@ def backward_dkdv(q, k, v, do, workspace, causal=False, scale=None, dk=None, dv=
 def backward_dq(q, k, v, do, workspace, causal=False, scale=None, dq=None):
     """Stage 3: dQ from the workspace of stage 1."""
     B, H, n_q, n_k, d = _check_qkv(q, k, v)
+    _require_mha(q, k, "backward_dq")
     dq = torch.empty_like(q) if dq is None else dq
     st = lib().fa_backward_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(do), *_ws(workspace), _ptr(dq),
                               B, H, n_q, n_k, d, _scale(scale, d), int(bool(causal)),

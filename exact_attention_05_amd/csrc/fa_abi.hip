@@ -78,20 +78,67 @@ int check_workspace(const void* ws, size_t bytes, int B, int H, int n_q) {
 
 fa::BwdArgs make_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
                      const float* lse, const void* ws, void* dq, void* dk, void* dv, int B, int H,
-                     int n_q, int n_k, float scale) {
+                     int n_q, int n_k, float scale, int H_kv) {
   fa::BwdArgs a;
   a.q = q; a.k = k; a.v = v; a.o = o; a.dO = dO; a.lse = lse;
   char* w = static_cast<char*>(const_cast<void*>(ws));
   a.delta = reinterpret_cast<float*>(w);
   a.lse2 = w ? reinterpret_cast<float*>(w + ws_half_bytes(B, H, n_q)) : nullptr;
   a.dq = dq; a.dk = dk; a.dv = dv;
-  a.BH = B * H; a.n_q = n_q; a.n_k = n_k;
+  a.BH = B * H; a.H = H; a.group = H / H_kv; a.n_q = n_q; a.n_k = n_k;
   a.scale = scale;
   a.scale_log2 = scale * 1.4426950408889634f;
   return a;
 }
 
 int status_of(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH; }
+
+// H_kv K/V heads shared by groups of H / H_kv consecutive query heads.
+int check_kv_heads(int H, int H_kv) {
+  if (H_kv < 1 || H_kv > H || H % H_kv != 0) return FA_ERR_INVALID_ARG;
+  return FA_OK;
+}
+
+int forward_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                 int H_kv, int n_q, int n_k, int d, float scale, int causal, int dtype,
+                 void* stream) {
+  int st = first_error(check_sizes(B, H, n_q, n_k, d, dtype), check_kv_heads(H, H_kv),
+                       check_scale_causal(scale, causal), check_tensor(q), check_tensor(k),
+                       check_tensor(v), check_tensor(o), check_rowvec(lse));
+  if (st != FA_OK) return st;
+  fa::FwdArgs a;
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+  a.BH = B * H; a.H = H; a.group = H / H_kv; a.n_q = n_q; a.n_k = n_k;
+  a.scale = scale;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return status_of(dtype == FA_DTYPE_BF16 ? fa::launch_fwd_bf16(a, d, causal != 0, s)
+                                          : fa::launch_fwd_f32(a, d, causal != 0, s));
+}
+
+int backward_impl(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                  const float* lse, void* dq, void* dk, void* dv, void* workspace,
+                  size_t workspace_bytes, int B, int H, int H_kv, int n_q, int n_k, int d,
+                  float scale, int causal, int dtype, void* stream) {
+  int st = first_error(check_sizes(B, H, n_q, n_k, d, dtype), check_kv_heads(H, H_kv),
+                       check_scale_causal(scale, causal), check_tensor(q), check_tensor(k),
+                       check_tensor(v), check_tensor(o), check_tensor(dO), check_rowvec(lse),
+                       check_tensor(dq), check_tensor(dk), check_tensor(dv));
+  if (st != FA_OK) return st;
+  st = check_workspace(workspace, workspace_bytes, B, H, n_q);
+  if (st != FA_OK) return st;
+  fa::BwdArgs a = make_bwd(q, k, v, o, dO, lse, workspace, dq, dk, dv, B, H, n_q, n_k, scale, H_kv);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool bf16 = dtype == FA_DTYPE_BF16;
+  hipError_t e = fa::launch_bwd_preprocess(a, d, bf16, s);
+  if (e != hipSuccess) return FA_ERR_LAUNCH;
+  e = bf16 ? fa::launch_bwd_dkdv_bf16(a, d, causal != 0, s)
+           : fa::launch_bwd_dkdv_f32(a, d, causal != 0, s);
+  if (e != hipSuccess) return FA_ERR_LAUNCH;
+  e = bf16 ? fa::launch_bwd_dq_bf16(a, d, causal != 0, s)
+           : fa::launch_bwd_dq_f32(a, d, causal != 0, s);
+  return status_of(e);
+}
 
 }  // namespace
 
@@ -113,18 +160,13 @@ const char* fa_status_string(int status) {
 
 int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                int n_q, int n_k, int d, float scale, int causal, int dtype, void* stream) {
-  int st = first_error(check_sizes(B, H, n_q, n_k, d, dtype), check_scale_causal(scale, causal),
-                       check_tensor(q), check_tensor(k), check_tensor(v), check_tensor(o),
-                       check_rowvec(lse));
-  if (st != FA_OK) return st;
-  fa::FwdArgs a;
-  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
-  a.BH = B * H; a.n_q = n_q; a.n_k = n_k;
-  a.scale = scale;
-  a.scale_log2 = scale * 1.4426950408889634f;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  return status_of(dtype == FA_DTYPE_BF16 ? fa::launch_fwd_bf16(a, d, causal != 0, s)
-                                          : fa::launch_fwd_f32(a, d, causal != 0, s));
+  return forward_impl(q, k, v, o, lse, B, H, H, n_q, n_k, d, scale, causal, dtype, stream);
+}
+
+int fa_forward_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                   int H_kv, int n_q, int n_k, int d, float scale, int causal, int dtype,
+                   void* stream) {
+  return forward_impl(q, k, v, o, lse, B, H, H_kv, n_q, n_k, d, scale, causal, dtype, stream);
 }
 
 size_t fa_backward_workspace_size(int B, int H, int n_q, int n_k, int d, int dtype) {
@@ -139,7 +181,7 @@ int fa_backward_preprocess(const void* o, const void* dO, const float* lse, void
                        check_rowvec(lse), check_workspace(workspace, workspace_bytes, B, H, n_q));
   if (st != FA_OK) return st;
   fa::BwdArgs a = make_bwd(nullptr, nullptr, nullptr, o, dO, lse, workspace, nullptr, nullptr,
-                           nullptr, B, H, n_q, 1, 0.f);
+                           nullptr, B, H, n_q, 1, 0.f, H);
   return status_of(fa::launch_bwd_preprocess(a, d, dtype == FA_DTYPE_BF16,
                                              static_cast<hipStream_t>(stream)));
 }
@@ -154,7 +196,7 @@ int fa_backward_dkdv(const void* q, const void* k, const void* v, const void* dO
                        check_tensor(dv));
   if (st != FA_OK) return st;
   fa::BwdArgs a = make_bwd(q, k, v, nullptr, dO, nullptr, workspace, nullptr, dk, dv, B, H, n_q,
-                           n_k, scale);
+                           n_k, scale, H);
   hipStream_t s = static_cast<hipStream_t>(stream);
   return status_of(dtype == FA_DTYPE_BF16 ? fa::launch_bwd_dkdv_bf16(a, d, causal != 0, s)
                                           : fa::launch_bwd_dkdv_f32(a, d, causal != 0, s));
@@ -168,7 +210,7 @@ int fa_backward_dq(const void* q, const void* k, const void* v, const void* dO,
                        check_workspace(workspace, workspace_bytes, B, H, n_q), check_tensor(dq));
   if (st != FA_OK) return st;
   fa::BwdArgs a = make_bwd(q, k, v, nullptr, dO, nullptr, workspace, dq, nullptr, nullptr, B, H,
-                           n_q, n_k, scale);
+                           n_q, n_k, scale, H);
   hipStream_t s = static_cast<hipStream_t>(stream);
   return status_of(dtype == FA_DTYPE_BF16 ? fa::launch_bwd_dq_bf16(a, d, causal != 0, s)
                                           : fa::launch_bwd_dq_f32(a, d, causal != 0, s));
@@ -178,24 +220,16 @@ int fa_backward(const void* q, const void* k, const void* v, const void* o, cons
                 const float* lse, void* dq, void* dk, void* dv, void* workspace,
                 size_t workspace_bytes, int B, int H, int n_q, int n_k, int d, float scale,
                 int causal, int dtype, void* stream) {
-  int st = first_error(check_sizes(B, H, n_q, n_k, d, dtype), check_scale_causal(scale, causal),
-                       check_tensor(q), check_tensor(k), check_tensor(v), check_tensor(o),
-                       check_tensor(dO), check_rowvec(lse), check_tensor(dq), check_tensor(dk),
-                       check_tensor(dv));
-  if (st != FA_OK) return st;
-  st = check_workspace(workspace, workspace_bytes, B, H, n_q);
-  if (st != FA_OK) return st;
-  fa::BwdArgs a = make_bwd(q, k, v, o, dO, lse, workspace, dq, dk, dv, B, H, n_q, n_k, scale);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const bool bf16 = dtype == FA_DTYPE_BF16;
-  hipError_t e = fa::launch_bwd_preprocess(a, d, bf16, s);
-  if (e != hipSuccess) return FA_ERR_LAUNCH;
-  e = bf16 ? fa::launch_bwd_dkdv_bf16(a, d, causal != 0, s)
-           : fa::launch_bwd_dkdv_f32(a, d, causal != 0, s);
-  if (e != hipSuccess) return FA_ERR_LAUNCH;
-  e = bf16 ? fa::launch_bwd_dq_bf16(a, d, causal != 0, s)
-           : fa::launch_bwd_dq_f32(a, d, causal != 0, s);
-  return status_of(e);
+  return backward_impl(q, k, v, o, dO, lse, dq, dk, dv, workspace, workspace_bytes, B, H, H, n_q,
+                       n_k, d, scale, causal, dtype, stream);
+}
+
+int fa_backward_gqa(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                    const float* lse, void* dq, void* dk, void* dv, void* workspace,
+                    size_t workspace_bytes, int B, int H, int H_kv, int n_q, int n_k, int d,
+                    float scale, int causal, int dtype, void* stream) {
+  return backward_impl(q, k, v, o, dO, lse, dq, dk, dv, workspace, workspace_bytes, B, H, H_kv,
+                       n_q, n_k, d, scale, causal, dtype, stream);
 }
 
 }  // extern "C"

@@ -103,9 +103,11 @@ struct DkdvCfg {
   static constexpr int kRowVecBytes = kBQ * 4;   // one stage of LSE2 or D
 };
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool GROUPED>
 __global__ __launch_bounds__(256) void bwd_dkdv_bf16_kernel(BwdArgs a, int n_ktiles) {
   using C = DkdvCfg<D>;
+  // Query heads per K/V head, a compile-time 1 without sharing.
+  const int group = GROUPED ? a.group : 1;
   __shared__ __attribute__((aligned(1024))) char sq[2][C::QT::kBytes];
   __shared__ __attribute__((aligned(1024))) char sdo[2][C::QT::kBytes];
   __shared__ __attribute__((aligned(16))) float slse[2][C::kBQ];
@@ -113,9 +115,13 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16_kernel(BwdArgs a, int n_kti
 
   // The workgroups with the first keys see the most query blocks under the
   // causal mask; they come first in the natural order.
+  // One workgroup per (key tile, batch * K/V head); with shared K/V heads it
+  // sums dK and dV over the query heads of its group.
   const int work = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = work / n_ktiles;
-  const int kt = work - bh * n_ktiles;
+  const int bhkv = work / n_ktiles;
+  const int kt = work - bhkv * n_ktiles;
+  const int h_kv = a.H / group;
+  const int bh0 = GROUPED ? (bhkv / h_kv) * a.H + (bhkv % h_kv) * group : bhkv;  // first query head
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -127,12 +133,13 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16_kernel(BwdArgs a, int n_kti
   const int k0 = kt * C::kBK;
   const int key = k0 + wave * 32 + l32;  // this lane's key (a column of S)
 
-  const __bf16* qp = static_cast<const __bf16*>(a.q) + (size_t)bh * n_q * D;
-  const __bf16* dop = static_cast<const __bf16*>(a.dO) + (size_t)bh * n_q * D;
-  const __bf16* kp = static_cast<const __bf16*>(a.k) + (size_t)bh * n_k * D;
-  const __bf16* vp = static_cast<const __bf16*>(a.v) + (size_t)bh * n_k * D;
-  const float* lsep = a.lse2 + (size_t)bh * n_q;
-  const float* delp = a.delta + (size_t)bh * n_q;
+  // Query-side rows of the current query head (advanced per head below).
+  const __bf16* qp = static_cast<const __bf16*>(a.q) + (size_t)bh0 * n_q * D;
+  const __bf16* dop = static_cast<const __bf16*>(a.dO) + (size_t)bh0 * n_q * D;
+  const float* lsep = a.lse2 + (size_t)bh0 * n_q;
+  const float* delp = a.delta + (size_t)bh0 * n_q;
+  const __bf16* kp = static_cast<const __bf16*>(a.k) + (size_t)bhkv * n_k * D;
+  const __bf16* vp = static_cast<const __bf16*>(a.v) + (size_t)bhkv * n_k * D;
 
   // The lane's K and V rows stay in registers as the B operands of
   // S = Q K^T and dP = dO V^T.
@@ -370,39 +377,55 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16_kernel(BwdArgs a, int n_kti
     }
   };
 
-  if (nblocks > 0) {
-    load_block(0, 0);
-    int b = 0;
-    if (any_masked)
-      for (; b < b_lo; ++b) masked_stage(b);
-    // Unmasked stages [b, b_hi) through the pipeline, in pairs with fixed
-    // buffers; its state starts empty (zero probabilities for the "previous"
-    // sub-block of the first iteration).
-    if (b < b_hi) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) { ex[i] = 0.f; dd[i] = 0.f; }
-      if (b & 1) {
-        do_stage(F{}, B1{}, b);
-        ++b;
-      }
-      for (; b + 1 < b_hi; b += 2) {
-        do_stage(F{}, B0{}, b);
-        do_stage(F{}, B1{}, b + 1);
-      }
+  // One pass over the query stages of one query head.
+  auto one_head = [&]() __attribute__((always_inline)) {
+      load_block(0, 0);
+      int b = 0;
+      if (any_masked)
+        for (; b < b_lo; ++b) masked_stage(b);
+      // Unmasked stages [b, b_hi) through the pipeline, in pairs with fixed
+      // buffers; its state starts empty (zero probabilities for the "previous"
+      // sub-block of the first iteration).
       if (b < b_hi) {
-        do_stage(F{}, B0{}, b);
-        ++b;
+  #pragma unroll
+        for (int i = 0; i < 16; ++i) { ex[i] = 0.f; dd[i] = 0.f; }
+        if (b & 1) {
+          do_stage(F{}, B1{}, b);
+          ++b;
+        }
+        for (; b + 1 < b_hi; b += 2) {
+          do_stage(F{}, B0{}, b);
+          do_stage(F{}, B1{}, b + 1);
+        }
+        if (b < b_hi) {
+          do_stage(F{}, B0{}, b);
+          ++b;
+        }
+        if ((b - 1) & 1) finish(B1{});
+        else finish(B0{});
       }
-      if ((b - 1) & 1) finish(B1{});
-      else finish(B0{});
+      if (any_masked)
+        for (; b < nblocks; ++b) masked_stage(b);
+  };
+  if constexpr (!GROUPED) {
+    if (nblocks > 0) one_head();
+  } else {
+    for (int g = 0; g < group && nblocks > 0; ++g) {
+      if (g > 0) {
+        qp += (size_t)n_q * D;
+        dop += (size_t)n_q * D;
+        lsep += n_q;
+        delp += n_q;
+        // Every wave is past the previous head's last reads of buffer 0.
+        phase_barrier();
+      }
+      one_head();
     }
-    if (any_masked)
-      for (; b < nblocks; ++b) masked_stage(b);
   }
 
   if (key < n_k) {
-    __bf16* dkp = static_cast<__bf16*>(a.dk) + ((size_t)bh * n_k + key) * D;
-    __bf16* dvp = static_cast<__bf16*>(a.dv) + ((size_t)bh * n_k + key) * D;
+    __bf16* dkp = static_cast<__bf16*>(a.dk) + ((size_t)bhkv * n_k + key) * D;
+    __bf16* dvp = static_cast<__bf16*>(a.dv) + ((size_t)bhkv * n_k + key) * D;
 #pragma unroll
     for (int db = 0; db < C::kDB; ++db)
 #pragma unroll
@@ -457,8 +480,9 @@ __global__ __launch_bounds__(512) void bwd_dq_bf16_kernel(BwdArgs a, int n_qtile
 
   const __bf16* qp = static_cast<const __bf16*>(a.q) + (size_t)bh * n_q * D;
   const __bf16* dop = static_cast<const __bf16*>(a.dO) + (size_t)bh * n_q * D;
-  const __bf16* kp = static_cast<const __bf16*>(a.k) + (size_t)bh * n_k * D;
-  const __bf16* vp = static_cast<const __bf16*>(a.v) + (size_t)bh * n_k * D;
+  const int kvh = kv_head_index(bh, a.H, a.group);
+  const __bf16* kp = static_cast<const __bf16*>(a.k) + (size_t)kvh * n_k * D;
+  const __bf16* vp = static_cast<const __bf16*>(a.v) + (size_t)kvh * n_k * D;
 
   bf16x8 qf[C::kDC], gf[C::kDC];
 #pragma unroll
@@ -585,9 +609,13 @@ __global__ __launch_bounds__(256) void bwd_dkdv_f32_kernel(BwdArgs a, int n_ktil
   __shared__ float slse[2][C::kBS];
   __shared__ float sdel[2][C::kBS];
 
+  // One workgroup per (key tile, batch * K/V head), summing over the query
+  // heads that share the K/V head.
   const int work = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = work / n_ktiles;
-  const int kt = work - bh * n_ktiles;
+  const int bhkv = work / n_ktiles;
+  const int kt = work - bhkv * n_ktiles;
+  const int h_kv = a.H / a.group;
+  const int bh0 = (bhkv / h_kv) * a.H + (bhkv % h_kv) * a.group;
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
@@ -598,12 +626,12 @@ __global__ __launch_bounds__(256) void bwd_dkdv_f32_kernel(BwdArgs a, int n_ktil
   const int kw = k0 + wave * 32;
   const int key = kw + l32;
 
-  const float* qp = static_cast<const float*>(a.q) + (size_t)bh * n_q * D;
-  const float* dop = static_cast<const float*>(a.dO) + (size_t)bh * n_q * D;
-  const float* kp = static_cast<const float*>(a.k) + (size_t)bh * n_k * D;
-  const float* vp = static_cast<const float*>(a.v) + (size_t)bh * n_k * D;
-  const float* lsep = a.lse2 + (size_t)bh * n_q;
-  const float* delp = a.delta + (size_t)bh * n_q;
+  const float* qp = nullptr;
+  const float* dop = nullptr;
+  const float* lsep = nullptr;
+  const float* delp = nullptr;
+  const float* kp = static_cast<const float*>(a.k) + (size_t)bhkv * n_k * D;
+  const float* vp = static_cast<const float*>(a.v) + (size_t)bhkv * n_k * D;
 
   // K and V rows of this lane's key, as B operands (d = 2c + hi).
   float kreg[D / 2], vreg[D / 2];
@@ -660,6 +688,12 @@ __global__ __launch_bounds__(256) void bwd_dkdv_f32_kernel(BwdArgs a, int n_ktil
 #pragma unroll
   for (int db = 0; db < C::kDB; ++db) { dk[db] = f32x16{}; dv[db] = f32x16{}; }
 
+  for (int g = 0; g < a.group; ++g) {
+  const size_t bh = (size_t)(bh0 + g);
+  qp = static_cast<const float*>(a.q) + bh * n_q * D;
+  dop = static_cast<const float*>(a.dO) + bh * n_q * D;
+  lsep = a.lse2 + bh * n_q;
+  delp = a.delta + bh * n_q;
   if (nblocks > 0) {
     gload(0);
     swrite(0);
@@ -704,10 +738,11 @@ __global__ __launch_bounds__(256) void bwd_dkdv_f32_kernel(BwdArgs a, int n_ktil
     if (b + 1 < nblocks) swrite(buf ^ 1);
     __syncthreads();
   }
+  }  // query heads of the group
 
   if (key < n_k) {
-    float* dkp = static_cast<float*>(a.dk) + ((size_t)bh * n_k + key) * D;
-    float* dvp = static_cast<float*>(a.dv) + ((size_t)bh * n_k + key) * D;
+    float* dkp = static_cast<float*>(a.dk) + ((size_t)bhkv * n_k + key) * D;
+    float* dvp = static_cast<float*>(a.dv) + ((size_t)bhkv * n_k + key) * D;
 #pragma unroll
     for (int db = 0; db < C::kDB; ++db)
 #pragma unroll
@@ -747,8 +782,9 @@ __global__ __launch_bounds__(256) void bwd_dq_f32_kernel(BwdArgs a, int n_qtiles
 
   const float* qp = static_cast<const float*>(a.q) + (size_t)bh * n_q * D;
   const float* dop = static_cast<const float*>(a.dO) + (size_t)bh * n_q * D;
-  const float* kp = static_cast<const float*>(a.k) + (size_t)bh * n_k * D;
-  const float* vp = static_cast<const float*>(a.v) + (size_t)bh * n_k * D;
+  const int kvh = kv_head_index(bh, a.H, a.group);
+  const float* kp = static_cast<const float*>(a.k) + (size_t)kvh * n_k * D;
+  const float* vp = static_cast<const float*>(a.v) + (size_t)kvh * n_k * D;
 
   // Q and dO rows of this lane's query, as B operands (d = 2c + hi).
   float qreg[D / 2], greg[D / 2];
@@ -861,8 +897,10 @@ hipError_t dkdv_bf16_t(const BwdArgs& a, hipStream_t s) {
   BwdArgs args = a;
   int nt = n_ktiles;
   void* params[] = {&args, &nt};
-  return launch_raw(reinterpret_cast<const void*>(bwd_dkdv_bf16_kernel<D, CAUSAL>),
-                    n_ktiles * a.BH, C::kThreads, params, s);
+  const void* kernel = a.group == 1
+                           ? reinterpret_cast<const void*>(bwd_dkdv_bf16_kernel<D, CAUSAL, false>)
+                           : reinterpret_cast<const void*>(bwd_dkdv_bf16_kernel<D, CAUSAL, true>);
+  return launch_raw(kernel, n_ktiles * (a.BH / a.group), C::kThreads, params, s);
 }
 
 template <int D, bool CAUSAL>
@@ -883,7 +921,7 @@ hipError_t dkdv_f32_t(const BwdArgs& a, hipStream_t s) {
   int nt = n_ktiles;
   void* params[] = {&args, &nt};
   return launch_raw(reinterpret_cast<const void*>(bwd_dkdv_f32_kernel<D, CAUSAL>),
-                    n_ktiles * a.BH, F32BwdCfg<D>::kThreads, params, s);
+                    n_ktiles * (a.BH / a.group), F32BwdCfg<D>::kThreads, params, s);
 }
 
 template <int D, bool CAUSAL>

@@ -83,8 +83,9 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdArgs a, int n_qtiles) 
   const float sl2 = a.scale_log2;
 
   const __bf16* qp = static_cast<const __bf16*>(a.q) + (size_t)bh * n_q * D;
-  const __bf16* kp = static_cast<const __bf16*>(a.k) + (size_t)bh * n_k * D;
-  const __bf16* vp = static_cast<const __bf16*>(a.v) + (size_t)bh * n_k * D;
+  const int kvh = kv_head_index(bh, a.H, a.group);
+  const __bf16* kp = static_cast<const __bf16*>(a.k) + (size_t)kvh * n_k * D;
+  const __bf16* vp = static_cast<const __bf16*>(a.v) + (size_t)kvh * n_k * D;
 
   // Q fragments: B operand of S^T = K Q^T, kept for the whole pass.
   bf16x8 qf[C::kDC];
@@ -326,8 +327,9 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdArgs a, int n_qtiles) {
   const int n_q = a.n_q, n_k = a.n_k;
 
   const float* qp = static_cast<const float*>(a.q) + (size_t)bh * n_q * D;
-  const float* kp = static_cast<const float*>(a.k) + (size_t)bh * n_k * D;
-  const float* vp = static_cast<const float*>(a.v) + (size_t)bh * n_k * D;
+  const int kvh = kv_head_index(bh, a.H, a.group);
+  const float* kp = static_cast<const float*>(a.k) + (size_t)kvh * n_k * D;
+  const float* vp = static_cast<const float*>(a.v) + (size_t)kvh * n_k * D;
 
   const int qi = qw + l32;
   float qf[D / 2];

@@ -14,7 +14,9 @@ struct FwdArgs {
   const void* v;
   void* o;
   float* lse;
-  int BH;           // B * H
+  int BH;           // B * H (query heads)
+  int H;            // query heads per batch entry
+  int group;        // query heads per K/V head (H / H_kv); 1 without sharing
   int n_q;
   int n_k;
   float scale;      // softmax scale on q . k
@@ -32,14 +34,24 @@ struct BwdArgs {
   float* delta;     // workspace: (B,H,n_q) float32 row sums of dO * O
   float* lse2;      // workspace: (B,H,n_q) float32 LSE * log2(e)
   void* dq;
-  void* dk;
+  void* dk;         // (B,H_kv,n_k,d), like k
   void* dv;
-  int BH;
+  int BH;           // B * H (query heads)
+  int H;            // query heads per batch entry
+  int group;        // query heads per K/V head (H / H_kv)
   int n_q;
   int n_k;
   float scale;
   float scale_log2;
 };
+
+// (batch, K/V head) index of the query head bh = b * H + h.  Query heads are
+// grouped consecutively: heads h = j * group .. j * group + group - 1 share
+// K/V head j ("Attention Mechanism", section 12 "GQA vs MQA").
+__host__ __device__ inline int kv_head_index(int bh, int H, int group) {
+  if (group == 1) return bh;
+  return (bh / H) * (H / group) + (bh % H) / group;
+}
 
 // Each launcher enqueues its kernel(s) on `stream` and returns the HIP status
 // of the launch.  Shapes were validated by the caller.

@@ -128,6 +128,27 @@ int fa_backward_dq(const void* q, const void* k, const void* v, const void* dO,
                    int B, int H, int n_q, int n_k, int d, float scale, int causal,
                    int dtype, void* stream);
 
+/* Grouped-query and multi-query attention ("Attention Mechanism: Revolusi
+ * Representasi Sequence", section 12 "GQA vs MQA -- KV Cache Optimization"):
+ * k and v hold H_kv heads, (B,H_kv,n_k,d), and query heads
+ * h = j*(H/H_kv) .. (j+1)*(H/H_kv) - 1 all attend to K/V head j -- the same
+ * result as repeating every K/V head H/H_kv times along the head axis.
+ * H_kv = H is fa_forward; H_kv = 1 is multi-query attention.  H_kv must
+ * divide H (otherwise FA_ERR_INVALID_ARG); everything else as fa_forward. */
+int fa_forward_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int H, int H_kv, int n_q, int n_k, int d, float scale,
+                   int causal, int dtype, void* stream);
+
+/* Backward pass of fa_forward_gqa.  dk and dv are (B,H_kv,n_k,d): the
+ * gradient of a shared K/V head is the sum over the query heads of its
+ * group (the adjoint of the repetition).  dq, workspace and errors as for
+ * fa_backward (the workspace is sized for the H query heads). */
+int fa_backward_gqa(const void* q, const void* k, const void* v, const void* o,
+                    const void* dO, const float* lse, void* dq, void* dk, void* dv,
+                    void* workspace, size_t workspace_bytes,
+                    int B, int H, int H_kv, int n_q, int n_k, int d, float scale,
+                    int causal, int dtype, void* stream);
+
 /* Static text for a status code ("unknown status" for other values). */
 const char* fa_status_string(int status);
 

@@ -63,6 +63,9 @@ __all__ = [
     "attention_bwd_bruteforce",
     "score_bytes",
     "attention_flops",
+    "expand_kv_heads",
+    "attention_fwd_gqa",
+    "attention_bwd_gqa",
 ]
 
 
@@ -342,3 +345,46 @@ def attention_flops(batch: int, heads: int, n_q: int, n_k: int, d: int, causal: 
         pairs = int(n_q) * int(n_k)
     per_pair = 10 * d if backward else 4 * d
     return int(batch) * int(heads) * pairs * per_pair
+
+
+# ------------------------------------------------------ grouped K/V heads
+
+
+def expand_kv_heads(x, n_heads: int) -> np.ndarray:
+    """K or V of shape (..., H_kv, n, d) repeated to (..., H, n, d).
+
+    "Attention Mechanism", section 12 "GQA vs MQA -- KV Cache Optimization":
+    the H query heads fall into H_kv consecutive groups of H / H_kv, and every
+    head of group j uses K/V head j; the page computes this by repeating each
+    K/V head H / H_kv times along the head axis (H_kv = H is ordinary
+    multi-head attention, H_kv = 1 is multi-query attention).
+    """
+    x = _f64(x)
+    h_kv = x.shape[-3]
+    if h_kv < 1 or n_heads % h_kv != 0:
+        raise ValueError(f"{h_kv} K/V heads do not divide {n_heads} query heads")
+    return np.repeat(x, n_heads // h_kv, axis=-3)
+
+
+def attention_fwd_gqa(q, k, v, scale: float, causal: bool = False):
+    """Forward pass with shared K/V heads: q (..., H, n_q, d), k and v
+    (..., H_kv, n_k, d).  Defined as attention_fwd on the repeated K/V."""
+    h = np.shape(q)[-3]
+    return attention_fwd(q, expand_kv_heads(k, h), expand_kv_heads(v, h), scale, causal)
+
+
+def attention_bwd_gqa(q, k, v, do, scale: float, causal: bool = False):
+    """Backward pass of attention_fwd_gqa: (dQ, dK, dV) with dK, dV shaped
+    like k.  The repetition is linear, so the gradient of a shared K/V head is
+    the sum of the gradients of its copies, i.e. over the query heads of its
+    group."""
+    h = np.shape(q)[-3]
+    h_kv = np.shape(k)[-3]
+    dq, dk, dv = attention_bwd(q, expand_kv_heads(k, h), expand_kv_heads(v, h), do, scale, causal)
+    g = h // h_kv
+
+    def fold(x):
+        return x.reshape(x.shape[:-3] + (h_kv, g) + x.shape[-2:]).sum(axis=-3)
+
+    return dq, fold(dk), fold(dv)
+

@@ -135,3 +135,20 @@ def test_binding_validates_shapes_before_calling():
     q = torch.zeros(1, 1, 8, 64)
     with pytest.raises(ValueError):
         fa.forward(q, q, q)  # CPU tensors are refused before any library call
+
+
+@pytest.mark.parametrize("H,H_kv", [(8, 0), (8, 3), (8, 16), (4, -1)])
+def test_gqa_rejects_bad_head_counts(H, H_kv):
+    L = fa.lib()
+    assert L.fa_forward_gqa(P, P, P, P2, P2, 1, H, H_kv, 8, 8, 64, 0.125, 0, 1, None) == fa.FA_ERR_INVALID_ARG
+    assert L.fa_backward_gqa(P, P, P, P, P, P, P2, P2, P2, P2, 1 << 20, 1, H, H_kv, 8, 8, 64, 0.125,
+                             0, 1, None) == fa.FA_ERR_INVALID_ARG
+
+
+def test_gqa_validates_like_forward():
+    L = fa.lib()
+    assert L.fa_forward_gqa(P, P, P, P2, P2, 1, 8, 2, 8, 8, 48, 0.125, 0, 1, None) == fa.FA_ERR_UNSUPPORTED
+    assert L.fa_forward_gqa(P, MIS, P, P2, P2, 1, 8, 2, 8, 8, 64, 0.125, 0, 1, None) == fa.FA_ERR_ALIGNMENT
+    assert L.fa_backward_gqa(P, P, P, P, P, P, P2, P2, P2, None, 1 << 20, 1, 8, 2, 8, 8, 64, 0.125,
+                             0, 1, None) == fa.FA_ERR_WORKSPACE
+

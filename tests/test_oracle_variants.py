@@ -1,0 +1,110 @@
+"""Pins for the oracle's attention variants (shared K/V heads, ...): each is
+checked against something other than its own definition -- brute force per
+head, finite differences of its own forward, and the special cases that
+reduce it to ordinary multi-head attention."""
+import numpy as np
+import pytest
+
+import oracle
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+# ------------------------------------------------------ grouped K/V heads
+
+def test_expand_kv_heads_groups_consecutive_query_heads():
+    # section 12's picture: 8 query heads over 2 K/V heads -> Q0..Q3 use K0,
+    # Q4..Q7 use K1.
+    k = np.stack([np.full((3, 2), j, dtype=float) for j in range(2)])  # (2, 3, 2), head j filled with j
+    e = oracle.expand_kv_heads(k, 8)
+    assert e.shape == (8, 3, 2)
+    assert [int(e[h, 0, 0]) for h in range(8)] == [0, 0, 0, 0, 1, 1, 1, 1]
+    with pytest.raises(ValueError):
+        oracle.expand_kv_heads(np.zeros((3, 4, 2)), 8)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("h_kv", [1, 2, 4])
+def test_gqa_forward_matches_per_head_bruteforce(h_kv, causal):
+    r = _rng(41 + h_kv)
+    H, n_q, n_k, d = 4, 6, 7, 3
+    q = r.standard_normal((H, n_q, d))
+    k = r.standard_normal((h_kv, n_k, d))
+    v = r.standard_normal((h_kv, n_k, d))
+    o, lse = oracle.attention_fwd_gqa(q, k, v, 0.7, causal)
+    for h in range(H):
+        j = h // (H // h_kv)
+        ob, lb = oracle.attention_fwd_bruteforce(q[h], k[j], v[j], 0.7, causal)
+        np.testing.assert_allclose(o[h], ob, atol=1e-13)
+        np.testing.assert_allclose(lse[h], lb, atol=1e-13)
+
+
+def test_gqa_with_one_group_per_head_is_multi_head():
+    r = _rng(43)
+    q, k, v, do = (r.standard_normal((3, 5, 4)) for _ in range(4))
+    o1, l1 = oracle.attention_fwd_gqa(q, k, v, 0.5, True)
+    o2, l2 = oracle.attention_fwd(q, k, v, 0.5, True)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(l1, l2)
+    got = oracle.attention_bwd_gqa(q, k, v, do, 0.5, True)
+    for h in range(3):
+        ref = oracle.attention_bwd_bruteforce(q[h], k[h], v[h], do[h], 0.5, True)
+        for a, b in zip(got, ref):
+            np.testing.assert_allclose(a[h], b, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("h_kv", [1, 2])
+def test_gqa_backward_finite_differences(h_kv, causal):
+    # the loss sum(dO * O) of the grouped forward, differentiated numerically
+    # in every element of q, of the shared k and of the shared v.
+    r = _rng(47 + h_kv)
+    H, n_q, n_k, d = 4, 4, 5, 2
+    q = r.standard_normal((H, n_q, d))
+    k = r.standard_normal((h_kv, n_k, d))
+    v = r.standard_normal((h_kv, n_k, d))
+    do = r.standard_normal((H, n_q, d))
+    scale = 0.8
+    dq, dk, dv = oracle.attention_bwd_gqa(q, k, v, do, scale, causal)
+    assert dk.shape == k.shape and dv.shape == v.shape
+
+    def loss():
+        o, _ = oracle.attention_fwd_gqa(q, k, v, scale, causal)
+        return float(np.sum(do * o))
+
+    h = 1e-6
+    for x, g in ((q, dq), (k, dk), (v, dv)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            old = x[idx]
+            x[idx] = old + h
+            lp = loss()
+            x[idx] = old - h
+            lm = loss()
+            x[idx] = old
+            num[idx] = (lp - lm) / (2 * h)
+        np.testing.assert_allclose(g, num, rtol=1e-6, atol=1e-8)
+
+
+def test_mqa_value_gradient_is_sum_over_heads_of_p_transpose_do():
+    # dV of the single shared head equals sum_h P_h^T dO_h, with each P_h
+    # from the scalar brute-force softmax.
+    r = _rng(53)
+    H, n, d = 3, 5, 2
+    q = r.standard_normal((H, n, d))
+    k = r.standard_normal((1, n, d))
+    v = r.standard_normal((1, n, d))
+    do = r.standard_normal((H, n, d))
+    _, _, dv = oracle.attention_bwd_gqa(q, k, v, do, 0.9, False)
+    ref = np.zeros((n, d))
+    for h in range(H):
+        for i in range(n):
+            s = [0.9 * float(np.dot(q[h, i], k[0, j])) for j in range(n)]
+            m = max(s)
+            e = [np.exp(x - m) for x in s]
+            z = sum(e)
+            for j in range(n):
+                ref[j] += (e[j] / z) * do[h, i]
+    np.testing.assert_allclose(dv[0], ref, atol=1e-12)
