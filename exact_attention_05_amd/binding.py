@@ -71,6 +71,11 @@ def lib() -> ctypes.CDLL:
         L.fa_backward_gqa.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
                                       i, i, i, i, i, i, f, i, i, vp]
         L.fa_backward_gqa.restype = i
+        L.fa_forward_ext.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, i, i, vp]
+        L.fa_forward_ext.restype = i
+        L.fa_backward_ext.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
+                                      i, i, i, i, i, i, f, i, i, i, i, vp]
+        L.fa_backward_ext.restype = i
         L.fa_status_string.argtypes = [i]
         L.fa_status_string.restype = ctypes.c_char_p
         L.fa_version.argtypes = []
@@ -129,13 +134,17 @@ def _scale(scale, d):
     return 1.0 / math.sqrt(d) if scale is None else float(scale)
 
 
-def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None):
+def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None,
+            q_offset: int = 0, window: int | None = None):
     """O, LSE = attention(q, k, v).  q: (B,H,n_q,d); k, v: (B,H_kv,n_k,d) with H_kv
     dividing H (H_kv < H shares each K/V head among H/H_kv consecutive query
     heads: grouped-query or, with H_kv = 1, multi-query attention).
 
     Returns O (q's dtype, (B,H,n_q,d)) and LSE (float32, (B,H,n_q)).
-    ``scale`` defaults to 1/sqrt(d).
+    ``scale`` defaults to 1/sqrt(d).  ``q_offset`` places query row i at key
+    position i + q_offset for the causal mask and the window; ``window`` = w
+    keeps only keys within +-w of that position (None: no window).  A row that
+    sees no key gets O = 0 and LSE = -inf.
     """
     B, H, n_q, n_k, d = _check_qkv(q, k, v)
     if out is None:
@@ -147,7 +156,13 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None,
     if lse.shape != (B, H, n_q) or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.device != q.device:
         raise ValueError("lse must be a contiguous float32 (B, H, n_q) tensor")
     h_kv = k.shape[1]
-    if h_kv == H:
+    if q_offset != 0 or window is not None:
+        st = lib().fa_forward_ext(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, h_kv, n_q,
+                                  n_k, d, _scale(scale, d), int(bool(causal)), int(q_offset),
+                                  -1 if window is None else int(window), _DTYPES[q.dtype],
+                                  _stream(q.device))
+        _check(st, "fa_forward_ext")
+    elif h_kv == H:
         st = lib().fa_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, n_q, n_k, d,
                               _scale(scale, d), int(bool(causal)), _DTYPES[q.dtype], _stream(q.device))
         _check(st, "fa_forward")
@@ -169,7 +184,8 @@ def _check_like(name, t, ref):
 
 
 def backward(q, k, v, o, do, lse, causal: bool = False, scale: float | None = None,
-             dq=None, dk=None, dv=None, workspace=None):
+             dq=None, dk=None, dv=None, workspace=None, q_offset: int = 0,
+             window: int | None = None):
     """dQ, dK, dV from the saved o and lse of ``forward``; dK, dV have k's shape."""
     B, H, n_q, n_k, d = _check_qkv(q, k, v)
     _check_like("o", o, q)
@@ -185,7 +201,14 @@ def backward(q, k, v, o, do, lse, causal: bool = False, scale: float | None = No
     if workspace is None:
         workspace = backward_workspace(B, H, n_q, n_k, d, q.dtype, q.device)
     h_kv = k.shape[1]
-    if h_kv == H:
+    if q_offset != 0 or window is not None:
+        st = lib().fa_backward_ext(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse),
+                                   _ptr(dq), _ptr(dk), _ptr(dv), *_ws(workspace),
+                                   B, H, h_kv, n_q, n_k, d, _scale(scale, d), int(bool(causal)),
+                                   int(q_offset), -1 if window is None else int(window),
+                                   _DTYPES[q.dtype], _stream(q.device))
+        _check(st, "fa_backward_ext")
+    elif h_kv == H:
         st = lib().fa_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq),
                                _ptr(dk), _ptr(dv), *_ws(workspace),
                                B, H, n_q, n_k, d, _scale(scale, d), int(bool(causal)),

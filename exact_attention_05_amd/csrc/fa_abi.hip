@@ -78,7 +78,7 @@ int check_workspace(const void* ws, size_t bytes, int B, int H, int n_q) {
 
 fa::BwdArgs make_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
                      const float* lse, const void* ws, void* dq, void* dk, void* dv, int B, int H,
-                     int n_q, int n_k, float scale, int H_kv) {
+                     int n_q, int n_k, float scale, int H_kv, int q_offset = 0, int window = -1) {
   fa::BwdArgs a;
   a.q = q; a.k = k; a.v = v; a.o = o; a.dO = dO; a.lse = lse;
   char* w = static_cast<char*>(const_cast<void*>(ws));
@@ -86,6 +86,7 @@ fa::BwdArgs make_bwd(const void* q, const void* k, const void* v, const void* o,
   a.lse2 = w ? reinterpret_cast<float*>(w + ws_half_bytes(B, H, n_q)) : nullptr;
   a.dq = dq; a.dk = dk; a.dv = dv;
   a.BH = B * H; a.H = H; a.group = H / H_kv; a.n_q = n_q; a.n_k = n_k;
+  a.q_offset = q_offset; a.window = window;
   a.scale = scale;
   a.scale_log2 = scale * 1.4426950408889634f;
   return a;
@@ -99,16 +100,30 @@ int check_kv_heads(int H, int H_kv) {
   return FA_OK;
 }
 
+// Query offset and window half-width within +-2^29, and with either of them
+// in use also n_q, n_k <= 2^29, so that the position arithmetic of the mask
+// (row + offset +- window) stays within 32-bit ints; window -1 means none.
+constexpr int kMaxBand = 1 << 29;
+int check_band(int n_q, int n_k, int q_offset, int window) {
+  if (q_offset < -kMaxBand || q_offset > kMaxBand) return FA_ERR_INVALID_ARG;
+  if (window < -1 || window > kMaxBand) return FA_ERR_INVALID_ARG;
+  if ((q_offset != 0 || window != -1) && (n_q > kMaxBand || n_k > kMaxBand))
+    return FA_ERR_INVALID_ARG;
+  return FA_OK;
+}
+
 int forward_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                  int H_kv, int n_q, int n_k, int d, float scale, int causal, int dtype,
-                 void* stream) {
+                 void* stream, int q_offset = 0, int window = -1) {
   int st = first_error(check_sizes(B, H, n_q, n_k, d, dtype), check_kv_heads(H, H_kv),
-                       check_scale_causal(scale, causal), check_tensor(q), check_tensor(k),
-                       check_tensor(v), check_tensor(o), check_rowvec(lse));
+                       check_band(n_q, n_k, q_offset, window), check_scale_causal(scale, causal),
+                       check_tensor(q), check_tensor(k), check_tensor(v), check_tensor(o),
+                       check_rowvec(lse));
   if (st != FA_OK) return st;
   fa::FwdArgs a;
   a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
   a.BH = B * H; a.H = H; a.group = H / H_kv; a.n_q = n_q; a.n_k = n_k;
+  a.q_offset = q_offset; a.window = window;
   a.scale = scale;
   a.scale_log2 = scale * 1.4426950408889634f;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -119,15 +134,18 @@ int forward_impl(const void* q, const void* k, const void* v, void* o, float* ls
 int backward_impl(const void* q, const void* k, const void* v, const void* o, const void* dO,
                   const float* lse, void* dq, void* dk, void* dv, void* workspace,
                   size_t workspace_bytes, int B, int H, int H_kv, int n_q, int n_k, int d,
-                  float scale, int causal, int dtype, void* stream) {
+                  float scale, int causal, int dtype, void* stream, int q_offset = 0,
+                  int window = -1) {
   int st = first_error(check_sizes(B, H, n_q, n_k, d, dtype), check_kv_heads(H, H_kv),
+                       check_band(n_q, n_k, q_offset, window),
                        check_scale_causal(scale, causal), check_tensor(q), check_tensor(k),
                        check_tensor(v), check_tensor(o), check_tensor(dO), check_rowvec(lse),
                        check_tensor(dq), check_tensor(dk), check_tensor(dv));
   if (st != FA_OK) return st;
   st = check_workspace(workspace, workspace_bytes, B, H, n_q);
   if (st != FA_OK) return st;
-  fa::BwdArgs a = make_bwd(q, k, v, o, dO, lse, workspace, dq, dk, dv, B, H, n_q, n_k, scale, H_kv);
+  fa::BwdArgs a = make_bwd(q, k, v, o, dO, lse, workspace, dq, dk, dv, B, H, n_q, n_k, scale, H_kv,
+                           q_offset, window);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool bf16 = dtype == FA_DTYPE_BF16;
   hipError_t e = fa::launch_bwd_preprocess(a, d, bf16, s);
@@ -216,6 +234,13 @@ int fa_backward_dq(const void* q, const void* k, const void* v, const void* dO,
                                           : fa::launch_bwd_dq_f32(a, d, causal != 0, s));
 }
 
+int fa_forward_ext(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                   int H_kv, int n_q, int n_k, int d, float scale, int causal, int q_offset,
+                   int window, int dtype, void* stream) {
+  return forward_impl(q, k, v, o, lse, B, H, H_kv, n_q, n_k, d, scale, causal, dtype, stream,
+                      q_offset, window);
+}
+
 int fa_backward(const void* q, const void* k, const void* v, const void* o, const void* dO,
                 const float* lse, void* dq, void* dk, void* dv, void* workspace,
                 size_t workspace_bytes, int B, int H, int n_q, int n_k, int d, float scale,
@@ -230,6 +255,14 @@ int fa_backward_gqa(const void* q, const void* k, const void* v, const void* o, 
                     float scale, int causal, int dtype, void* stream) {
   return backward_impl(q, k, v, o, dO, lse, dq, dk, dv, workspace, workspace_bytes, B, H, H_kv,
                        n_q, n_k, d, scale, causal, dtype, stream);
+}
+
+int fa_backward_ext(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                    const float* lse, void* dq, void* dk, void* dv, void* workspace,
+                    size_t workspace_bytes, int B, int H, int H_kv, int n_q, int n_k, int d,
+                    float scale, int causal, int q_offset, int window, int dtype, void* stream) {
+  return backward_impl(q, k, v, o, dO, lse, dq, dk, dv, workspace, workspace_bytes, B, H, H_kv,
+                       n_q, n_k, d, scale, causal, dtype, stream, q_offset, window);
 }
 
 }  // extern "C"

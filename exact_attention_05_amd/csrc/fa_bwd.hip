@@ -152,9 +152,12 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16_kernel(BwdArgs a, int n_kti
                       : bf16x8{};
   }
 
-  // Query stages that can see any key of this workgroup.
-  const int qb_first = CAUSAL ? (k0 / C::kBQ) : 0;
-  const int nblocks = (CAUSAL && k0 >= n_q) ? 0 : (n_q + C::kBQ - 1) / C::kBQ - qb_first;
+  // Query stages holding rows that see some key of this workgroup.
+  const Band band = band_of(a, CAUSAL);
+  const int k1 = min(n_k, k0 + C::kBK);
+  const int q_first = band.q_lo(k0), q_last = band.q_hi(k1);
+  const int qb_first = q_first / C::kBQ;
+  const int nblocks = q_last > q_first ? (q_last + C::kBQ - 1) / C::kBQ - qb_first : 0;
 
   TileDma<D, C::kBQ, C::kWaves> dma;
   dma.init(wave, lane);
@@ -206,7 +209,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16_kernel(BwdArgs a, int n_kti
     float p = fast_exp2(fmaf(s[i], sl2, -lv[g4][e]));
     if constexpr (decltype(mask_tag)::value) {
       const int q = qrow0 + 8 * g4 + 4 * hi + e;
-      if (q >= n_q || key >= n_k || (CAUSAL && key > q)) p = 0.f;
+      if (q >= n_q || band.hidden(q, key)) p = 0.f;
     }
     ex[i] = p;
     dd[i] = dp[i] - dl[g4][e];
@@ -311,17 +314,15 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16_kernel(BwdArgs a, int n_kti
     iteration(mask_tag, IB{}, R32{}, IB{}, R0{}, qrow0 + 32);
   };
 
-  // Stages needing the mask: the causal diagonal (query stages starting
-  // before the workgroup's last key), a ragged last stage, or every stage
-  // when the workgroup's keys run past n_k.
-  int b_lo = 0, b_hi = nblocks;
-  if (CAUSAL) {
-    const int first_clear = k0 + C::kBK - 1;  // first query row that sees every key here
-    b_lo = min(nblocks, max(0, (first_clear - qb_first * C::kBQ + C::kBQ - 1) / C::kBQ));
+  // Stages [b_lo, b_hi) need no mask: every row sees every key of the
+  // workgroup (none when its keys run past n_k).  The others -- causal
+  // diagonal, window edges, a ragged last stage -- are masked.
+  int b_lo = nblocks, b_hi = nblocks;
+  if (k0 + C::kBK <= n_k) {
+    const int full_lo = band.q_full_lo(k0 + C::kBK), full_hi = min(n_q, band.q_full_hi(k0));
+    b_lo = min(nblocks, max(0, (full_lo - qb_first * C::kBQ + C::kBQ - 1) / C::kBQ));
+    b_hi = max(b_lo, min(nblocks, (full_hi - qb_first * C::kBQ) / C::kBQ));
   }
-  if (n_q % C::kBQ != 0) b_hi = nblocks - 1;
-  if (k0 + C::kBK > n_k) b_lo = b_hi = nblocks;
-  b_hi = max(b_hi, b_lo);
 
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
@@ -499,9 +500,14 @@ __global__ __launch_bounds__(512) void bwd_dq_bf16_kernel(BwdArgs a, int n_qtile
   const float lse2 = (qi < n_q) ? a.lse2[(size_t)bh * n_q + qi] : 0.f;
   const float dlt = (qi < n_q) ? a.delta[(size_t)bh * n_q + qi] : 0.f;
 
+  // Key blocks [t_lo, t_hi) hold keys some row of the workgroup sees;
+  // blocks [f_lo, f_hi) need no mask for any row.
+  const Band band = band_of(a, CAUSAL);
   const int q_end = min(n_q, q0 + C::kBM);
-  const int k_end = CAUSAL ? min(n_k, q_end) : n_k;
-  const int ntiles = (k_end + C::kBN - 1) / C::kBN;
+  const int t_lo = band.key_lo(q0) / C::kBN;
+  const int t_hi = max(t_lo, (band.key_hi(q_end) + C::kBN - 1) / C::kBN);
+  const int f_lo = min(t_hi, max(t_lo, (band.key_full_lo(q_end) + C::kBN - 1) / C::kBN));
+  const int f_hi = max(f_lo, min(t_hi, band.key_full_hi(q0) / C::kBN));
 
   TileDma<D, C::kBN, C::kWaves> dma;
   dma.init(wave, lane);
@@ -523,13 +529,14 @@ __global__ __launch_bounds__(512) void bwd_dq_bf16_kernel(BwdArgs a, int n_qtile
     const int buf = BUFC >= 0 ? BUFC : (t & 1);
     wait_lds_dma();
     __syncthreads();
-    if (t + 1 < ntiles) load_tile(t + 1, buf ^ 1);
+    if (t + 1 < t_hi) load_tile(t + 1, buf ^ 1);
     const char* ks = sk[buf];
     const char* vs = sv[buf];
     const int k0 = t * C::kBN;
 #pragma unroll
     for (int kb = 0; kb < C::kKB; ++kb) {
-      if (MASK && CAUSAL && k0 + kb * 32 > qw + 31) continue;  // every key hidden from this wave
+      // every key of the sub-block hidden from this wave
+      if (MASK && (k0 + kb * 32 >= band.key_hi(qw + 32) || k0 + kb * 32 + 32 <= band.key_lo(qw))) continue;
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
       for (int c = 0; c < C::kDC; ++c) {
@@ -543,8 +550,8 @@ __global__ __launch_bounds__(512) void bwd_dq_bf16_kernel(BwdArgs a, int n_qtile
         float p1 = fast_exp2(fmaf(s[i + 1], sl2, -lse2));
         if constexpr (MASK) {
           const int kj = k0 + kb * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
-          if (kj >= n_k || (CAUSAL && kj > qi)) p0 = 0.f;
-          if (kj + 1 >= n_k || (CAUSAL && kj + 1 > qi)) p1 = 0.f;
+          if (band.hidden(qi, kj)) p0 = 0.f;
+          if (band.hidden(qi, kj + 1)) p1 = 0.f;
         }
         dsb[i >> 3][(i & 7) >> 1] = pack_bf16x2(p0 * (dp[i] - dlt), p1 * (dp[i + 1] - dlt));
       }
@@ -557,15 +564,21 @@ __global__ __launch_bounds__(512) void bwd_dq_bf16_kernel(BwdArgs a, int n_qtile
     }
   };
 
-  const int n_full = min(ntiles, (CAUSAL ? min(q0 + 1, n_k) : n_k) / C::kBN);
-  load_tile(0, 0);
-  int t = 0;
-  for (; t + 1 < n_full; t += 2) {
+  // Unmasked blocks two at a time with fixed buffers (block t in buffer
+  // t % 2), the others masked.
+  if (t_lo < t_hi) load_tile(t_lo, t_lo & 1);
+  int t = t_lo;
+  for (; t < f_lo; ++t) block(T{}, Buf<-1>{}, t);
+  if (t < f_hi && (t & 1)) {
+    block(F{}, Buf<-1>{}, t);
+    ++t;
+  }
+  for (; t + 1 < f_hi; t += 2) {
     block(F{}, Buf<0>{}, t);
     block(F{}, Buf<1>{}, t + 1);
   }
-  for (; t < n_full; ++t) block(F{}, Buf<0>{}, t);
-  for (; t < ntiles; ++t) block(T{}, Buf<-1>{}, t);
+  for (; t < f_hi; ++t) block(F{}, Buf<-1>{}, t);
+  for (; t < t_hi; ++t) block(T{}, Buf<-1>{}, t);
 
   if (qi < n_q) {
     __bf16* dqp = static_cast<__bf16*>(a.dq) + ((size_t)bh * n_q + qi) * D;
@@ -641,9 +654,12 @@ __global__ __launch_bounds__(256) void bwd_dkdv_f32_kernel(BwdArgs a, int n_ktil
     vreg[c] = (key < n_k) ? vp[(size_t)key * D + 2 * c + hi] : 0.f;
   }
 
-  const int qb_first = CAUSAL ? (k0 / C::kBS) : 0;
-  const int qb_end = (n_q + C::kBS - 1) / C::kBS;
-  const int nblocks = (CAUSAL && k0 >= n_q) ? 0 : max(0, qb_end - qb_first);
+  const Band band = band_of(a, CAUSAL);
+  const int k1 = min(n_k, k0 + C::kBlk);
+  const int q_first = band.q_lo(k0), q_last = band.q_hi(k1);
+  const int qb_first = q_first / C::kBS;
+  const int nblocks = q_last > q_first ? (q_last + C::kBS - 1) / C::kBS - qb_first : 0;
+  const int wq_lo = band.q_lo(kw), wq_hi = band.q_hi(min(n_k, kw + 32));  // rows seeing this wave's keys
 
   f32x4 qst[C::kLoads], dost[C::kLoads];
   float lse_st = 0.f, del_st = 0.f;
@@ -704,7 +720,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_f32_kernel(BwdArgs a, int n_ktil
     const int buf = b & 1;
     if (b + 1 < nblocks) gload(b + 1);
     const int qbase = (qb_first + b) * C::kBS;
-    if (!(CAUSAL && qbase + 31 < kw)) {
+    if (kw < n_k && qbase < wq_hi && qbase + C::kBS > wq_lo) {
       // S = Q K^T and dP = dO V^T: A = Q/dO rows (query l%32, d = 2c + hi),
       // B = K/V rows (key l%32, d = 2c + hi).
       f32x16 s = f32x16{}, dp = f32x16{};
@@ -719,7 +735,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_f32_kernel(BwdArgs a, int n_ktil
         const int r = 8 * (i >> 2) + 4 * hi + (i & 3);
         const int qi = qbase + r;
         float pv = fast_exp2(fmaf(s[i], a.scale_log2, -slse[buf][r]));
-        const bool hide = qi >= n_q || key >= n_k || (CAUSAL && key > qi);
+        const bool hide = qi >= n_q || band.hidden(qi, key);
         pv = hide ? 0.f : pv;
         p[i] = pv;
         ds[i] = pv * (dp[i] - sdel[buf][r]);
@@ -734,6 +750,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_f32_kernel(BwdArgs a, int n_ktil
           dk[db] = mfma_f32(sq[buf][r * C::kStride + 32 * db + l32], ds[i], dk[db]);
         }
       }
+      settle_acc(dv, dk);
     }
     if (b + 1 < nblocks) swrite(buf ^ 1);
     __syncthreads();
@@ -796,9 +813,11 @@ __global__ __launch_bounds__(256) void bwd_dq_f32_kernel(BwdArgs a, int n_qtiles
   const float lse2 = (qi < n_q) ? a.lse2[(size_t)bh * n_q + qi] : 0.f;
   const float dlt = (qi < n_q) ? a.delta[(size_t)bh * n_q + qi] : 0.f;
 
+  const Band band = band_of(a, CAUSAL);
   const int q_end = min(n_q, q0 + C::kBlk);
-  const int k_end = CAUSAL ? min(n_k, q_end) : n_k;
-  const int ntiles = (k_end + C::kBS - 1) / C::kBS;
+  const int t_lo = band.key_lo(q0) / C::kBS;
+  const int t_hi = max(t_lo, (band.key_hi(q_end) + C::kBS - 1) / C::kBS);
+  const int wk_lo = band.key_lo(qw), wk_hi = band.key_hi(qw + 32);  // keys this wave sees
 
   f32x4 kst[C::kLoads], vst[C::kLoads];
   auto gload = [&](int t) {
@@ -832,15 +851,17 @@ __global__ __launch_bounds__(256) void bwd_dq_f32_kernel(BwdArgs a, int n_qtiles
 #pragma unroll
   for (int db = 0; db < C::kDB; ++db) dq[db] = f32x16{};
 
-  gload(0);
-  swrite(0);
+  if (t_lo < t_hi) {
+    gload(t_lo);
+    swrite(t_lo & 1);
+  }
   __syncthreads();
 
-  for (int t = 0; t < ntiles; ++t) {
+  for (int t = t_lo; t < t_hi; ++t) {
     const int buf = t & 1;
-    if (t + 1 < ntiles) gload(t + 1);
+    if (t + 1 < t_hi) gload(t + 1);
     const int k0 = t * C::kBS;
-    if (!(CAUSAL && k0 > qw + 31)) {
+    if (k0 < wk_hi && k0 + C::kBS > wk_lo) {
       // S^T = K Q^T, dP^T = V dO^T (one query per lane).
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
@@ -853,7 +874,7 @@ __global__ __launch_bounds__(256) void bwd_dq_f32_kernel(BwdArgs a, int n_qtiles
       for (int i = 0; i < 16; ++i) {
         const int kj = k0 + 8 * (i >> 2) + 4 * hi + (i & 3);
         float pv = fast_exp2(fmaf(s[i], a.scale_log2, -lse2));
-        const bool hide = qi >= n_q || kj >= n_k || (CAUSAL && kj > qi);
+        const bool hide = qi >= n_q || band.hidden(qi, kj);
         pv = hide ? 0.f : pv;
         ds[i] = pv * (dp[i] - dlt);
       }
@@ -865,8 +886,9 @@ __global__ __launch_bounds__(256) void bwd_dq_f32_kernel(BwdArgs a, int n_qtiles
         for (int db = 0; db < C::kDB; ++db)
           dq[db] = mfma_f32(sk[buf][r * C::kStride + 32 * db + l32], ds[i], dq[db]);
       }
+      settle_acc(dq);
     }
-    if (t + 1 < ntiles) swrite(buf ^ 1);
+    if (t + 1 < t_hi) swrite(buf ^ 1);
     __syncthreads();
   }
 

@@ -98,6 +98,43 @@ __device__ __forceinline__ void phase_barrier() {
 __device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
 __device__ __forceinline__ void pin(uint32_t& x) { asm volatile("" : "+v"(x)); }
 
+// Accumulators of fp32 matrix products (AGPR form) made safe to read after
+// the loop that built them.  On a loop-exit path the compiler's wait-state
+// count for "matrix product writes a register, vector instruction reads it"
+// has been seen to fall short (the epilogue read the last accumulator
+// register 7 wait states after the final 16-pass product, and got the value
+// from before it).  Here 32 wait states pass inside a statement that takes
+// every accumulator in its AGPRs, so any later read (the copy to VGPRs
+// included) depends on the wait.
+// Every accumulator is an operand of the one statement that holds the
+// wait, so no product that writes one can be scheduled after the wait.
+template <int N>
+__device__ __forceinline__ void settle_acc(f32x16 (&acc)[N]) {
+  static_assert(N == 1 || N == 2 || N == 4, "one, two or four accumulators");
+  if constexpr (N == 1) {
+    asm volatile("s_nop 15\n\ts_nop 15" : "+a"(acc[0]));
+  } else if constexpr (N == 2) {
+    asm volatile("s_nop 15\n\ts_nop 15" : "+a"(acc[0]), "+a"(acc[1]));
+  } else {
+    asm volatile("s_nop 15\n\ts_nop 15"
+                 : "+a"(acc[0]), "+a"(acc[1]), "+a"(acc[2]), "+a"(acc[3]));
+  }
+}
+// Same for two accumulator sets built in the same loop.
+template <int N>
+__device__ __forceinline__ void settle_acc(f32x16 (&x)[N], f32x16 (&y)[N]) {
+  static_assert(N == 1 || N == 2 || N == 4, "one, two or four accumulators");
+  if constexpr (N == 1) {
+    asm volatile("s_nop 15\n\ts_nop 15" : "+a"(x[0]), "+a"(y[0]));
+  } else if constexpr (N == 2) {
+    asm volatile("s_nop 15\n\ts_nop 15" : "+a"(x[0]), "+a"(x[1]), "+a"(y[0]), "+a"(y[1]));
+  } else {
+    asm volatile("s_nop 15\n\ts_nop 15"
+                 : "+a"(x[0]), "+a"(x[1]), "+a"(x[2]), "+a"(x[3]),
+                   "+a"(y[0]), "+a"(y[1]), "+a"(y[2]), "+a"(y[3]));
+  }
+}
+
 // Calls f(std::integral_constant<int, I>{}) for I = BEGIN .. END-1, so that
 // the index is a compile-time constant in the body.
 template <int BEGIN, int END, typename F>

@@ -97,9 +97,14 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdArgs a, int n_qtiles) 
       qf[c] = bf16x8{};
   }
 
+  // Key blocks [t_lo, t_hi) hold keys some row of the workgroup sees;
+  // blocks [f_lo, f_hi) inside them need no mask for any row.
+  const Band band = band_of(a, CAUSAL);
   const int q_end = min(n_q, q0 + C::kBM);
-  const int k_end = CAUSAL ? min(n_k, q_end) : n_k;
-  const int ntiles = (k_end + C::kBN - 1) / C::kBN;
+  const int t_lo = band.key_lo(q0) / C::kBN;
+  const int t_hi = max(t_lo, (band.key_hi(q_end) + C::kBN - 1) / C::kBN);
+  const int f_lo = min(t_hi, max(t_lo, (band.key_full_lo(q_end) + C::kBN - 1) / C::kBN));
+  const int f_hi = max(f_lo, min(t_hi, band.key_full_hi(q0) / C::kBN));
 
   TileDma<D, C::kBN, C::kWaves> dma;
   dma.init(wave, lane);
@@ -129,7 +134,7 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdArgs a, int n_qtiles) 
     // after the barrier nobody reads buffer buf ^ 1 any more.
     wait_lds_dma();
     __syncthreads();
-    if (t + 1 < ntiles) load_tile(t + 1, buf ^ 1);
+    if (t + 1 < t_hi) load_tile(t + 1, buf ^ 1);
     const char* ks = sk[buf];
     const char* vs = sv[buf];
     const int k0 = t * C::kBN;
@@ -160,7 +165,7 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdArgs a, int n_qtiles) 
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = k0 + kb * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
-          if (key >= n_k || (CAUSAL && key > qi)) s[kb][i] = -INFINITY;
+          if (band.hidden(qi, key)) s[kb][i] = -INFINITY;
         }
     }
     // Row maximum of the block (raw scores), then the lazy reference update.
@@ -220,23 +225,30 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdArgs a, int n_qtiles) 
     __builtin_amdgcn_s_setprio(0);
   };
 
-  // Leading blocks that need no mask for any row of the workgroup, two at a
-  // time with fixed buffers; the rest (key tail, causal diagonal) masked.
-  const int n_full = min(ntiles, (CAUSAL ? min(q0 + 1, n_k) : n_k) / C::kBN);
+  // Blocks that need no mask for any row of the workgroup go two at a time
+  // with fixed buffers (block t in buffer t % 2); the others (window edges,
+  // key tail, causal diagonal) masked.
   using F = std::false_type;
   using T = std::true_type;
-  load_tile(0, 0);
-  int t = 0;
-  for (; t + 1 < n_full; t += 2) {
+  using BR = std::integral_constant<int, -1>;
+  if (t_lo < t_hi) load_tile(t_lo, t_lo & 1);
+  int t = t_lo;
+  for (; t < f_lo; ++t) block(T{}, BR{}, t);
+  if (t < f_hi && (t & 1)) {
+    block(F{}, BR{}, t);
+    ++t;
+  }
+  for (; t + 1 < f_hi; t += 2) {
     block(F{}, std::integral_constant<int, 0>{}, t);
     block(F{}, std::integral_constant<int, 1>{}, t + 1);
   }
-  for (; t < n_full; ++t) block(F{}, std::integral_constant<int, -1>{}, t);
-  for (; t < ntiles; ++t) block(T{}, std::integral_constant<int, -1>{}, t);
+  for (; t < f_hi; ++t) block(F{}, BR{}, t);
+  for (; t < t_hi; ++t) block(T{}, BR{}, t);
 
-  // Epilogue: normalise, store O (bf16) and LSE (natural log).
+  // Epilogue: normalise, store O (bf16) and LSE (natural log).  A row that
+  // sees no key at all gets O = 0 and LSE = -inf.
   const float lt = l + swap_halves(l);
-  const float inv = 1.f / lt;
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
   if (qi < n_q) {
     __bf16* op = static_cast<__bf16*>(a.o) + ((size_t)bh * n_q + qi) * D;
 #pragma unroll
@@ -336,9 +348,12 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdArgs a, int n_qtiles) {
 #pragma unroll
   for (int c = 0; c < D / 2; ++c) qf[c] = (qi < n_q) ? qp[(size_t)qi * D + 2 * c + hi] : 0.f;
 
+  const Band band = band_of(a, CAUSAL);
   const int q_end = min(n_q, q0 + C::kBM);
-  const int k_end = CAUSAL ? min(n_k, q_end) : n_k;
-  const int ntiles = (k_end + C::kBN - 1) / C::kBN;
+  const int t_lo = band.key_lo(q0) / C::kBN;
+  const int t_hi = max(t_lo, (band.key_hi(q_end) + C::kBN - 1) / C::kBN);
+  // Keys every row of this wave sees.
+  const int wfull_lo = band.key_full_lo(qw + 32), wfull_hi = band.key_full_hi(qw);
 
   // The 16-byte row chunks are stored unaligned into the padded K rows
   // (pitch D + 2), so K goes through LDS as float2 pairs.
@@ -376,13 +391,15 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdArgs a, int n_qtiles) {
   for (int db = 0; db < C::kDB; ++db) oacc[db] = f32x16{};
   float m = -INFINITY, l = 0.f;
 
-  gload(0);
-  swrite(0);
+  if (t_lo < t_hi) {
+    gload(t_lo);
+    swrite(t_lo & 1);
+  }
   __syncthreads();
 
-  for (int t = 0; t < ntiles; ++t) {
+  for (int t = t_lo; t < t_hi; ++t) {
     const int buf = t & 1;
-    if (t + 1 < ntiles) gload(t + 1);
+    if (t + 1 < t_hi) gload(t + 1);
     const int k0 = t * C::kBN;
 
     f32x16 s[1];
@@ -391,14 +408,14 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdArgs a, int n_qtiles) {
     for (int c = 0; c < D / 2; ++c)
       s[0] = mfma_f32(sk[buf][l32 * C::kKStride + 2 * c + hi], qf[c], s[0]);
 
-    const bool need_mask = (k0 + C::kBN > n_k) || (CAUSAL && k0 + C::kBN - 1 > qw);
+    const bool need_mask = k0 < wfull_lo || k0 + C::kBN > wfull_hi;
     float alpha;
     if (need_mask) {
       uint32_t bits = 0;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int key = k0 + 8 * (i >> 2) + 4 * hi + (i & 3);
-        const bool h = key >= n_k || (CAUSAL && key > qi);
+        const bool h = band.hidden(qi, key);
         bits |= (h ? 1u : 0u) << i;
       }
       alpha = softmax_block<1, true>(s, m, l, a.scale_log2, &bits);
@@ -417,13 +434,14 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdArgs a, int n_qtiles) {
       for (int db = 0; db < C::kDB; ++db)
         oacc[db] = mfma_f32(sv[buf][key * C::kVStride + 32 * db + l32], s[0][i], oacc[db]);
     }
+    settle_acc(oacc);
 
-    if (t + 1 < ntiles) swrite(buf ^ 1);
+    if (t + 1 < t_hi) swrite(buf ^ 1);
     __syncthreads();
   }
 
   const float lt = l + swap_halves(l);
-  const float inv = 1.f / lt;
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
   if (qi < n_q) {
     float* op = static_cast<float*>(a.o) + ((size_t)bh * n_q + qi) * D;
 #pragma unroll

@@ -19,6 +19,8 @@ struct FwdArgs {
   int group;        // query heads per K/V head (H / H_kv); 1 without sharing
   int n_q;
   int n_k;
+  int q_offset;     // absolute position of query row 0 against key 0 (see Band)
+  int window;       // sliding-window half-width, or -1 for none (see Band)
   float scale;      // softmax scale on q . k
   float scale_log2; // scale * log2(e): scores are exponentiated base 2
 };
@@ -41,6 +43,8 @@ struct BwdArgs {
   int group;        // query heads per K/V head (H / H_kv)
   int n_q;
   int n_k;
+  int q_offset;
+  int window;
   float scale;
   float scale_log2;
 };
@@ -51,6 +55,71 @@ struct BwdArgs {
 __host__ __device__ inline int kv_head_index(int bh, int H, int group) {
   if (group == 1) return bh;
   return (bh / H) * (H / group) + (bh % H) / group;
+}
+
+// Which keys a query row sees.  Query row i sits at absolute position
+// p = i + q_offset on the key axis (q_offset = 0: the top-left alignment of
+// the causal mask, "Attention Mechanism", section 4.4); key j is hidden when
+// j >= n_k, when causal and j > p, or, with a sliding window of half-width
+// w >= 0, when |p - j| > w (same page, section 4.5 "Sparse Attention", the
+// window of the +-w neighbours).  The helpers give half-open index ranges.
+struct Band {
+  int n_q, n_k, q_offset, window;
+  bool causal;
+
+  __host__ __device__ bool hidden(int q, int key) const {
+    const int p = q + q_offset;
+    return key >= n_k || (causal && key > p) || (window >= 0 && (key < p - window || key > p + window));
+  }
+  // Keys seen by some row of [r0, r1) (r0 < r1).
+  __host__ __device__ int key_lo(int r0) const {
+    return window < 0 ? 0 : max(0, r0 + q_offset - window);
+  }
+  __host__ __device__ int key_hi(int r1) const {
+    int h = n_k;
+    if (causal) h = min(h, r1 + q_offset);
+    if (window >= 0) h = min(h, r1 + q_offset + window);
+    return max(h, 0);
+  }
+  // Keys seen by every row of [r0, r1) (possibly an empty range).
+  __host__ __device__ int key_full_lo(int r1) const {
+    return window < 0 ? 0 : max(0, r1 - 1 + q_offset - window);
+  }
+  __host__ __device__ int key_full_hi(int r0) const {
+    int h = n_k;
+    if (causal) h = min(h, r0 + q_offset + 1);
+    if (window >= 0) h = min(h, r0 + q_offset + window + 1);
+    return max(h, 0);
+  }
+  // Query rows that see some key of [k0, k1) (k0 < k1 <= n_k).
+  __host__ __device__ int q_lo(int k0) const {
+    int l = 0;
+    if (causal) l = max(l, k0 - q_offset);
+    if (window >= 0) l = max(l, k0 - q_offset - window);
+    return min(l, n_q);
+  }
+  __host__ __device__ int q_hi(int k1) const {
+    int h = n_q;
+    if (window >= 0) h = min(h, k1 - 1 - q_offset + window + 1);
+    return max(h, 0);
+  }
+  // Query rows that see every key of [k0, k1) (possibly an empty range).
+  __host__ __device__ int q_full_lo(int k1) const {
+    int l = 0;
+    if (causal) l = max(l, k1 - 1 - q_offset);
+    if (window >= 0) l = max(l, k1 - 1 - q_offset - window);
+    return min(l, n_q);
+  }
+  __host__ __device__ int q_full_hi(int k0) const {
+    int h = n_q;
+    if (window >= 0) h = min(h, k0 - q_offset + window + 1);
+    return max(h, 0);
+  }
+};
+
+template <typename Args>
+__host__ __device__ inline Band band_of(const Args& a, bool causal) {
+  return Band{a.n_q, a.n_k, a.q_offset, a.window, causal};
 }
 
 // Each launcher enqueues its kernel(s) on `stream` and returns the HIP status

@@ -149,6 +149,28 @@ int fa_backward_gqa(const void* q, const void* k, const void* v, const void* o,
                     int B, int H, int H_kv, int n_q, int n_k, int d, float scale,
                     int causal, int dtype, void* stream);
 
+/* Extended forward pass: shared K/V heads as fa_forward_gqa, plus where each
+ * query row sits on the key axis and a sliding window.  Query row i is at
+ * absolute position p = i + q_offset; key j is hidden when causal and j > p
+ * ("Attention Mechanism", section 4.4, with the rows shifted by q_offset:
+ * q_offset = n_k - n_q aligns the last query with the last key, as when new
+ * queries attend to a longer cache) and, when window >= 0, when
+ * |p - j| > window (section 4.5 "Sparse Attention": only the +-w
+ * neighbours).  q_offset = 0, window = -1 is fa_forward_gqa.  A row that sees
+ * no key gets o = 0 and lse = -inf.  |q_offset| <= 2^29,
+ * -1 <= window <= 2^29 and, when either is in use, n_q, n_k <= 2^29;
+ * otherwise FA_ERR_INVALID_ARG. */
+int fa_forward_ext(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int H, int H_kv, int n_q, int n_k, int d, float scale,
+                   int causal, int q_offset, int window, int dtype, void* stream);
+
+/* Backward pass of fa_forward_ext (same q_offset and window). */
+int fa_backward_ext(const void* q, const void* k, const void* v, const void* o,
+                    const void* dO, const float* lse, void* dq, void* dk, void* dv,
+                    void* workspace, size_t workspace_bytes,
+                    int B, int H, int H_kv, int n_q, int n_k, int d, float scale,
+                    int causal, int q_offset, int window, int dtype, void* stream);
+
 /* Static text for a status code ("unknown status" for other values). */
 const char* fa_status_string(int status);
 

@@ -66,6 +66,9 @@ __all__ = [
     "expand_kv_heads",
     "attention_fwd_gqa",
     "attention_bwd_gqa",
+    "band_visible",
+    "attention_fwd_band",
+    "attention_bwd_band",
 ]
 
 
@@ -387,4 +390,87 @@ def attention_bwd_gqa(q, k, v, do, scale: float, causal: bool = False):
         return x.reshape(x.shape[:-3] + (h_kv, g) + x.shape[-2:]).sum(axis=-3)
 
     return dq, fold(dk), fold(dv)
+
+
+# ------------------------------------------- query offset and sliding window
+
+
+def band_visible(n_q: int, n_k: int, causal: bool, q_offset: int = 0, window: int = -1) -> np.ndarray:
+    """Boolean (n_q, n_k): True where key j is visible to query row i.
+
+    Row i sits at absolute position p = i + q_offset on the key axis.  The
+    causal mask ("Attention Mechanism", section 4.4) hides j > p -- with
+    q_offset = 0 this is causal_visible's top-left alignment, and
+    q_offset = n_k - n_q puts the last query on the last key.  A sliding
+    window of half-width w >= 0 (same page, section 4.5 "Sparse Attention":
+    each query sees only its +-w neighbours) hides |p - j| > w; w < 0 means no
+    window.
+    """
+    p = np.arange(n_q)[:, None] + int(q_offset)
+    j = np.arange(n_k)[None, :]
+    vis = np.ones((n_q, n_k), dtype=bool)
+    if causal:
+        vis &= j <= p
+    if window >= 0:
+        vis &= np.abs(p - j) <= window
+    return vis
+
+
+def _band_probs(q, k, scale, causal, q_offset, window):
+    """P (rows summing to one, or all zero for a row that sees no key) and
+    LSE (-inf for such a row) under band_visible."""
+    q = _f64(q)
+    k = _f64(k)
+    vis = band_visible(q.shape[-2], k.shape[-2], causal, q_offset, window)
+    s = float(scale) * np.matmul(q, np.swapaxes(k, -1, -2))
+    s = np.where(vis, s, -np.inf)
+    m = np.max(s, axis=-1, keepdims=True)
+    empty = ~np.isfinite(m)
+    m = np.where(empty, 0.0, m)
+    e = np.where(vis, np.exp(s - m), 0.0)
+    l = np.sum(e, axis=-1, keepdims=True)
+    p = np.where(empty, 0.0, e / np.where(empty, 1.0, l))
+    with np.errstate(divide="ignore"):
+        lse = np.where(empty, -np.inf, m + np.log(np.where(empty, 1.0, l)))[..., 0]
+    return p, lse
+
+
+def attention_fwd_band(q, k, v, scale: float, causal: bool = False, q_offset: int = 0,
+                       window: int = -1):
+    """Forward pass under band_visible, with K/V heads shared when k has fewer
+    heads than q (as attention_fwd_gqa).  A row that sees no key has O = 0 and
+    LSE = -inf."""
+    h = np.shape(q)[-3] if np.ndim(q) >= 3 else None
+    if h is not None and np.shape(k)[-3] != h:
+        k, v = expand_kv_heads(k, h), expand_kv_heads(v, h)
+    p, lse = _band_probs(q, k, scale, causal, q_offset, window)
+    return np.matmul(p, _f64(v)), lse
+
+
+def attention_bwd_band(q, k, v, do, scale: float, causal: bool = False, q_offset: int = 0,
+                       window: int = -1):
+    """Explicit backward pass of attention_fwd_band (the chain rule of
+    attention_bwd on the banded P; a row that sees no key contributes
+    nothing); dK, dV are summed over the query heads sharing a K/V head."""
+    q, do = _f64(q), _f64(do)
+    h = q.shape[-3] if q.ndim >= 3 else None
+    h_kv = np.shape(k)[-3] if h is not None else None
+    if h is not None and h_kv != h:
+        k, v = expand_kv_heads(k, h), expand_kv_heads(v, h)
+    k, v = _f64(k), _f64(v)
+    p, _ = _band_probs(q, k, scale, causal, q_offset, window)
+    o = np.matmul(p, v)
+    dv = np.matmul(np.swapaxes(p, -1, -2), do)
+    dp = np.matmul(do, np.swapaxes(v, -1, -2))
+    ds = p * (dp - np.sum(do * o, axis=-1, keepdims=True))
+    dq = float(scale) * np.matmul(ds, k)
+    dk = float(scale) * np.matmul(np.swapaxes(ds, -1, -2), q)
+    if h is not None and h_kv != h:
+        g = h // h_kv
+
+        def fold(x):
+            return x.reshape(x.shape[:-3] + (h_kv, g) + x.shape[-2:]).sum(axis=-3)
+
+        dk, dv = fold(dk), fold(dv)
+    return dq, dk, dv
 

@@ -152,3 +152,14 @@ def test_gqa_validates_like_forward():
     assert L.fa_backward_gqa(P, P, P, P, P, P, P2, P2, P2, None, 1 << 20, 1, 8, 2, 8, 8, 64, 0.125,
                              0, 1, None) == fa.FA_ERR_WORKSPACE
 
+
+@pytest.mark.parametrize("n,q_offset,window", [(8, (1 << 29) + 1, -1), (8, -(1 << 29) - 1, -1),
+                                                (8, 0, -2), (8, 0, (1 << 29) + 1),
+                                                ((1 << 29) + 1, 0, 5), ((1 << 29) + 1, 3, -1)])
+def test_ext_rejects_out_of_range_band(n, q_offset, window):
+    L = fa.lib()
+    assert L.fa_forward_ext(P, P, P, P2, P2, 1, 2, 2, n, 8, 64, 0.125, 1, q_offset, window, 1,
+                            None) == fa.FA_ERR_INVALID_ARG
+    assert L.fa_backward_ext(P, P, P, P, P, P, P2, P2, P2, P2, 1 << 20, 1, 2, 2, 8, n, 64, 0.125, 1,
+                             q_offset, window, 1, None) == fa.FA_ERR_INVALID_ARG
+

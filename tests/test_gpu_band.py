@@ -1,0 +1,122 @@
+"""GPU parity of the query offset and the sliding window (fa_forward_ext /
+fa_backward_ext) against the fp64 oracle."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import exact_attention_05_amd as fa
+import oracle
+import workloads
+from parity import RTOL_BF16_TERMS, TOL_LSE, assert_close, np64, require_gpu, tol_for
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return require_gpu()
+
+
+def draw(seed, B, H, h_kv, n_q, n_k, d, dtype):
+    q, _, _, do = workloads.random_qkv(seed, B, H, n_q, n_k, d, dtype, with_do=True)
+    _, k, v = workloads.random_qkv(seed + 1, B, h_kv, n_q, n_k, d, dtype)
+    return q, k, v, do
+
+
+def run(dev, q, k, v, do, scale, causal, off, w):
+    qd, kd, vd, dod = (t.to(dev) for t in (q, k, v, do))
+    o, lse = fa.forward(qd, kd, vd, causal=causal, scale=scale, q_offset=off, window=w)
+    dq, dk, dv = fa.backward(qd, kd, vd, o, dod, lse, causal=causal, scale=scale, q_offset=off, window=w)
+    torch.cuda.synchronize()
+    return o.cpu(), lse.cpu(), dq.cpu(), dk.cpu(), dv.cpu()
+
+
+def check(tag, got, q, k, v, do, scale, causal, off, w, dtype):
+    o, lse, dq, dk, dv = got
+    q64, k64, v64, do64 = np64(q), np64(k), np64(v), np64(do)
+    ro, rl = oracle.attention_fwd_band(q64, k64, v64, scale, causal, off, w)
+    assert_close(f"O {tag}", o, ro, tol_for(dtype))
+    fin = np.isfinite(rl)
+    assert np.array_equal(np.isfinite(np64(lse)), fin), f"LSE {tag}: rows without keys differ"
+    assert_close(f"LSE {tag}", np64(lse)[fin], rl[fin], TOL_LSE)
+    rq, rk, rv = oracle.attention_bwd_band(q64, k64, v64, do64, scale, causal, off, w)
+    if dtype == torch.bfloat16:
+        # the sums of absolute terms, as for ordinary heads (see parity.py):
+        # dQ: scale |dS| |K|, dK: scale |dS|^T |Q|, dV: |P|^T |dO|, with P and
+        # dS of the banded oracle (K/V heads repeated, then folded).
+        H, h_kv = q64.shape[1], k64.shape[1]
+        ke, ve = oracle.expand_kv_heads(k64, H), oracle.expand_kv_heads(v64, H)
+        vis = oracle.band_visible(q64.shape[2], k64.shape[2], causal, off, w)
+        s = np.where(vis, scale * q64 @ np.swapaxes(ke, -1, -2), -np.inf)
+        m = np.max(s, -1, keepdims=True)
+        m = np.where(np.isfinite(m), m, 0.0)
+        e = np.where(vis, np.exp(s - m), 0.0)
+        z = e.sum(-1, keepdims=True)
+        p = e / np.where(z > 0, z, 1.0)
+        ds = p * (do64 @ np.swapaxes(ve, -1, -2) - np.sum(do64 * (p @ ve), -1, keepdims=True))
+        t = lambda x: np.swapaxes(x, -1, -2)  # noqa: E731
+        g = H // h_kv
+
+        def fold(x):
+            return x.reshape(x.shape[:-3] + (h_kv, g) + x.shape[-2:]).sum(axis=-3)
+
+        mags = (scale * np.abs(ds) @ np.abs(ke), fold(scale * t(np.abs(ds)) @ np.abs(q64)),
+                fold(t(p) @ np.abs(do64)))
+        tol, rtol = tol_for(dtype), RTOL_BF16_TERMS
+    else:
+        tol, rtol, mags = 2e-5, 0.0, (None, None, None)
+    for name, g, r, m in zip(("dQ", "dK", "dV"), (dq, dk, dv), (rq, rk, rv), mags):
+        assert_close(f"{name} {tag}", g, r, tol, rtol, mag=m)
+
+
+CASES = [  # B, H, H_kv, n_q, n_k, causal, q_offset, window
+    (1, 2, 2, 200, 200, True, 0, 0),
+    (1, 2, 2, 200, 200, True, 0, 31),
+    (1, 2, 1, 300, 300, False, 0, 64),
+    (2, 2, 2, 257, 300, True, 43, 100),
+    (1, 2, 2, 129, 600, True, 471, -1),
+    (1, 4, 2, 333, 333, False, -20, 150),
+    (1, 2, 2, 150, 150, True, -40, -1),
+    (1, 2, 2, 64, 1000, False, 500, 90),
+]
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "B{}H{}kv{}_{}x{}_c{}_off{}_w{}".format(*c))
+def test_band_parity(dev, case, d, dtype):
+    B, H, h_kv, n_q, n_k, causal, off, w = case
+    q, k, v, do = draw(4000 + n_q + n_k + d + (w % 97), B, H, h_kv, n_q, n_k, d, dtype)
+    scale = 1 / math.sqrt(d)
+    got = run(dev, q, k, v, do, scale, causal, off, w)
+    check(f"{case} d{d} {dtype}", got, q, k, v, do, scale, causal, off, w, dtype)
+
+
+def test_wide_window_and_zero_offset_equal_plain_attention_bitwise(dev):
+    q, k, v, do = draw(4100, 1, 4, 4, 300, 300, 128, torch.bfloat16)
+    qd, kd, vd, dod = (t.to(dev) for t in (q, k, v, do))
+    for causal in (False, True):
+        o1, l1 = fa.forward(qd, kd, vd, causal=causal)
+        o2, l2 = fa.forward(qd, kd, vd, causal=causal, window=10000)
+        g1 = fa.backward(qd, kd, vd, o1, dod, l1, causal=causal)
+        g2 = fa.backward(qd, kd, vd, o2, dod, l2, causal=causal, window=10000)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(l1, l2)
+        for a, b in zip(g1, g2):
+            assert torch.equal(a, b)
+
+
+def test_sliding_window_workload_size(dev):
+    # n = 4096, 32 heads, causal sliding window of 512 keys (+-512 before the
+    # diagonal), bf16; four whole heads against the oracle.
+    B, H, n, d, w = 1, 32, 4096, 128, 512
+    q, k, v, _ = draw(4200, B, H, H, n, n, d, torch.bfloat16)
+    o, lse = fa.forward(q.to(dev), k.to(dev), v.to(dev), causal=True, window=w)
+    torch.cuda.synchronize()
+    o, lse = o.cpu(), lse.cpu()
+    for h in (0, 9, 22, 31):
+        ro, rl = oracle.attention_fwd_band(np64(q[0, h]), np64(k[0, h]), np64(v[0, h]), 1 / math.sqrt(d), True, 0, w)
+        assert_close(f"O head {h}", o[0, h], ro, 2e-2)
+        assert_close(f"LSE head {h}", lse[0, h], rl, TOL_LSE)

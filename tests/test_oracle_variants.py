@@ -108,3 +108,113 @@ def test_mqa_value_gradient_is_sum_over_heads_of_p_transpose_do():
             for j in range(n):
                 ref[j] += (e[j] / z) * do[h, i]
     np.testing.assert_allclose(dv[0], ref, atol=1e-12)
+
+
+# ------------------------------------------- query offset and sliding window
+
+def _band_bruteforce(q, k, v, scale, causal, off, w):
+    """Scalar loops with the visibility rule written out per pair."""
+    n_q, n_k = len(q), len(k)
+    o = np.zeros((n_q, v.shape[1]))
+    lse = np.full(n_q, -np.inf)
+    for i in range(n_q):
+        p = i + off
+        keys = [j for j in range(n_k) if (not causal or j <= p) and (w < 0 or abs(p - j) <= w)]
+        if not keys:
+            continue
+        s = [scale * float(np.dot(q[i], k[j])) for j in keys]
+        m = max(s)
+        e = [np.exp(x - m) for x in s]
+        z = sum(e)
+        o[i] = sum(e[a] * v[j] for a, j in enumerate(keys)) / z
+        lse[i] = m + np.log(z)
+    return o, lse
+
+
+def test_band_without_offset_or_window_is_the_top_left_causal_mask():
+    for n_q, n_k in ((5, 5), (3, 7), (8, 2)):
+        np.testing.assert_array_equal(oracle.band_visible(n_q, n_k, True), oracle.causal_visible(n_q, n_k))
+        assert oracle.band_visible(n_q, n_k, False).all()
+
+
+@pytest.mark.parametrize("n,w", [(10, 0), (10, 3), (10, 9), (17, 4)])
+def test_window_pair_count_closed_form(n, w):
+    # +-w neighbours of every row, clipped at both ends: n(2w+1) - w(w+1).
+    assert int(oracle.band_visible(n, n, False, 0, w).sum()) == n * (2 * w + 1) - w * (w + 1)
+    # causal: the w previous keys and the key itself, clipped at the start.
+    assert int(oracle.band_visible(n, n, True, 0, w).sum()) == n * (w + 1) - w * (w + 1) // 2
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("off,w", [(0, 2), (3, 1), (-2, 3), (4, -1), (0, 0), (-6, -1)])
+def test_band_forward_matches_bruteforce(causal, off, w):
+    r = _rng(61 + off * 7 + w)
+    q, k, v = r.standard_normal((6, 3)), r.standard_normal((8, 3)), r.standard_normal((8, 2))
+    o, lse = oracle.attention_fwd_band(q, k, v, 0.8, causal, off, w)
+    ob, lb = _band_bruteforce(q, k, v, 0.8, causal, off, w)
+    np.testing.assert_allclose(o, ob, atol=1e-13)
+    np.testing.assert_array_equal(np.isfinite(lse), np.isfinite(lb))
+    np.testing.assert_allclose(lse[np.isfinite(lse)], lb[np.isfinite(lb)], atol=1e-13)
+
+
+def test_window_zero_causal_returns_the_aligned_value_row():
+    # Each row sees exactly key i + off: O_i = V_{i+off}, LSE_i = scale q_i.k_{i+off}.
+    r = _rng(67)
+    q, k, v = r.standard_normal((4, 3)), r.standard_normal((9, 3)), r.standard_normal((9, 2))
+    o, lse = oracle.attention_fwd_band(q, k, v, 0.5, True, 5, 0)
+    for i in range(4):
+        np.testing.assert_allclose(o[i], v[i + 5], atol=1e-15)
+        np.testing.assert_allclose(lse[i], 0.5 * np.dot(q[i], k[i + 5]), atol=1e-14)
+
+
+def test_last_query_on_last_key_sees_everything():
+    # One query at offset n_k - 1 with the causal mask is plain attention
+    # over all keys; a window at least n_k wide changes nothing.
+    r = _rng(71)
+    q, k, v = r.standard_normal((1, 4)), r.standard_normal((20, 4)), r.standard_normal((20, 4))
+    o1, l1 = oracle.attention_fwd_band(q, k, v, 0.4, True, 19, -1)
+    o2, l2 = oracle.attention_fwd(q, k, v, 0.4, False)
+    np.testing.assert_allclose(o1, o2, atol=1e-14)
+    np.testing.assert_allclose(l1, l2, atol=1e-14)
+    o3, l3 = oracle.attention_fwd_band(q, k, v, 0.4, False, 7, 25)
+    np.testing.assert_allclose(o3, o2, atol=1e-14)
+
+
+def test_rows_that_see_no_key_are_zero_with_minus_infinite_lse():
+    r = _rng(73)
+    q, k, v = r.standard_normal((5, 2)), r.standard_normal((5, 2)), r.standard_normal((5, 2))
+    o, lse = oracle.attention_fwd_band(q, k, v, 1.0, True, -3, -1)  # rows 0..2 sit before key 0
+    assert np.all(o[:3] == 0) and np.all(np.isneginf(lse[:3]))
+    assert np.all(np.isfinite(lse[3:]))
+    _, _, dv = oracle.attention_bwd_band(q, k, v, np.ones((5, 2)), 1.0, True, -3, -1)
+    # only rows 3, 4 contribute: dV sums their probabilities
+    assert abs(float(dv.sum()) - 2 * 2) < 1e-12
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("off,w,h_kv", [(0, 1, 2), (2, 2, 1), (-1, -1, 2)])
+def test_band_backward_finite_differences(causal, off, w, h_kv):
+    r = _rng(79 + w + 3 * off)
+    H, n_q, n_k, d = 2, 4, 5, 2
+    q = r.standard_normal((H, n_q, d))
+    k = r.standard_normal((h_kv, n_k, d))
+    v = r.standard_normal((h_kv, n_k, d))
+    do = r.standard_normal((H, n_q, d))
+    dq, dk, dv = oracle.attention_bwd_band(q, k, v, do, 0.7, causal, off, w)
+
+    def loss():
+        o, _ = oracle.attention_fwd_band(q, k, v, 0.7, causal, off, w)
+        return float(np.sum(do * o))
+
+    h = 1e-6
+    for x, g in ((q, dq), (k, dk), (v, dv)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            old = x[idx]
+            x[idx] = old + h
+            lp = loss()
+            x[idx] = old - h
+            lm = loss()
+            x[idx] = old
+            num[idx] = (lp - lm) / (2 * h)
+        np.testing.assert_allclose(g, num, rtol=1e-6, atol=1e-8)
