@@ -1,0 +1,171 @@
+"""Static check of matrix-product result reads in gfx950 device assembly.
+
+A matrix-core product (v_mfma_*) writes its result registers some cycles
+after it issues, and the hardware does not stall a vector instruction that
+reads them early: the program must leave enough wait states (instructions,
+or s_nop N = N + 1 states) in between.  The compiler counts them, but its
+count has been seen to fall short on a loop-exit path.  This module walks the
+control-flow graph of each kernel and reports every read of a product's
+result register (by a vector, memory or AGPR-copy instruction, or as the A/B
+operand of another product) whose distance from the product, minimised over
+all paths, is below the requirement.  Chained accumulation (the register as
+the C operand of the next product) is interlocked and not checked.
+
+Requirements used: passes + 2 wait states, the figure the compiler itself
+emits in straight-line code (18 for the 16-pass fp32 32x32x2 product, 10 for
+the 8-pass bf16 32x32x16 product).
+"""
+from __future__ import annotations
+
+import re
+from collections import defaultdict
+
+NEED = {
+    "v_mfma_f32_32x32x2_f32": 18,
+    "v_mfma_f32_32x32x16_bf16": 10,
+    "v_mfma_f32_16x16x32_bf16": 6,
+}
+DEFAULT_NEED = 18  # unknown products: the longest requirement above
+
+
+def need_of(op: str) -> int:
+    return NEED.get(op, DEFAULT_NEED)
+
+
+def registers(tok: str) -> list[tuple[str, int]]:
+    m = re.fullmatch(r"([va])(\d+)", tok)
+    if m:
+        return [(m.group(1), int(m.group(2)))]
+    m = re.fullmatch(r"([va])\[(\d+):(\d+)\]", tok)
+    if m:
+        return [(m.group(1), i) for i in range(int(m.group(2)), int(m.group(3)) + 1)]
+    return []
+
+
+def split_functions(text: str) -> dict[str, list[tuple[str, str]]]:
+    """{kernel symbol: [("label", name) | ("ins", text)]} for every function."""
+    funcs: dict[str, list] = {}
+    cur = None
+    for raw in text.splitlines():
+        code = raw.split(";")[0].rstrip()
+        if re.match(r"^_Z\S*:$", code):
+            cur = funcs.setdefault(code[:-1], [])
+            continue
+        if cur is None:
+            continue
+        if code.startswith(".Lfunc_end"):
+            cur = None
+            continue
+        if re.match(r"^\.LBB\S*:$", code):
+            cur.append(("label", code[:-1]))
+            continue
+        if raw.strip().startswith("; %bb."):
+            cur.append(("label", raw.strip()))
+            continue
+        code = code.strip()
+        if code and not code.startswith("."):
+            cur.append(("ins", code))
+    return funcs
+
+
+def _ops(ins: str) -> tuple[str, list[str]]:
+    parts = ins.replace(",", " ").split()
+    return parts[0], parts[1:]
+
+
+def _is_store(op: str) -> bool:
+    return op.startswith(("ds_write", "global_store", "buffer_store", "flat_store", "scratch_store"))
+
+
+def check_function(items: list[tuple[str, str]]) -> list[tuple[str, str, tuple[str, int], int, int]]:
+    """Violations (block label, instruction, register, wait states, needed)."""
+    blocks: list[dict] = []
+    blk = {"label": None, "ins": []}
+    for kind, x in items:
+        if kind == "label":
+            if blk["ins"] or blk["label"]:
+                blocks.append(blk)
+            blk = {"label": x, "ins": []}
+            continue
+        blk["ins"].append(x)
+        op = x.split()[0]
+        if op.startswith(("s_branch", "s_cbranch", "s_setpc")) or op == "s_endpgm":
+            blocks.append(blk)
+            blk = {"label": None, "ins": []}
+    if blk["ins"] or blk["label"]:
+        blocks.append(blk)
+    index = {b["label"]: i for i, b in enumerate(blocks) if b["label"]}
+    preds: dict[int, list[int]] = defaultdict(list)
+    for i, b in enumerate(blocks):
+        last = b["ins"][-1].split() if b["ins"] else ["s_nop"]
+        op = last[0]
+        if op == "s_branch":
+            preds[index[last[1]]].append(i)
+        elif op.startswith("s_cbranch"):
+            preds[index[last[1]]].append(i)
+            preds[i + 1].append(i)
+        elif op == "s_endpgm" or op.startswith("s_setpc"):
+            pass
+        else:
+            preds[i + 1].append(i)
+
+    def states(ins: str) -> int:
+        op, ops = _ops(ins)
+        return int(ops[0], 0) + 1 if op == "s_nop" else 1
+
+    def nearest(bi: int, pos: int, reg, budget: int, seen: frozenset):
+        """(wait states, needed) of the closest product writing reg before
+        (bi, pos) on any path, minimising wait states - needed; None if no
+        product within budget."""
+        dist = 0
+        lst = blocks[bi]["ins"]
+        for j in range(pos - 1, -1, -1):
+            op, ops = _ops(lst[j])
+            if op.startswith("v_mfma"):
+                if ops and reg in registers(ops[0]):
+                    return dist, need_of(op)
+            elif ops and not op.startswith("s_") and not _is_store(op) and reg in registers(ops[0]):
+                return None  # rewritten by something else first
+            dist += states(lst[j])
+            if dist >= budget:
+                return None
+        best = None
+        for p in preds.get(bi, []):
+            if (p, reg) in seen:
+                continue
+            r = nearest(p, len(blocks[p]["ins"]), reg, budget - dist, seen | {(p, reg)})
+            if r is not None:
+                r = (r[0] + dist, r[1])
+                if best is None or r[0] - r[1] < best[0] - best[1]:
+                    best = r
+        return best
+
+    budget = max(NEED.values()) + 1
+    out = []
+    for bi, b in enumerate(blocks):
+        for j, ins in enumerate(b["ins"]):
+            op, ops = _ops(ins)
+            if op.startswith("s_") or not ops:
+                continue
+            if op.startswith("v_mfma"):
+                srcs = ops[1:3]
+            elif _is_store(op):
+                srcs = ops
+            else:
+                srcs = ops[1:]
+            for tok in srcs:
+                for reg in registers(tok):
+                    r = nearest(bi, j, reg, budget, frozenset())
+                    if r is not None and r[0] < r[1]:
+                        out.append((b["label"], ins, reg, r[0], r[1]))
+    return out
+
+
+def check_text(text: str) -> dict[str, list]:
+    """{kernel: violations} for every function with at least one."""
+    res = {}
+    for name, items in split_functions(text).items():
+        v = check_function(items)
+        if v:
+            res[name] = v
+    return res
