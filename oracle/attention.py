@@ -40,9 +40,9 @@ Readings where the pages are silent or garbled (each is listed in the design doc):
   corrected update and can also run the printed one (``literal_page_rule``)
   so that a test shows it is wrong.
 
-Every function here is pinned by ``tests/test_oracle_pins.py`` against brute
-force, closed forms, invariants, finite differences and the values the pages
-print.
+Every function here is pinned by ``tests/test_oracle_pins.py`` and
+``tests/test_oracle_variants.py`` against brute force, closed forms,
+invariants, finite differences and the values the pages print.
 """
 from __future__ import annotations
 
@@ -69,6 +69,7 @@ __all__ = [
     "band_visible",
     "attention_fwd_band",
     "attention_bwd_band",
+    "lse_merge",
 ]
 
 
@@ -424,7 +425,7 @@ def _band_probs(q, k, scale, causal, q_offset, window):
     vis = band_visible(q.shape[-2], k.shape[-2], causal, q_offset, window)
     s = float(scale) * np.matmul(q, np.swapaxes(k, -1, -2))
     s = np.where(vis, s, -np.inf)
-    m = np.max(s, axis=-1, keepdims=True)
+    m = np.max(s, axis=-1, keepdims=True, initial=-np.inf)  # no keys at all: -inf
     empty = ~np.isfinite(m)
     m = np.where(empty, 0.0, m)
     e = np.where(vis, np.exp(s - m), 0.0)
@@ -473,4 +474,43 @@ def attention_bwd_band(q, k, v, do, scale: float, causal: bool = False, q_offset
 
         dk, dv = fold(dk), fold(dv)
     return dq, dk, dv
+
+
+# ------------------------------------------------ merging key-split results
+
+
+def lse_merge(o_parts, lse_parts):
+    """Combine attention results over disjoint key sets into the result over
+    their union.
+
+    Part p holds O_p (softmax over its own keys, times their values) and
+    LSE_p = ln sum_{j in part p} exp(S_ij).  Over the union the softmax
+    denominator is sum_p exp(LSE_p), so
+
+        LSE = ln sum_p exp(LSE_p),    O = sum_p exp(LSE_p - LSE) O_p.
+
+    This is the online softmax's rescaling by exp(m_old - m_new) ("Attention
+    Mechanism", section 13 "FlashAttention -- How It Works") applied to whole
+    parts; it is what lets the key axis be split across workers (same page,
+    section 16, "Ring Attention") or a long KV cache be split for decoding
+    (same page, section 8, "Key-Value (KV) Cache").  A part with LSE = -inf
+    (no visible key) contributes nothing; a row with no visible key in any
+    part gets O = 0 and LSE = -inf.
+
+    o_parts (P, ..., n, d), lse_parts (P, ..., n).
+    """
+    o = _f64(o_parts)
+    lse = _f64(lse_parts)
+    if o.shape[:-1] != lse.shape:
+        raise ValueError(f"O parts {o.shape} do not match LSE parts {lse.shape}")
+    m = np.max(lse, axis=0)
+    empty = ~np.isfinite(m)
+    ref = np.where(empty, 0.0, m)
+    w = np.exp(lse - ref)                     # exp(-inf) = 0 for empty parts
+    total = np.sum(w, axis=0)
+    safe = np.where(empty, 1.0, total)
+    out = np.sum(w[..., None] * o, axis=0) / safe[..., None]
+    with np.errstate(divide="ignore"):
+        out_lse = np.where(empty, -np.inf, ref + np.log(safe))
+    return np.where(empty[..., None], 0.0, out), out_lse
 

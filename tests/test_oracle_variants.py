@@ -218,3 +218,84 @@ def test_band_backward_finite_differences(causal, off, w, h_kv):
             x[idx] = old
             num[idx] = (lp - lm) / (2 * h)
         np.testing.assert_allclose(g, num, rtol=1e-6, atol=1e-8)
+
+
+# ------------------------------------------------ merging key-split results
+
+def _chunks(n_k, cuts):
+    edges = [0] + list(cuts) + [n_k]
+    return [(a, b) for a, b in zip(edges[:-1], edges[1:])]
+
+
+@pytest.mark.parametrize("causal,off,w", [(False, 0, -1), (True, 0, -1), (True, 37, -1), (True, 5, 9),
+                                          (False, -3, 6)])
+@pytest.mark.parametrize("cuts", [(17,), (1, 2, 30), (11, 11, 40)])
+def test_merge_of_key_chunks_is_the_attention_over_all_keys(causal, off, w, cuts):
+    # Each chunk [a, b) is attention over keys a..b-1 alone, with the query
+    # offset shifted by -a so that positions stay absolute; merged, the chunks
+    # must give the plain definition over all keys (brute force).
+    rng = _rng(70)
+    n_q, n_k, d, scale = 9, 48, 5, 0.4
+    q, k, v = rng.standard_normal((n_q, d)), rng.standard_normal((n_k, d)), rng.standard_normal((n_k, d))
+    parts = [oracle.attention_fwd_band(q, k[a:b], v[a:b], scale, causal, off - a, w) for a, b in _chunks(n_k, cuts)]
+    o, lse = oracle.lse_merge(np.stack([p[0] for p in parts]), np.stack([p[1] for p in parts]))
+    ro, rl = _band_bruteforce(q, k, v, scale, causal, off, w)
+    assert np.array_equal(np.isfinite(lse), np.isfinite(rl))
+    np.testing.assert_allclose(o, ro, atol=1e-12)
+    fin = np.isfinite(rl)
+    np.testing.assert_allclose(lse[fin], rl[fin], atol=1e-12)
+
+
+def test_merge_of_a_random_key_partition_non_causal():
+    # Without a mask any partition of the keys works, not just contiguous
+    # chunks: softmax is a sum over a set.
+    rng = _rng(71)
+    q, k, v = rng.standard_normal((6, 4)), rng.standard_normal((30, 4)), rng.standard_normal((30, 4))
+    perm = rng.permutation(30)
+    sets = [perm[:7], perm[7:8], perm[8:]]
+    parts = [oracle.attention_fwd(q, k[s], v[s], 0.7) for s in sets]
+    o, lse = oracle.lse_merge(np.stack([p[0] for p in parts]), np.stack([p[1] for p in parts]))
+    ro, rl = _band_bruteforce(q, k, v, 0.7, False, 0, -1)
+    np.testing.assert_allclose(o, ro, atol=1e-12)
+    np.testing.assert_allclose(lse, rl, atol=1e-12)
+
+
+def test_merge_special_cases():
+    rng = _rng(72)
+    o1, l1 = rng.standard_normal((4, 3)), rng.standard_normal(4)
+    # one part: unchanged
+    o, l = oracle.lse_merge(o1[None], l1[None])
+    np.testing.assert_array_equal(o, o1)
+    np.testing.assert_array_equal(l, l1)
+    # two equal parts: same O, LSE + ln 2
+    o, l = oracle.lse_merge(np.stack([o1, o1]), np.stack([l1, l1]))
+    np.testing.assert_allclose(o, o1, atol=1e-15)
+    np.testing.assert_allclose(l, l1 + np.log(2.0), atol=1e-15)
+    # a part without visible keys (O = 0, LSE = -inf) changes nothing
+    o, l = oracle.lse_merge(np.stack([np.zeros_like(o1), o1]), np.stack([np.full(4, -np.inf), l1]))
+    np.testing.assert_array_equal(o, o1)
+    np.testing.assert_array_equal(l, l1)
+    # no part with visible keys: O = 0, LSE = -inf
+    o, l = oracle.lse_merge(np.zeros((3, 4, 3)), np.full((3, 4), -np.inf))
+    assert np.all(o == 0) and np.all(l == -np.inf)
+    # weights: parts with LSE a and b weigh e^a : e^b
+    o, l = oracle.lse_merge(np.stack([np.ones((1, 1)), np.zeros((1, 1))]), np.array([[0.0], [np.log(3.0)]]))
+    np.testing.assert_allclose(o, [[0.25]], atol=1e-15)
+    np.testing.assert_allclose(l, [np.log(4.0)], atol=1e-15)
+
+
+def test_merge_of_decode_chunks_with_shared_heads():
+    # The decode shape: a few new queries at the end of a long cache
+    # (q_offset = n_k - n_q, causal), 4 query heads on 2 K/V heads, the cache
+    # split in uneven chunks.
+    rng = _rng(73)
+    H, h_kv, n_q, n_k, d = 4, 2, 3, 70, 8
+    q = rng.standard_normal((H, n_q, d))
+    k, v = rng.standard_normal((h_kv, n_k, d)), rng.standard_normal((h_kv, n_k, d))
+    off = n_k - n_q
+    parts = [oracle.attention_fwd_band(q, k[:, a:b], v[:, a:b], 0.35, True, off - a) for a, b in _chunks(n_k, (20, 21, 64))]
+    o, lse = oracle.lse_merge(np.stack([p[0] for p in parts]), np.stack([p[1] for p in parts]))
+    for h in range(H):
+        ro, rl = _band_bruteforce(q[h], k[h // 2], v[h // 2], 0.35, True, off, -1)
+        np.testing.assert_allclose(o[h], ro, atol=1e-12)
+        np.testing.assert_allclose(lse[h], rl, atol=1e-12)
