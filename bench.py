@@ -15,6 +15,12 @@ roofline   = the kernel taking the largest share of the step, its algorithmic
              matrix-core peak.
 cpu_baseline = the fp64 oracle timed on a bounded sample of the same workload.
 
+With --workload decode the step is instead one split-KV decoding call
+(fa_decode: 4 sequences x 64 query heads over 8 K/V heads, one new query row
+each, 32768 cached keys, d=128, bf16), an HBM-bound pass: value is the
+algorithmic bytes (K and V read once, q read, o and lse written) over the
+call time in GB/s, and the roofline is against HBM bandwidth.
+
 One JSON line is printed.  Only one GPU is supported: --gpus above 1 exits.
 """
 from __future__ import annotations
@@ -136,11 +142,127 @@ def cpu_baseline(w, budget_s: float):
     }
 
 
+def decode_bytes(B, H, H_kv, n_q, n_k, d, e=2):
+    """Algorithmic HBM bytes of one decoding call: K and V read once, q read,
+    o and lse written (the chunk partials are overhead)."""
+    return 2 * B * H_kv * n_k * d * e + 2 * B * H * n_q * d * e + B * H * n_q * 4
+
+
+def cpu_baseline_decode(w, budget_s: float):
+    """The fp64 oracle (banded forward) on whole (b, h) units of the decoding
+    workload until about ``budget_s`` seconds of CPU work; reported as K/V
+    bytes processed per second, like the GPU value."""
+    import numpy as np
+
+    import oracle
+
+    B, H, n_q, d = w.q.shape
+    h_kv, n_k = w.k.shape[1], w.k.shape[2]
+    group = H // h_kv
+    t0 = time.perf_counter()
+    done = 0
+    for b in range(B):
+        for j in range(h_kv):
+            k = w.k[b, j].float().numpy().astype(np.float64)
+            v = w.v[b, j].float().numpy().astype(np.float64)
+            for h in range(j * group, (j + 1) * group):
+                q = w.q[b, h].float().numpy().astype(np.float64)
+                oracle.attention_fwd_band(q, k, v, w.scale, True, n_k - n_q)
+                done += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    per_unit = decode_bytes(B, H, h_kv, n_q, n_k, d) / (B * H)
+    return {
+        "value": done * per_unit / dt / 1e9,
+        "unit": "GB/s",
+        "cores": None,
+        "kind": "oracle",
+        "sample": f"{done} of {B * H} (b,h) query heads, fp64 numpy banded forward over {n_k} keys, {dt:.1f} s",
+    }
+
+
+def run_decode(args, torch, fa, workloads, dev):
+    w = workloads.decode_gqa()
+    B, H, n_q, d = w.q.shape
+    h_kv, n_k = w.k.shape[1], w.k.shape[2]
+    q, k, v = (t.to(dev).contiguous() for t in (w.q, w.k, w.v))
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, n_q), dtype=torch.float32, device=dev)
+    splits = fa.decode_splits(B, H, h_kv, n_q, n_k)
+    ws = torch.empty(max(1, fa.decode_workspace_size(B, H, n_q, d, splits)), dtype=torch.uint8, device=dev)
+    steps = args.steps if args.steps != 20 else 200   # a call is ~0.1 ms: time more of them
+
+    def step():
+        fa.decode(q, k, v, causal=True, scale=w.scale, n_splits=splits, out=o, lse=lse, workspace=ws)
+
+    for _ in range(max(args.warmup, 5)):
+        step()
+    torch.cuda.synchronize()
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1 in events:
+        e0.record()
+        step()
+        e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    call_ms = sum(e0.elapsed_time(e1) for e0, e1 in events) / steps
+    ms_per_step = wall * 1e3 / steps
+    nbytes = decode_bytes(B, H, h_kv, n_q, n_k, d)
+    achieved = nbytes / (call_ms * 1e-3) / 1e9
+    out = {
+        "metric": "split-KV decoding: algorithmic HBM GB/s (K, V read once) at 32K context",
+        "value": round(nbytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": max(args.warmup, 5),
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) q, k, v; no dataset)",
+        "config": {"workload": w.name, "B": B, "H": H, "H_kv": h_kv, "n_q": n_q, "n_k": n_k, "d": d,
+                   "causal": True, "q_offset": n_k - n_q, "n_splits": splits,
+                   "step": "fa_decode (decode kernel + chunk merge)"},
+        "kernels": {"decode": {"ms": round(call_ms, 4), "gbs": round(achieved, 1)}},
+        "roofline": {
+            "kernel": "decode",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "traffic": None,
+        },
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_decode(w, args.cpu_budget)
+        out["cpu_baseline"]["value"] = round(out["cpu_baseline"]["value"], 3)
+        try:
+            import threadpoolctl
+
+            info = threadpoolctl.threadpool_info()
+            out["cpu_baseline"]["cores"] = max([i.get("num_threads", 1) for i in info
+                                                if i.get("user_api") == "blas"] or [1])
+        except Exception:  # noqa: BLE001
+            pass
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", choices=["train", "decode"], default="train",
+                    help="train: forward + backward at n=4096 (default); decode: split-KV decoding")
     ap.add_argument("--causal", action="store_true", help="causal mask (default: non-causal)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle CPU work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -163,6 +285,8 @@ def main(argv=None):
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
     dev = torch.device("cuda:0")
+    if args.workload == "decode":
+        return run_decode(args, torch, fa, workloads, dev)
     w = workloads.c3_train(args.causal)
     B, H, n, d = w.q.shape
     q, k, v, do = (t.to(dev).contiguous() for t in (w.q, w.k, w.v, w.do))

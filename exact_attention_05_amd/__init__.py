@@ -2,7 +2,9 @@
 
 The computation runs in hand-written HIP kernels behind the C ABI declared in
 ``include/fa.h`` (library ``lib/libfa.so``); this package is its Python
-binding.  See ``forward`` and ``backward``.
+binding.  See ``forward`` and ``backward``; ``decode`` (split-KV decoding
+against a long K/V cache) and ``lse_merge`` (attention results over disjoint
+key sets combined into the result over all keys).
 """
 from .binding import (  # noqa: F401
     FA_DTYPE_BF16,
@@ -20,7 +22,11 @@ from .binding import (  # noqa: F401
     backward_preprocess,
     backward_workspace,
     backward_workspace_size,
+    decode,
+    decode_splits,
+    decode_workspace_size,
     forward,
+    lse_merge,
     lib,
     library_path,
     status_string,

@@ -18,6 +18,7 @@ __all__ = [
     "FA_ERR_ALIGNMENT", "FA_DTYPE_FP32", "FA_DTYPE_BF16", "FaError", "library_path", "lib",
     "forward", "backward", "backward_workspace_size", "backward_workspace", "workspace_delta",
     "backward_preprocess", "backward_dkdv", "backward_dq", "status_string", "version",
+    "lse_merge", "decode", "decode_splits", "decode_workspace_size",
 ]
 
 FA_OK = 0
@@ -76,6 +77,15 @@ def lib() -> ctypes.CDLL:
         L.fa_backward_ext.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
                                       i, i, i, i, i, i, f, i, i, i, i, vp]
         L.fa_backward_ext.restype = i
+        ll = ctypes.c_longlong
+        L.fa_lse_merge.argtypes = [vp, vp, vp, vp, i, ll, i, i, i, vp]
+        L.fa_lse_merge.restype = i
+        L.fa_decode.argtypes = [vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, f, i, i, i, i, i, vp]
+        L.fa_decode.restype = i
+        L.fa_decode_workspace_size.argtypes = [i, i, i, i, i]
+        L.fa_decode_workspace_size.restype = sz
+        L.fa_decode_splits.argtypes = [i, i, i, i, i]
+        L.fa_decode_splits.restype = i
         L.fa_status_string.argtypes = [i]
         L.fa_status_string.restype = ctypes.c_char_p
         L.fa_version.argtypes = []
@@ -281,3 +291,77 @@ def backward_dq(q, k, v, do, workspace, causal=False, scale=None, dq=None):
                               _DTYPES[q.dtype], _stream(q.device))
     _check(st, "fa_backward_dq")
     return dq
+
+
+def lse_merge(o_parts, lse_parts, out_dtype: torch.dtype | None = None, out=None, lse=None):
+    """Merge attention results over disjoint key sets (fa_lse_merge).
+
+    o_parts: (P, ..., d) float32 or bfloat16, lse_parts: (P, ...) float32,
+    both contiguous on the GPU.  Returns (o, lse) of shapes (..., d), (...):
+    lse = ln sum_p exp(lse_p), o = sum_p exp(lse_p - lse) o_p.  ``out_dtype``
+    defaults to the parts' dtype."""
+    for name, t in (("o_parts", o_parts), ("lse_parts", lse_parts)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    if o_parts.dtype not in _DTYPES or lse_parts.dtype != torch.float32:
+        raise ValueError("o_parts must be float32 or bfloat16 and lse_parts float32")
+    if o_parts.dim() < 2 or tuple(o_parts.shape[:-1]) != tuple(lse_parts.shape):
+        raise ValueError(f"o_parts {tuple(o_parts.shape)} and lse_parts {tuple(lse_parts.shape)} do not match")
+    n_parts, d = o_parts.shape[0], o_parts.shape[-1]
+    rows = lse_parts[0].numel()
+    out_dtype = o_parts.dtype if out_dtype is None else out_dtype
+    if out_dtype not in _DTYPES:
+        raise ValueError(f"out_dtype {out_dtype} not supported")
+    shape = tuple(o_parts.shape[1:])
+    if out is None:
+        out = torch.empty(shape, dtype=out_dtype, device=o_parts.device)
+    if lse is None:
+        lse = torch.empty(shape[:-1], dtype=torch.float32, device=o_parts.device)
+    if tuple(out.shape) != shape or out.dtype != out_dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor of the merged shape and out_dtype")
+    if tuple(lse.shape) != shape[:-1] or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 tensor of the merged row shape")
+    st = lib().fa_lse_merge(_ptr(o_parts), _ptr(lse_parts), _ptr(out), _ptr(lse), n_parts, rows, d,
+                            _DTYPES[o_parts.dtype], _DTYPES[out_dtype], _stream(o_parts.device))
+    _check(st, "fa_lse_merge")
+    return out, lse
+
+
+def decode_splits(B, H, H_kv, n_q, n_k) -> int:
+    """The library's default number of key chunks for fa_decode."""
+    return int(lib().fa_decode_splits(B, H, H_kv, n_q, n_k))
+
+
+def decode_workspace_size(B, H, n_q, d, n_splits) -> int:
+    return int(lib().fa_decode_workspace_size(B, H, n_q, d, n_splits))
+
+
+def decode(q, k, v, causal: bool = True, scale: float | None = None, q_offset: int | None = None,
+           window: int | None = None, n_splits: int | None = None, out=None, lse=None,
+           workspace=None):
+    """Split-KV decoding (fa_decode, bfloat16): a few query rows q (B,H,n_q,d)
+    against a long K/V cache k, v (B,H_kv,n_k,d).  ``q_offset`` defaults to
+    n_k - n_q (the queries are the last n_q positions); masks as forward().
+    ``n_splits`` defaults to decode_splits(); the workspace is allocated when
+    not given.  Returns (o, lse)."""
+    B, H, n_q, n_k, d = _check_qkv(q, k, v)
+    h_kv = k.shape[1]
+    off = n_k - n_q if q_offset is None else int(q_offset)
+    splits = decode_splits(B, H, h_kv, n_q, n_k) if n_splits is None else int(n_splits)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, n_q), dtype=torch.float32, device=q.device)
+    _check_like("out", out, q)
+    if lse.shape != (B, H, n_q) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 (B, H, n_q) tensor")
+    if workspace is None:
+        n = decode_workspace_size(B, H, n_q, d, max(1, splits))
+        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+    st = lib().fa_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), *_ws(workspace),
+                         B, H, h_kv, n_q, n_k, d, _scale(scale, d), int(bool(causal)), off,
+                         -1 if window is None else int(window), splits, _DTYPES[q.dtype],
+                         _stream(q.device))
+    _check(st, "fa_decode")
+    return out, lse
+

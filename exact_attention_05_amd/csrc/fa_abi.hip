@@ -5,6 +5,7 @@
 #include "fa.h"
 #include "fa_internal.hpp"
 
+#include <algorithm>
 #include <climits>
 #include <cmath>
 #include <cstdint>
@@ -93,6 +94,25 @@ fa::BwdArgs make_bwd(const void* q, const void* k, const void* v, const void* o,
 }
 
 int status_of(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH; }
+
+size_t round256(size_t x) { return (x + 255) / 256 * 256; }
+
+// Split-KV decoding.  Chunks hold whole key blocks and at least
+// kDecodeMinChunk keys; the default aims at kDecodeTargetWgs workgroups (one
+// per compute unit).
+constexpr int kDecodeMinChunk = 256;
+constexpr long long kDecodeTargetWgs = 256;
+constexpr int kDecodeMaxSplits = 65536;
+
+// Workspace: float32 partial outputs (n_splits, B*H*n_q, d), then partial
+// LSE (n_splits, B*H*n_q), each rounded up to 256 bytes.
+size_t dec_part_o_bytes(int B, int H, int n_q, int d, int n_splits) {
+  return round256((size_t)n_splits * B * H * n_q * d * sizeof(float));
+}
+size_t dec_ws_bytes(int B, int H, int n_q, int d, int n_splits) {
+  if (n_splits <= 1) return 0;
+  return dec_part_o_bytes(B, H, n_q, d, n_splits) + round256((size_t)n_splits * B * H * n_q * sizeof(float));
+}
 
 // H_kv K/V heads shared by groups of H / H_kv consecutive query heads.
 int check_kv_heads(int H, int H_kv) {
@@ -263,6 +283,77 @@ int fa_backward_ext(const void* q, const void* k, const void* v, const void* o, 
                     float scale, int causal, int q_offset, int window, int dtype, void* stream) {
   return backward_impl(q, k, v, o, dO, lse, dq, dk, dv, workspace, workspace_bytes, B, H, H_kv,
                        n_q, n_k, d, scale, causal, dtype, stream, q_offset, window);
+}
+
+
+int fa_lse_merge(const void* o_parts, const float* lse_parts, void* o, float* lse, int n_parts,
+                 long long rows, int d, int parts_dtype, int out_dtype, void* stream) {
+  if (n_parts < 1 || rows < 1) return FA_ERR_INVALID_ARG;
+  if (d != 32 && d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  const auto dtype_ok = [](int t) { return t == FA_DTYPE_FP32 || t == FA_DTYPE_BF16; };
+  if (!dtype_ok(parts_dtype) || !dtype_ok(out_dtype)) return FA_ERR_UNSUPPORTED;
+  int st = first_error(check_tensor(o_parts), check_tensor(o), check_rowvec(lse_parts), check_rowvec(lse));
+  if (st != FA_OK) return st;
+  const long long rows_per_wg = 256 / (d / 4);
+  if ((rows + rows_per_wg - 1) / rows_per_wg > INT_MAX) return FA_ERR_INVALID_ARG;
+  if ((double)n_parts * (double)rows * d > 9.0e15) return FA_ERR_INVALID_ARG;
+  fa::MergeArgs m;
+  m.o_parts = o_parts;
+  m.lse_parts = lse_parts;
+  m.o = o;
+  m.lse = lse;
+  m.rows = rows;
+  m.n_parts = n_parts;
+  return status_of(fa::launch_lse_merge(m, d, parts_dtype == FA_DTYPE_BF16, out_dtype == FA_DTYPE_BF16,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+size_t fa_decode_workspace_size(int B, int H, int n_q, int d, int n_splits) {
+  if (B < 1 || H < 1 || n_q < 1 || n_splits < 1 || n_splits > kDecodeMaxSplits) return 0;
+  if (d != 32 && d != 64 && d != 128) return 0;
+  return dec_ws_bytes(B, H, n_q, d, n_splits);
+}
+
+int fa_decode_splits(int B, int H, int H_kv, int n_q, int n_k) {
+  if (B < 1 || H < 1 || n_q < 1 || n_k < 1 || check_kv_heads(H, H_kv) != FA_OK) return 0;
+  const long long rows = (long long)(H / H_kv) * n_q;
+  const long long units = (long long)B * H_kv * ((rows + 31) / 32);
+  const long long most = std::max(1LL, (long long)n_k / kDecodeMinChunk);
+  const long long want = (kDecodeTargetWgs + units - 1) / units;
+  return (int)std::max(1LL, std::min(want, most));
+}
+
+int fa_decode(const void* q, const void* k, const void* v, void* o, float* lse, void* workspace,
+              size_t workspace_bytes, int B, int H, int H_kv, int n_q, int n_k, int d, float scale,
+              int causal, int q_offset, int window, int n_splits, int dtype, void* stream) {
+  int st = first_error(check_sizes(B, H, n_q, n_k, d, dtype), check_kv_heads(H, H_kv),
+                       check_band(n_q, n_k, q_offset, window), check_scale_causal(scale, causal),
+                       check_tensor(q), check_tensor(k), check_tensor(v), check_tensor(o),
+                       check_rowvec(lse));
+  if (st != FA_OK) return st;
+  if (dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
+  if (n_splits < 1 || n_splits > kDecodeMaxSplits) return FA_ERR_INVALID_ARG;
+  const long long rows = (long long)(H / H_kv) * n_q;
+  const long long n_rb = (rows + 31) / 32;
+  long long chunk = ((long long)n_k + n_splits - 1) / n_splits;
+  chunk = (chunk + fa::kDecodeBlock - 1) / fa::kDecodeBlock * fa::kDecodeBlock;
+  const long long splits = ((long long)n_k + chunk - 1) / chunk;  // chunks that hold keys
+  if (rows > INT_MAX || (long long)B * H_kv * splits * n_rb > INT_MAX) return FA_ERR_INVALID_ARG;
+  if (splits > 1) {
+    if (workspace == nullptr || workspace_bytes < dec_ws_bytes(B, H, n_q, d, n_splits)) return FA_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return FA_ERR_ALIGNMENT;
+  }
+  fa::DecArgs a;
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+  char* w = static_cast<char*>(workspace);
+  a.part_o = splits > 1 ? reinterpret_cast<float*>(w) : nullptr;
+  a.part_lse = splits > 1 ? reinterpret_cast<float*>(w + dec_part_o_bytes(B, H, n_q, d, n_splits)) : nullptr;
+  a.B = B; a.H = H; a.group = H / H_kv; a.h_kv = H_kv;
+  a.n_q = n_q; a.n_k = n_k; a.q_offset = q_offset; a.window = window;
+  a.rows = (int)rows; a.n_rb = (int)n_rb;
+  a.n_splits = (int)splits; a.chunk = (int)chunk;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  return status_of(fa::launch_decode_bf16(a, d, causal != 0, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

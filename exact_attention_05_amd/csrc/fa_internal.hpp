@@ -122,6 +122,46 @@ __host__ __device__ inline Band band_of(const Args& a, bool causal) {
   return Band{a.n_q, a.n_k, a.q_offset, a.window, causal};
 }
 
+// Arguments of one split-KV decoding launch (bf16).  The group * n_q query
+// rows that share a K/V head are packed: packed row r is row r % n_q of query
+// head kv * group + r / n_q.  The keys are cut into n_splits chunks of `chunk`
+// keys (a multiple of the key block); each (batch, K/V head, row block,
+// chunk) workgroup leaves a partial result that the merge combines, unless
+// n_splits == 1, when it writes O and LSE itself.
+struct DecArgs {
+  const void* q;     // (B,H,n_q,d)
+  const void* k;     // (B,H_kv,n_k,d)
+  const void* v;
+  void* o;           // (B,H,n_q,d) bf16
+  float* lse;        // (B,H,n_q)
+  float* part_o;     // (n_splits, B*H*n_q, d) float32 partial outputs
+  float* part_lse;   // (n_splits, B*H*n_q) float32 partial LSE
+  int B;
+  int H;             // query heads per batch entry
+  int group;         // query heads per K/V head
+  int h_kv;          // K/V heads per batch entry
+  int n_q;
+  int n_k;
+  int q_offset;
+  int window;
+  int rows;          // group * n_q packed rows per (batch, K/V head)
+  int n_rb;          // 32-row blocks of packed rows
+  int n_splits;
+  int chunk;         // keys per split
+  float scale_log2;
+};
+
+// Arguments of the LSE merge of n_parts partial results over disjoint key
+// sets: parts (n_parts, rows, d) and (n_parts, rows) -> (rows, d), (rows).
+struct MergeArgs {
+  const void* o_parts;
+  const float* lse_parts;
+  void* o;
+  float* lse;
+  long long rows;
+  int n_parts;
+};
+
 // Each launcher enqueues its kernel(s) on `stream` and returns the HIP status
 // of the launch.  Shapes were validated by the caller.
 hipError_t launch_fwd_bf16(const FwdArgs& a, int d, bool causal, hipStream_t stream);
@@ -132,5 +172,11 @@ hipError_t launch_bwd_dkdv_bf16(const BwdArgs& a, int d, bool causal, hipStream_
 hipError_t launch_bwd_dq_bf16(const BwdArgs& a, int d, bool causal, hipStream_t stream);
 hipError_t launch_bwd_dkdv_f32(const BwdArgs& a, int d, bool causal, hipStream_t stream);
 hipError_t launch_bwd_dq_f32(const BwdArgs& a, int d, bool causal, hipStream_t stream);
+
+// Key block of the decoding kernel: chunks are whole multiples of it.
+constexpr int kDecodeBlock = 128;
+hipError_t launch_decode_bf16(const DecArgs& a, int d, bool causal, hipStream_t stream);
+// in_bf16 / out_bf16: bf16 (else float32) partial and merged outputs.
+hipError_t launch_lse_merge(const MergeArgs& a, int d, bool in_bf16, bool out_bf16, hipStream_t stream);
 
 }  // namespace fa

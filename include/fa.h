@@ -171,6 +171,50 @@ int fa_backward_ext(const void* q, const void* k, const void* v, const void* o,
                     int B, int H, int H_kv, int n_q, int n_k, int d, float scale,
                     int causal, int q_offset, int window, int dtype, void* stream);
 
+/* Merge of attention results over disjoint key sets into the result over
+ * their union ("Attention Mechanism", section 13: the online softmax's
+ * rescaling applied to whole parts; section 16 "Ring Attention": attention
+ * over keys spread across workers).  Part p holds o_p (normalised over its
+ * own keys) and lse_p; the result is lse = ln sum_p exp(lse_p) and
+ * o = sum_p exp(lse_p - lse) o_p.  Parts with lse_p = -inf (no visible key)
+ * contribute nothing; a row with -inf in every part gets o = 0, lse = -inf.
+ *   o_parts    (n_parts, rows, d), parts_dtype (FA_DTYPE_FP32 or _BF16)
+ *   lse_parts  (n_parts, rows) float32
+ *   o          (rows, d), out_dtype;  lse (rows) float32
+ * The parts of fa_forward_ext calls over key chunks [a, b) with query offset
+ * q_offset - a (rows = B*H*n_q) merge into the call over all keys.  n_parts,
+ * rows >= 1; d in {32, 64, 128}; o_parts, o 16-byte aligned; outputs must not
+ * alias the parts.  Asynchronous on `stream`. */
+int fa_lse_merge(const void* o_parts, const float* lse_parts, void* o, float* lse,
+                 int n_parts, long long rows, int d, int parts_dtype, int out_dtype,
+                 void* stream);
+
+/* Split-KV decoding ("Attention Mechanism", section 8, "Key-Value (KV)
+ * Cache"): a few query rows (q: (B,H,n_q,d)) against a long cache (k, v:
+ * (B,H_kv,n_k,d)), with the masks of fa_forward_ext -- for new tokens at the
+ * end of the cache pass causal = 1, q_offset = n_k - n_q.  The key axis is
+ * cut into n_splits chunks of whole 128-key blocks; each chunk's result goes
+ * to the workspace and fa_lse_merge's rule combines them into o (B,H,n_q,d)
+ * and lse (B,H,n_q).  bf16 only (FA_ERR_UNSUPPORTED otherwise); other
+ * arguments and errors as fa_forward_ext.  n_splits >= 1 (fa_decode_splits
+ * gives the library's choice); with more than one chunk the workspace must
+ * hold fa_decode_workspace_size(B, H, n_q, d, n_splits) bytes, 256-byte
+ * aligned (else FA_ERR_WORKSPACE / FA_ERR_ALIGNMENT); with one chunk it may
+ * be NULL. */
+int fa_decode(const void* q, const void* k, const void* v, void* o, float* lse,
+              void* workspace, size_t workspace_bytes,
+              int B, int H, int H_kv, int n_q, int n_k, int d, float scale,
+              int causal, int q_offset, int window, int n_splits, int dtype, void* stream);
+
+/* Workspace bytes fa_decode needs for n_splits chunks (0 for one chunk;
+ * 0 for invalid sizes). */
+size_t fa_decode_workspace_size(int B, int H, int n_q, int d, int n_splits);
+
+/* The number of chunks fa_decode uses by default for a shape: enough
+ * workgroups to fill the GPU, chunks of at least 256 keys (>= 1; 0 for
+ * invalid sizes). */
+int fa_decode_splits(int B, int H, int H_kv, int n_q, int n_k);
+
 /* Static text for a status code ("unknown status" for other values). */
 const char* fa_status_string(int status);
 

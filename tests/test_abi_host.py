@@ -163,3 +163,66 @@ def test_ext_rejects_out_of_range_band(n, q_offset, window):
     assert L.fa_backward_ext(P, P, P, P, P, P, P2, P2, P2, P2, 1 << 20, 1, 2, 2, 8, n, 64, 0.125, 1,
                              q_offset, window, 1, None) == fa.FA_ERR_INVALID_ARG
 
+
+
+# ---------------------------------------------------- decoding and merging
+
+def dec(q=P, k=P, v=P, o=P2, lse=P2, ws=None, ws_bytes=0, B=1, H=8, H_kv=2, n_q=1, n_k=4096, d=128,
+        scale=0.088, causal=1, q_offset=4095, window=-1, n_splits=4, dtype=1):
+    return fa.lib().fa_decode(q, k, v, o, lse, ws, ws_bytes, B, H, H_kv, n_q, n_k, d, scale, causal,
+                              q_offset, window, n_splits, dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n_splits=0), fa.FA_ERR_INVALID_ARG),
+    (dict(n_splits=65537), fa.FA_ERR_INVALID_ARG),
+    (dict(dtype=0), fa.FA_ERR_UNSUPPORTED),           # float32 decoding is not provided
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(H_kv=3), fa.FA_ERR_INVALID_ARG),
+    (dict(window=-2), fa.FA_ERR_INVALID_ARG),
+    (dict(q=None), fa.FA_ERR_INVALID_ARG),
+    (dict(k=MIS), fa.FA_ERR_ALIGNMENT),
+    (dict(), fa.FA_ERR_WORKSPACE),                      # 4 chunks, no workspace
+    (dict(ws=P, ws_bytes=1024), fa.FA_ERR_WORKSPACE),   # too small
+    (dict(ws=ctypes.c_void_p(0x100010), ws_bytes=1 << 30), fa.FA_ERR_ALIGNMENT),
+])
+def test_decode_rejects(kw, code):
+    assert dec(**kw) == code
+
+
+def test_decode_workspace_size():
+    # float32 partial outputs and LSE per chunk, each rounded up to 256 bytes
+    assert fa.decode_workspace_size(1, 8, 1, 128, 1) == 0
+    rows = 2 * 8 * 3
+    expect = -(-4 * rows * 128 * 4 // 256) * 256 + -(-4 * rows * 4 // 256) * 256
+    assert fa.decode_workspace_size(2, 8, 3, 128, 4) == expect
+    assert fa.decode_workspace_size(2, 8, 3, 96, 4) == 0
+    assert fa.decode_workspace_size(0, 8, 3, 128, 4) == 0
+
+
+def test_decode_splits():
+    # enough (batch, K/V head, row block, chunk) workgroups for one per
+    # compute unit, chunks of at least 256 keys
+    assert fa.decode_splits(4, 64, 8, 1, 32768) == 8      # 32 units -> 8 chunks of 4096 keys
+    assert fa.decode_splits(1, 8, 8, 1, 1000) == 3        # at most n_k / 256
+    assert fa.decode_splits(64, 32, 32, 1, 4096) == 1     # 2048 units already
+    assert fa.decode_splits(1, 8, 3, 1, 4096) == 0        # H_kv must divide H
+
+
+def merge(op=P, lp=P2, o=P, lse=P2, n_parts=2, rows=16, d=64, pdt=0, odt=1):
+    return fa.lib().fa_lse_merge(op, lp, o, lse, n_parts, rows, d, pdt, odt, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n_parts=0), fa.FA_ERR_INVALID_ARG),
+    (dict(rows=0), fa.FA_ERR_INVALID_ARG),
+    (dict(d=48), fa.FA_ERR_UNSUPPORTED),
+    (dict(pdt=2), fa.FA_ERR_UNSUPPORTED),
+    (dict(odt=-1), fa.FA_ERR_UNSUPPORTED),
+    (dict(op=None), fa.FA_ERR_INVALID_ARG),
+    (dict(o=MIS), fa.FA_ERR_ALIGNMENT),
+    (dict(lse=ctypes.c_void_p(0x200002)), fa.FA_ERR_ALIGNMENT),
+    (dict(rows=1 << 40), fa.FA_ERR_INVALID_ARG),
+])
+def test_lse_merge_rejects(kw, code):
+    assert merge(**kw) == code

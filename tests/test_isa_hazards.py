@@ -12,7 +12,7 @@ from isa_hazards import check_text
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "exact_attention_05_amd", "csrc")
-SOURCES = ["fa_fwd.hip", "fa_bwd.hip"]
+SOURCES = ["fa_fwd.hip", "fa_bwd.hip", "fa_decode.hip"]
 
 
 def _device_asm(src: str, out_dir: str) -> str:
@@ -41,7 +41,7 @@ def assembly(tmp_path_factory):
 @pytest.mark.parametrize("src", SOURCES)
 def test_matrix_results_read_after_enough_wait_states(assembly, src):
     text = assembly[src]
-    assert text.count("v_mfma") > 100, "no matrix products found: assembly not parsed?"
+    assert text.count("v_mfma") > 40, "no matrix products found: assembly not parsed?"
     bad = check_text(text)
     lines = [f"{k}: {v[:3]}" for k, v in bad.items()]
     assert not bad, "reads too close to a matrix product:\n" + "\n".join(lines)

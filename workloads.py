@@ -24,6 +24,13 @@ float32 draws):
   256 checked rows are the first 256 entries of ``torch.randperm(32 * 16384)``
   under seed 4004, row r -> (h, i) = (r // 16384, r % 16384).
 * ``c5``: (2, 16, 4096, 128) bf16, seed 5, causal; draws q, k, v, dO.
+* ``decode_gqa``: one decoding step of a grouped-K/V attention layer at long
+  context, the shape "Attention Mechanism" uses for its KV-cache arithmetic
+  (section 12: a 70B-class model at 32K context; 64 query heads over 8 K/V
+  heads, head width 128): 4 sequences, one new query row each, against
+  32768 cached keys; bf16, seed 8, draws q (4, 64, 1, 128) then k and v
+  (4, 8, 32768, 128); causal with the query on the last key, scale
+  1/sqrt(128).
 
 All values are i.i.d. N(0, 1), so with scale 1/sqrt(d) the scores are close
 to N(0, 1): dense heads, no padding, no variable lengths.
@@ -35,7 +42,7 @@ from dataclasses import dataclass
 
 import torch
 
-__all__ = ["Workload", "c1", "c2", "c3", "c3_train", "c4", "c4_rows", "c5", "random_qkv"]
+__all__ = ["Workload", "c1", "c2", "c3", "c3_train", "c4", "c4_rows", "c5", "decode_gqa", "random_qkv"]
 
 
 @dataclass
@@ -101,6 +108,14 @@ def c5() -> Workload:
     gen = torch.Generator().manual_seed(5)
     q, k, v, do = (t.to(torch.bfloat16) for t in _draw(gen, (2, 16, 4096, 128), 4))
     return Workload("c5 bwd bf16 B2 H16 n4096 d128 causal", q, k, v, 1.0 / math.sqrt(128), True, do)
+
+
+def decode_gqa(B: int = 4, H: int = 64, H_kv: int = 8, n_k: int = 32768, d: int = 128) -> Workload:
+    gen = torch.Generator().manual_seed(8)
+    q = torch.randn(B, H, 1, d, generator=gen).to(torch.bfloat16)
+    k = torch.randn(B, H_kv, n_k, d, generator=gen).to(torch.bfloat16)
+    v = torch.randn(B, H_kv, n_k, d, generator=gen).to(torch.bfloat16)
+    return Workload(f"decode bf16 B{B} H{H} Hkv{H_kv} n_q1 n_k{n_k} d{d}", q, k, v, 1.0 / math.sqrt(d), True)
 
 
 def random_qkv(seed: int, B: int, H: int, n_q: int, n_k: int, d: int,
