@@ -42,6 +42,7 @@ PEAK_HBM_GBS = 8000.0
 METRIC = "attention fwd/bwd TFLOP/s (4·B·H·n²·d/t) and % bf16 MFMA peak at n=4096,d=128"
 
 KERNEL_SOURCES = {
+    "decode": "exact_attention_05_amd/csrc/fa_decode.hip",
     "fwd": "exact_attention_05_amd/csrc/fa_fwd.hip",
     "bwd_preprocess": "exact_attention_05_amd/csrc/fa_bwd.hip",
     "bwd_dkdv": "exact_attention_05_amd/csrc/fa_bwd.hip",
@@ -142,6 +143,16 @@ def cpu_baseline(w, budget_s: float):
     }
 
 
+def calibration_copy(torch, dev):
+    """One elementwise copy of 512 MiB (fp32 x*1 into a second buffer): a
+    kernel of known traffic for scaling the memory counters."""
+    src = torch.ones(1 << 27, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def decode_bytes(B, H, H_kv, n_q, n_k, d, e=2):
     """Algorithmic HBM bytes of one decoding call: K and V read once, q read,
     o and lse written (the chunk partials are overhead)."""
@@ -210,6 +221,8 @@ def run_decode(args, torch, fa, workloads, dev):
         e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    if args.calibration_copy:
+        calibration_copy(torch, dev)
     call_ms = sum(e0.elapsed_time(e1) for e0, e1 in events) / steps
     ms_per_step = wall * 1e3 / steps
     nbytes = decode_bytes(B, H, h_kv, n_q, n_k, d)
@@ -238,7 +251,7 @@ def run_decode(args, torch, fa, workloads, dev):
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
-            "traffic": None,
+            "traffic": load_traffic("decode"),
         },
     }
     if not args.no_cpu_baseline:
@@ -327,11 +340,7 @@ def main(argv=None):
     wall = time.perf_counter() - t0
 
     if args.calibration_copy:
-        src = torch.ones(1 << 27, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        torch.mul(src, 1.0, out=dst)
-        torch.cuda.synchronize()
-        del src, dst
+        calibration_copy(torch, dev)
 
     per_stage = {s: 0.0 for s in stages}
     step_ms = []

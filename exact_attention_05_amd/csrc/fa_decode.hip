@@ -337,17 +337,35 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(MergeArgs a) {
   const TI* op = static_cast<const TI*>(a.o_parts);
   const float* lp = a.lse_parts;
 
+  // Parts in groups of kU, so that a group's loads are in flight together.
+  constexpr int kU = 8;
   float mx = -INFINITY;
-  for (int p = 0; p < a.n_parts; ++p) mx = fmaxf(mx, lp[(size_t)p * a.rows + row]);
+  for (int p0 = 0; p0 < a.n_parts; p0 += kU) {
+    float lv[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+      lv[u] = p0 + u < a.n_parts ? lp[(size_t)(p0 + u) * a.rows + row] : -INFINITY;
+#pragma unroll
+    for (int u = 0; u < kU; ++u) mx = fmaxf(mx, lv[u]);
+  }
   const float ref = mx == -INFINITY ? 0.f : mx;
   f32x4 acc = f32x4{};
   float s = 0.f;
-  for (int p = 0; p < a.n_parts; ++p) {
-    const size_t pr = (size_t)p * a.rows + row;
-    const float w = fast_exp2((lp[pr] - ref) * kLog2e);  // 0 for a part without keys
-    const f32x4 x = Vec4<TI>::load(op + pr * D + c);
-    acc += w * x;
-    s += w;
+  for (int p0 = 0; p0 < a.n_parts; p0 += kU) {
+    float w[kU];
+    f32x4 x[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const bool in = p0 + u < a.n_parts;
+      const size_t pr = (size_t)(in ? p0 + u : p0) * a.rows + row;
+      w[u] = in ? fast_exp2((lp[pr] - ref) * kLog2e) : 0.f;  // 0 for a part without keys
+      x[u] = Vec4<TI>::load(op + pr * D + c);
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      acc += w[u] * x[u];
+      s += w[u];
+    }
   }
   const float inv = s > 0.f ? 1.f / s : 0.f;
   Vec4<TO>::store(static_cast<TO*>(a.o) + (size_t)row * D + c, acc * inv);
