@@ -14,23 +14,33 @@
 // D_i in the workspace, so the later stages exponentiate base 2 with a single
 // fused multiply-add and can copy both rows straight into LDS.
 //
-// bf16 stage 2 (dK, dV): 8 waves (two per SIMD); each wave owns 32 keys and
-// keeps their K and V rows in registers as matrix-core B operands for the
-// whole pass.  Query blocks of 64 rows (Q, dO, and the two row vectors)
-// stream through double-buffered LDS by direct global -> LDS copies.
-// S = Q K^T and dP = dO V^T land in the accumulator layout with one key per
-// lane, which is the B-operand layout needed for dV^T += dO^T P and
+// bf16 stage 2 (dK, dV): 4 waves (one per SIMD, 512 registers each); each
+// wave owns 32 keys and keeps their K and V rows in registers as matrix-core
+// B operands for the whole pass.  Query stages of 64 rows (Q, dO, and the two
+// row vectors) stream through double-buffered LDS by direct global -> LDS
+// copies.  S = Q K^T and dP = dO V^T land in the accumulator layout with one
+// key per lane, which is the B-operand layout needed for dV^T += dO^T P and
 // dK^T += Q^T dS; the dO^T and Q^T A operands come from the same LDS tiles
-// through the transposing read.
+// through the transposing read.  Each stage is two 32-query sub-blocks, and
+// the unmasked stages run software-pipelined: the S and dP products of one
+// sub-block issue while the vector unit turns the previous sub-block's
+// probabilities into bf16 dS, and the dV and dK products of a sub-block
+// overlap the next one's exponentials; operand fragments are read from LDS
+// four products ahead.  Stages that need a mask (causal diagonal, window
+// edges, ragged ends) take a plain, unpipelined path.  With shared K/V heads
+// the workgroup loops over the query heads of its group and sums.
 //
 // bf16 stage 3 (dQ): mirrors the forward kernel.  8 waves own 32 queries
 // each and keep Q and dO in registers; key blocks of 64 rows (K, V) stream
 // through LDS.  S^T = K Q^T and dP^T = V dO^T put one query per lane, so
 // LSE_i and D_i are one register each, and dQ^T += K^T dS^T reads K^T
-// through the transposing read.
+// through the transposing read.  Key blocks that need no mask for any row of
+// the workgroup run through a separate code path, two at a time with fixed
+// LDS buffers.
 //
-// In both, blocks that need no mask for any row of the workgroup run
-// through a separate code path, two at a time with fixed LDS buffers.
+// Masks: the query offset and sliding window of the extended entry points
+// (see Band) decide which query stages or key blocks a workgroup visits at
+// all and which of those need a per-element mask.
 #include "fa_internal.hpp"
 #include "fa_device.hpp"
 #include "fa_tiles.hpp"

@@ -7,11 +7,11 @@
 //
 // bf16 kernel (the hot path)
 // --------------------------
-// A workgroup is 4 waves (one per SIMD) and owns 256 consecutive query rows
-// of one (batch, head); each wave owns 64 of them as two 32-row blocks.  Key
-// and value blocks of 64 rows stream through double-buffered LDS: the global
-// loads of block t+1 are in flight while block t is computed, and one
-// barrier per block separates the two buffers.
+// A workgroup is 8 waves (two per SIMD) and owns 256 consecutive query rows
+// of one (batch, head), 32 per wave.  Key and value blocks of 64 rows stream
+// through double-buffered LDS by direct global -> LDS copies: the copies of
+// block t+1 are in flight while block t is computed, and one barrier per
+// block separates the two buffers.
 //
 // The wave computes the transposed score tile S^T = K Q^T on the
 // 32x32x16 bf16 matrix cores, with K read from LDS as the A operand and Q
@@ -26,7 +26,10 @@
 //
 // Grid: one workgroup per (query tile, batch*head), remapped so that the
 // workgroups of one head run on the same XCD and share its L2; with the
-// causal mask the longest query tiles are issued first.
+// causal mask the longest query tiles are issued first.  A workgroup visits
+// only the key blocks some of its rows see (causal mask, query offset,
+// sliding window; see Band); blocks that every row sees entirely run through
+// an unmasked code path, two at a time with fixed LDS buffers.
 //
 // fp32 kernel
 // -----------
