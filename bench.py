@@ -269,13 +269,178 @@ def run_decode(args, torch, fa, workloads, dev):
     return 0
 
 
+PEAK_FP32_TFLOPS = 157.3   # MI355X fp32 matrix / vector peak
+
+
+def _median_us(torch, fn, reps: int, warmup: int = 3, batch: int = 10):
+    """Per-call time of fn() in microseconds: the median over ``reps`` HIP-event
+    measurements of ``batch`` back-to-back calls each (calls issued one at a
+    time with an idle GPU in between run at a lower clock)."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(batch):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e3 / batch)
+    ts.sort()
+    return ts[len(ts) // 2]
+
+
+def _sclk_sampler():
+    """Best-effort sampling of the GPU's shader clock (amd-smi) in a thread;
+    returns (start, stop) where stop() gives the mean MHz or None."""
+    import subprocess
+    import threading
+
+    samples, done = [], threading.Event()
+
+    def run():
+        while not done.is_set():
+            try:
+                r = subprocess.run(["amd-smi", "metric", "-g", "0", "--clock", "--json"],
+                                   capture_output=True, text=True, timeout=5)
+                data = json.loads(r.stdout)
+                node = data["gpu_data"][0] if isinstance(data, dict) and "gpu_data" in data else (
+                    data[0] if isinstance(data, list) else data)
+                clk = node.get("clock", {})
+                vals = [float(v["clk"]["value"]) for k, v in clk.items()
+                        if k.startswith("gfx_") and isinstance(v, dict) and isinstance(v.get("clk"), dict)
+                        and v["clk"].get("value") not in (None, "N/A")]
+                if vals:
+                    samples.append(sum(vals) / len(vals))  # mean over the XCDs
+            except Exception:  # noqa: BLE001
+                return
+            done.wait(0.05)
+
+    t = threading.Thread(target=run, daemon=True)
+
+    def stop():
+        done.set()
+        t.join(timeout=10)
+        return round(sum(samples) / len(samples), 1) if samples else None
+
+    return t.start, stop
+
+
+def run_configs(args, torch, fa, workloads, dev):
+    """Each workload's hot call timed on its own (median of HIP-event times),
+    plus the short-sequence HBM sweep of the forward pass."""
+    res = {}
+
+    def fwd_entry(w, reps=10):
+        q, k, v = (t.to(dev).contiguous() for t in (w.q, w.k, w.v))
+        o = torch.empty_like(q)
+        B, H, n, d = q.shape
+        lse = torch.empty((B, H, n), dtype=torch.float32, device=dev)
+        us = _median_us(torch, lambda: fa.forward(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse), reps)
+        flops = 4 * d * B * H * visible_pairs(n, n, w.causal)
+        peak = PEAK_BF16_TFLOPS if q.dtype == torch.bfloat16 else PEAK_FP32_TFLOPS
+        tf = flops / (us * 1e-6) / 1e12
+        entry = {"us": round(us, 1), "tflops": round(tf, 2), "pct_peak": round(100 * tf / peak, 2),
+                 "peak": peak}
+        if w.causal:
+            entry["tflops_literal"] = round(4 * d * B * H * n * n / (us * 1e-6) / 1e12, 2)
+        return entry
+
+    res["c1"] = fwd_entry(workloads.c1())
+    res["c2_fp32"] = fwd_entry(workloads.c2(torch.float32))
+    res["c2_bf16"] = fwd_entry(workloads.c2(torch.bfloat16))
+    res["c3_noncausal"] = fwd_entry(workloads.c3(False))
+    # the shader clock while the c3 forward runs back to back for about a second
+    start, stop = _sclk_sampler()
+    w3 = workloads.c3(False)
+    q3, k3, v3 = (t.to(dev) for t in (w3.q, w3.k, w3.v))
+    start()
+    for _ in range(4000):
+        fa.forward(q3, k3, v3, scale=w3.scale)
+    torch.cuda.synchronize()
+    sclk = stop()
+    del q3, k3, v3
+    res["c3_causal"] = fwd_entry(workloads.c3(True))
+    res["c4_causal"] = fwd_entry(workloads.c4(), reps=5)
+    torch.cuda.empty_cache()
+    # c5: the backward pass (three stages) after one forward.
+    w = workloads.c5()
+    q, k, v, do = (t.to(dev).contiguous() for t in (w.q, w.k, w.v, w.do))
+    o, lse = fa.forward(q, k, v, causal=True, scale=w.scale)
+    ws = fa.backward_workspace(*q.shape[:3], k.shape[2], q.shape[3], q.dtype, dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    us = _median_us(torch, lambda: fa.backward(q, k, v, o, do, lse, causal=True, scale=w.scale,
+                                                dq=dq, dk=dk, dv=dv, workspace=ws), 10)
+    B, H, n, d = q.shape
+    pairs = B * H * visible_pairs(n, n, True)
+    tf = 10 * d * pairs / (us * 1e-6) / 1e12
+    res["c5_backward_causal"] = {"us": round(us, 1), "tflops": round(tf, 2),
+                                 "pct_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2),
+                                 "tflops_literal": round(4 * B * H * n * n * d / (us * 1e-6) / 1e12, 2)}
+    del q, k, v, do, o, lse, ws, dq, dk, dv
+    torch.cuda.empty_cache()
+
+    # Short-sequence sweep: B=16, H=32, d=128 bf16 non-causal forward, input
+    # sets rotated so that the bytes touched between two calls of the same
+    # set exceed the 256 MB last-level cache.
+    sweep = {}
+    for n in (128, 256, 512, 1024):
+        B, H, d = 16, 32, 128
+        per_set = 4 * B * H * n * d * 2
+        sets = max(3, -(-768 * 2**20 // per_set))
+        bufs = []
+        g = torch.Generator(device="cpu").manual_seed(n)
+        for _ in range(sets):
+            t = torch.randn(3, B, H, n, d, generator=g).to(torch.bfloat16).to(dev)
+            bufs.append((t[0], t[1], t[2], torch.empty((B, H, n, d), dtype=torch.bfloat16, device=dev),
+                         torch.empty((B, H, n), dtype=torch.float32, device=dev)))
+        it = [0]
+
+        def call():
+            qq, kk, vv, oo, ll = bufs[it[0] % sets]
+            it[0] += 1
+            fa.forward(qq, kk, vv, out=oo, lse=ll)
+
+        us = _median_us(torch, call, 20, warmup=sets)
+        nbytes = 4 * B * H * n * d * 2 + 4 * B * H * n
+        sweep[f"n{n}"] = {"us": round(us, 1), "gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
+                          "pct_hbm": round(100 * nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 2),
+                          "tflops": round(4 * d * B * H * n * n / (us * 1e-6) / 1e12, 2)}
+        del bufs
+        torch.cuda.empty_cache()
+
+    out = {
+        "metric": "per-workload hot-call throughput (TFLOP/s algorithmic, % of the dtype's peak)",
+        "value": res["c3_noncausal"]["tflops"],
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": 1,
+        "warmup": 3,
+        "ms_per_step": None,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1); no dataset)",
+        "config": {"workload": "c1..c5 hot calls + short-sequence HBM sweep (B16 H32 d128)"},
+        "configs": res,
+        "hbm_sweep": sweep,
+        "sclk_mhz_mean_c3_forward": sclk,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", choices=["train", "decode"], default="train",
-                    help="train: forward + backward at n=4096 (default); decode: split-KV decoding")
+    ap.add_argument("--workload", choices=["train", "decode", "configs"], default="train",
+                    help="train: forward + backward at n=4096 (default); decode: split-KV decoding; "
+                         "configs: every workload's hot call plus the short-sequence HBM sweep")
     ap.add_argument("--causal", action="store_true", help="causal mask (default: non-causal)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle CPU work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -300,6 +465,8 @@ def main(argv=None):
     dev = torch.device("cuda:0")
     if args.workload == "decode":
         return run_decode(args, torch, fa, workloads, dev)
+    if args.workload == "configs":
+        return run_configs(args, torch, fa, workloads, dev)
     w = workloads.c3_train(args.causal)
     B, H, n, d = w.q.shape
     q, k, v, do = (t.to(dev).contiguous() for t in (w.q, w.k, w.v, w.do))

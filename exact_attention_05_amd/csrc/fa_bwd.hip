@@ -123,13 +123,17 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16_kernel(BwdArgs a, int n_kti
   __shared__ __attribute__((aligned(16))) float slse[2][C::kBQ];
   __shared__ __attribute__((aligned(16))) float sdel[2][C::kBQ];
 
-  // The workgroups with the first keys see the most query blocks under the
-  // causal mask; they come first in the natural order.
   // One workgroup per (key tile, batch * K/V head); with shared K/V heads it
   // sums dK and dV over the query heads of its group.
-  const int work = xcd_remap(blockIdx.x, gridDim.x);
-  const int bhkv = work / n_ktiles;
-  const int kt = work - bhkv * n_ktiles;
+  int bhkv, kt;
+  if (CAUSAL) {
+    // the first key tiles are seen by the most queries: they go first
+    costliest_first(blockIdx.x, gridDim.x, n_ktiles, bhkv, kt);
+  } else {
+    const int work = xcd_remap(blockIdx.x, gridDim.x);
+    bhkv = work / n_ktiles;
+    kt = work - bhkv * n_ktiles;
+  }
   const int h_kv = a.H / group;
   const int bh0 = GROUPED ? (bhkv / h_kv) * a.H + (bhkv % h_kv) * group : bhkv;  // first query head
 
@@ -473,10 +477,16 @@ __global__ __launch_bounds__(512) void bwd_dq_bf16_kernel(BwdArgs a, int n_qtile
   __shared__ __attribute__((aligned(1024))) char sk[2][C::KV::kBytes];
   __shared__ __attribute__((aligned(1024))) char sv[2][C::KV::kBytes];
 
-  const int work = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = work / n_qtiles;
-  int qt = work - bh * n_qtiles;
-  if (CAUSAL) qt = n_qtiles - 1 - qt;
+  int bh, qt;
+  if (CAUSAL) {
+    // the last query tiles see the most keys: they go first
+    costliest_first(blockIdx.x, gridDim.x, n_qtiles, bh, qt);
+    qt = n_qtiles - 1 - qt;
+  } else {
+    const int work = xcd_remap(blockIdx.x, gridDim.x);
+    bh = work / n_qtiles;
+    qt = work - bh * n_qtiles;
+  }
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -634,9 +644,15 @@ __global__ __launch_bounds__(256) void bwd_dkdv_f32_kernel(BwdArgs a, int n_ktil
 
   // One workgroup per (key tile, batch * K/V head), summing over the query
   // heads that share the K/V head.
-  const int work = xcd_remap(blockIdx.x, gridDim.x);
-  const int bhkv = work / n_ktiles;
-  const int kt = work - bhkv * n_ktiles;
+  int bhkv, kt;
+  if (CAUSAL) {
+    // the first key tiles are seen by the most queries: they go first
+    costliest_first(blockIdx.x, gridDim.x, n_ktiles, bhkv, kt);
+  } else {
+    const int work = xcd_remap(blockIdx.x, gridDim.x);
+    bhkv = work / n_ktiles;
+    kt = work - bhkv * n_ktiles;
+  }
   const int h_kv = a.H / a.group;
   const int bh0 = (bhkv / h_kv) * a.H + (bhkv % h_kv) * a.group;
   const int tid = threadIdx.x;
@@ -793,10 +809,16 @@ __global__ __launch_bounds__(256) void bwd_dq_f32_kernel(BwdArgs a, int n_qtiles
   __shared__ __attribute__((aligned(16))) float sk[2][C::kBS * C::kStride];
   __shared__ __attribute__((aligned(16))) float sv[2][C::kBS * C::kStride];
 
-  const int work = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = work / n_qtiles;
-  int qt = work - bh * n_qtiles;
-  if (CAUSAL) qt = n_qtiles - 1 - qt;
+  int bh, qt;
+  if (CAUSAL) {
+    // the last query tiles see the most keys: they go first
+    costliest_first(blockIdx.x, gridDim.x, n_qtiles, bh, qt);
+    qt = n_qtiles - 1 - qt;
+  } else {
+    const int work = xcd_remap(blockIdx.x, gridDim.x);
+    bh = work / n_qtiles;
+    qt = work - bh * n_qtiles;
+  }
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;

@@ -171,7 +171,7 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecArgs a) {
     float mx = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[i]);
-    mx = fmaxf(mx, swap_halves(mx));
+    mx = max_halves(mx);
     const float m_new = fmaxf(m, mx == -INFINITY ? -INFINITY : mx * sl2);
     const float ref = m_new == -INFINITY ? 0.f : m_new;
     const float alpha = fast_exp2(m - ref);  // 0 while the row has seen nothing
@@ -228,7 +228,7 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecArgs a) {
 
   // Merge the four waves: each scales its O^T by exp2(m_w - M), M the
   // largest m_w of the query, and the sums add up.
-  const float lt = l + swap_halves(l);
+  const float lt = sum_halves(l);
   __syncthreads();  // every wave is done with its K/V tiles
   float* sm = reinterpret_cast<float*>(smem);  // [wave][32] m
   float* sl = sm + C::kWaves * 32;             // [wave][32] l

@@ -153,9 +153,27 @@ __device__ __forceinline__ uint32_t lds_address(const T* p) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
-// Value from the lane 32 positions away (the other half of the wave).
-__device__ __forceinline__ float swap_halves(float x) {
-  return __shfl_xor(x, 32, 64);
+// The two halves of the wave combined, the result in every lane: lane l and
+// lane l ^ 32 both get op(x[l mod 32], x[l mod 32 + 32]).  v_permlane32_swap
+// exchanges the upper half of its first operand with the lower half of its
+// second; with x as both operands one result holds x's lower half twice and
+// the other x's upper half twice.  A register-to-register move, unlike a
+// shuffle through the LDS unit, so it does not wait behind LDS reads.
+__device__ __forceinline__ void halves(float x, float& lo, float& hi) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
+                                                  __builtin_bit_cast(uint32_t, x), false, false);
+  lo = __builtin_bit_cast(float, (uint32_t)r[0]);
+  hi = __builtin_bit_cast(float, (uint32_t)r[1]);
+}
+__device__ __forceinline__ float max_halves(float x) {
+  float lo, hi;
+  halves(x, lo, hi);
+  return fmaxf(lo, hi);
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  float lo, hi;
+  halves(x, lo, hi);
+  return lo + hi;
 }
 
 // Round-to-nearest-even float -> bf16 pair.
@@ -198,6 +216,27 @@ __device__ __forceinline__ int xcd_remap(int bid, int total) {
   if (total % kXcds != 0) return bid;
   const int per = total / kXcds;
   return (bid % kXcds) * per + bid / kXcds;
+}
+
+// Work order for tiles of unequal cost (under the causal mask the query
+// tiles near the end and the key tiles near the start see the most keys or
+// queries): block `bid` of `total` = heads * n_tiles gets (head, rank), rank 0
+// being a head's costliest tile.  Blocks go round-robin over the XCDs; each
+// XCD gets whole heads (their K/V stay in one L2) and issues its tiles
+// costliest first across all of its heads, so that no large tile starts
+// last while the other compute units idle.  Without an even split of the
+// heads over the XCDs the order is costliest first over all heads.
+__device__ __forceinline__ void costliest_first(int bid, int total, int n_tiles, int& head, int& rank) {
+  const int heads = total / n_tiles;
+  if (heads % kXcds == 0) {
+    const int per = heads / kXcds;
+    const int i = bid / kXcds;
+    head = (bid % kXcds) * per + i % per;
+    rank = i / per;
+  } else {
+    head = bid % heads;
+    rank = bid / heads;
+  }
 }
 
 }  // namespace fa

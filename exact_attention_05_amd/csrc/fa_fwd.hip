@@ -69,10 +69,16 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdArgs a, int n_qtiles) 
   __shared__ __attribute__((aligned(1024))) char sk[2][C::KV::kBytes];
   __shared__ __attribute__((aligned(1024))) char sv[2][C::KV::kBytes];
 
-  const int work = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = work / n_qtiles;
-  int qt = work - bh * n_qtiles;
-  if (CAUSAL) qt = n_qtiles - 1 - qt;
+  int bh, qt;
+  if (CAUSAL) {
+    // the last query tiles see the most keys: they go first
+    costliest_first(blockIdx.x, gridDim.x, n_qtiles, bh, qt);
+    qt = n_qtiles - 1 - qt;
+  } else {
+    const int work = xcd_remap(blockIdx.x, gridDim.x);
+    bh = work / n_qtiles;
+    qt = work - bh * n_qtiles;
+  }
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -177,7 +183,7 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdArgs a, int n_qtiles) 
     for (int kb = 0; kb < C::kKB; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(s[kb][i], s[kb][i + 1]));
-    mx = fmaxf(mx, swap_halves(mx));
+    mx = max_halves(mx);
     const float mt = (mx == -INFINITY) ? -INFINITY : mx * sl2;
     if (__builtin_amdgcn_ballot_w64(mt > m + kLazyRescale) != 0) {
       const float m_new = fmaxf(m, mt);
@@ -250,7 +256,7 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdArgs a, int n_qtiles) 
 
   // Epilogue: normalise, store O (bf16) and LSE (natural log).  A row that
   // sees no key at all gets O = 0 and LSE = -inf.
-  const float lt = l + swap_halves(l);
+  const float lt = sum_halves(l);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   if (qi < n_q) {
     __bf16* op = static_cast<__bf16*>(a.o) + ((size_t)bh * n_q + qi) * D;
@@ -287,7 +293,7 @@ __device__ __forceinline__ float softmax_block(f32x16 (&s)[KB], float& m, float&
       if (MASK && ((hide[kb] >> i) & 1u)) continue;
       mx = fmaxf(mx, s[kb][i]);
     }
-  mx = fmaxf(mx, swap_halves(mx));
+  mx = max_halves(mx);
   const float mt = (mx == -INFINITY) ? -INFINITY : mx * scale_log2;
   const float m_new = fmaxf(m, mt);
   const float ref = (m_new == -INFINITY) ? 0.f : m_new;
@@ -327,10 +333,16 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdArgs a, int n_qtiles) {
   __shared__ __attribute__((aligned(16))) float sk[2][C::kBN * C::kKStride];
   __shared__ __attribute__((aligned(16))) float sv[2][C::kBN * C::kVStride];
 
-  const int work = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = work / n_qtiles;
-  int qt = work - bh * n_qtiles;
-  if (CAUSAL) qt = n_qtiles - 1 - qt;
+  int bh, qt;
+  if (CAUSAL) {
+    // the last query tiles see the most keys: they go first
+    costliest_first(blockIdx.x, gridDim.x, n_qtiles, bh, qt);
+    qt = n_qtiles - 1 - qt;
+  } else {
+    const int work = xcd_remap(blockIdx.x, gridDim.x);
+    bh = work / n_qtiles;
+    qt = work - bh * n_qtiles;
+  }
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -443,7 +455,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdArgs a, int n_qtiles) {
     __syncthreads();
   }
 
-  const float lt = l + swap_halves(l);
+  const float lt = sum_halves(l);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   if (qi < n_q) {
     float* op = static_cast<float*>(a.o) + ((size_t)bh * n_q + qi) * D;
