@@ -351,6 +351,21 @@ def run_configs(args, torch, fa, workloads, dev):
     res["c1"] = fwd_entry(workloads.c1())
     res["c2_fp32"] = fwd_entry(workloads.c2(torch.float32))
     res["c2_bf16"] = fwd_entry(workloads.c2(torch.bfloat16))
+    # c2 has one head: 16 query tiles for 256 compute units.  The split-KV
+    # entry point (fa_decode) spreads the keys over more workgroups.
+    w2 = workloads.c2(torch.bfloat16)
+    q2, k2, v2 = (t.to(dev) for t in (w2.q, w2.k, w2.v))
+    o2 = torch.empty_like(q2)
+    l2 = torch.empty(q2.shape[:3], dtype=torch.float32, device=dev)
+    sp = fa.decode_splits(1, 1, 1, q2.shape[2], k2.shape[2])
+    ws2 = torch.empty(max(1, fa.decode_workspace_size(1, 1, q2.shape[2], q2.shape[3], sp)),
+                      dtype=torch.uint8, device=dev)
+    us = _median_us(torch, lambda: fa.decode(q2, k2, v2, causal=False, q_offset=0, scale=w2.scale,
+                                              n_splits=sp, out=o2, lse=l2, workspace=ws2), 10)
+    tf = 4 * 64 * 4096 * 4096 / (us * 1e-6) / 1e12
+    res["c2_bf16_split_kv"] = {"us": round(us, 1), "tflops": round(tf, 2),
+                               "pct_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2), "n_splits": sp}
+    del q2, k2, v2, o2, l2, ws2
     res["c3_noncausal"] = fwd_entry(workloads.c3(False))
     # the shader clock while the c3 forward runs back to back for about a second
     start, stop = _sclk_sampler()
