@@ -346,6 +346,11 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16_kernel(BwdArgs a, int n_kti
   // and ragged ends): per sub-block S and dP, masked P and dS, then the dV
   // and dK products.  The next stage is started at once, since nothing here
   // reads the other buffer.
+  // Query rows that see some key of this wave (none past n_k): a masked
+  // sub-block outside them is skipped.
+  const int kw0 = k0 + wave * 32;
+  const int wq_lo = kw0 < n_k ? band.q_lo(kw0) : 0;
+  const int wq_hi = kw0 < n_k ? band.q_hi(min(n_k, kw0 + 32)) : 0;
   auto masked_stage = [&](int b) __attribute__((always_inline)) {
     const int buf = b & 1;
     wait_lds_dma();
@@ -355,6 +360,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16_kernel(BwdArgs a, int n_kti
     const char* gt = sdo[buf];
 #pragma unroll 1
     for (int r0 = 0; r0 < C::kBQ; r0 += 32) {
+      const int qs = (qb_first + b) * C::kBQ + r0;
+      if (qs + 32 <= wq_lo || qs >= wq_hi) continue;  // no row here sees a key of this wave
       s = f32x16{};
       dp = f32x16{};
 #pragma unroll

@@ -149,6 +149,9 @@ void fwd_bf16_kernel(FwdArgs a, int n_qtiles) {
     const char* ks = sk[buf];
     const char* vs = sv[buf];
     const int k0 = t * C::kBN;
+    // A masked block whose keys none of this wave's rows sees (the causal
+    // diagonal above the wave, a window edge) changes nothing for it.
+    if (MASK && (qw >= n_q || band.key_hi(qw + 32) <= k0 || band.key_lo(qw) >= k0 + C::kBN)) return;
 
     // Matrix-core phases run at raised wave priority, the softmax at normal
     // priority: of the two waves on a SIMD, the one still issuing matrix
