@@ -58,6 +58,8 @@ def lib() -> ctypes.CDLL:
         L.fa_forward.restype = i
         L.fa_backward_workspace_size.argtypes = [i, i, i, i, i, i]
         L.fa_backward_workspace_size.restype = sz
+        L.fa_backward_gqa_workspace_size.argtypes = [i, i, i, i, i, i, i]
+        L.fa_backward_gqa_workspace_size.restype = sz
         L.fa_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
                                   i, i, i, i, i, f, i, i, vp]
         L.fa_backward.restype = i
@@ -184,8 +186,12 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None,
     return out, lse
 
 
-def backward_workspace_size(B, H, n_q, n_k, d, dtype: torch.dtype) -> int:
-    return int(lib().fa_backward_workspace_size(B, H, n_q, n_k, d, _DTYPES[dtype]))
+def backward_workspace_size(B, H, n_q, n_k, d, dtype: torch.dtype, H_kv: int | None = None) -> int:
+    """Workspace bytes of the backward pass (with H_kv K/V heads shared by the
+    H query heads: the size fa_backward_gqa / fa_backward_ext need)."""
+    if H_kv is None or H_kv == H:
+        return int(lib().fa_backward_workspace_size(B, H, n_q, n_k, d, _DTYPES[dtype]))
+    return int(lib().fa_backward_gqa_workspace_size(B, H, H_kv, n_q, n_k, d, _DTYPES[dtype]))
 
 
 def _check_like(name, t, ref):
@@ -208,9 +214,9 @@ def backward(q, k, v, o, do, lse, causal: bool = False, scale: float | None = No
     _check_like("dq", dq, q)
     _check_like("dk", dk, k)
     _check_like("dv", dv, v)
-    if workspace is None:
-        workspace = backward_workspace(B, H, n_q, n_k, d, q.dtype, q.device)
     h_kv = k.shape[1]
+    if workspace is None:
+        workspace = backward_workspace(B, H, n_q, n_k, d, q.dtype, q.device, H_kv=h_kv)
     if q_offset != 0 or window is not None:
         st = lib().fa_backward_ext(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse),
                                    _ptr(dq), _ptr(dk), _ptr(dv), *_ws(workspace),
@@ -233,9 +239,9 @@ def backward(q, k, v, o, do, lse, causal: bool = False, scale: float | None = No
     return dq, dk, dv
 
 
-def backward_workspace(B, H, n_q, n_k, d, dtype: torch.dtype, device) -> torch.Tensor:
-    """A device buffer of fa_backward_workspace_size bytes (256-byte aligned)."""
-    n = backward_workspace_size(B, H, n_q, n_k, d, dtype)
+def backward_workspace(B, H, n_q, n_k, d, dtype: torch.dtype, device, H_kv: int | None = None) -> torch.Tensor:
+    """A device buffer of backward_workspace_size bytes (256-byte aligned)."""
+    n = backward_workspace_size(B, H, n_q, n_k, d, dtype, H_kv)
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 

@@ -17,6 +17,8 @@ constexpr int kVersion = 1 * 10000 + 0 * 100 + 0;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+size_t round256(size_t x) { return (x + 255) / 256 * 256; }
+
 int check_sizes(int B, int H, int n_q, int n_k, int d, int dtype) {
   if (B < 1 || H < 1 || n_q < 1 || n_k < 1) return FA_ERR_INVALID_ARG;
   if ((long long)B * (long long)H > INT_MAX) return FA_ERR_INVALID_ARG;
@@ -77,6 +79,28 @@ int check_workspace(const void* ws, size_t bytes, int B, int H, int n_q) {
   return FA_OK;
 }
 
+// Shared K/V heads in the backward pass: a K/V head's query heads are split
+// into `slices` runs (a divisor of the group size), each dK/dV workgroup
+// taking one run, and each run leaves float32 partial dK and dV after the two
+// row vectors of the workspace.  Runs of one query head give the most
+// parallel work and keep the dK/dV kernel free of a head loop (which costs it
+// 72 spilled registers); the runs grow only when the partials would pass
+// kBwdPartLimit bytes.
+constexpr int kBwdKeyTile = 128;  // keys per dK/dV workgroup (both dtypes)
+constexpr double kBwdPartLimit = 4294967296.0;
+int bwd_slices(int B, int H, int H_kv, int n_k) {
+  const int group = H / H_kv;
+  for (int sl = group; sl > 1; --sl)
+    if (group % sl == 0 && 2.0 * sl * B * H_kv * n_k * 128 * 4 <= kBwdPartLimit) return sl;
+  return 1;
+}
+size_t part_bytes(int B, int H_kv, int n_k, int d, int slices) {
+  return slices > 1 ? round256((size_t)slices * B * H_kv * n_k * d * sizeof(float)) : 0;
+}
+size_t gqa_ws_bytes(int B, int H, int H_kv, int n_q, int n_k, int d) {
+  return ws_bytes(B, H, n_q) + 2 * part_bytes(B, H_kv, n_k, d, bwd_slices(B, H, H_kv, n_k));
+}
+
 fa::BwdArgs make_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
                      const float* lse, const void* ws, void* dq, void* dk, void* dv, int B, int H,
                      int n_q, int n_k, float scale, int H_kv, int q_offset = 0, int window = -1) {
@@ -90,12 +114,12 @@ fa::BwdArgs make_bwd(const void* q, const void* k, const void* v, const void* o,
   a.q_offset = q_offset; a.window = window;
   a.scale = scale;
   a.scale_log2 = scale * 1.4426950408889634f;
+  a.slices = 1;
+  a.part_dk = a.part_dv = nullptr;
   return a;
 }
 
 int status_of(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH; }
-
-size_t round256(size_t x) { return (x + 255) / 256 * 256; }
 
 // Split-KV decoding.  Chunks hold whole key blocks and at least
 // kDecodeMinChunk keys; the default aims at kDecodeTargetWgs workgroups (one
@@ -164,8 +188,18 @@ int backward_impl(const void* q, const void* k, const void* v, const void* o, co
   if (st != FA_OK) return st;
   st = check_workspace(workspace, workspace_bytes, B, H, n_q);
   if (st != FA_OK) return st;
+  const int slices = bwd_slices(B, H, H_kv, n_k);
+  if (workspace_bytes < gqa_ws_bytes(B, H, H_kv, n_q, n_k, d)) return FA_ERR_WORKSPACE;
+  if ((long long)((n_k + kBwdKeyTile - 1) / kBwdKeyTile) * B * H_kv * slices > INT_MAX)
+    return FA_ERR_INVALID_ARG;
   fa::BwdArgs a = make_bwd(q, k, v, o, dO, lse, workspace, dq, dk, dv, B, H, n_q, n_k, scale, H_kv,
                            q_offset, window);
+  a.slices = slices;
+  if (slices > 1) {
+    char* w = static_cast<char*>(workspace) + ws_bytes(B, H, n_q);
+    a.part_dk = reinterpret_cast<float*>(w);
+    a.part_dv = reinterpret_cast<float*>(w + part_bytes(B, H_kv, n_k, d, slices));
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool bf16 = dtype == FA_DTYPE_BF16;
   hipError_t e = fa::launch_bwd_preprocess(a, d, bf16, s);
@@ -173,6 +207,10 @@ int backward_impl(const void* q, const void* k, const void* v, const void* o, co
   e = bf16 ? fa::launch_bwd_dkdv_bf16(a, d, causal != 0, s)
            : fa::launch_bwd_dkdv_f32(a, d, causal != 0, s);
   if (e != hipSuccess) return FA_ERR_LAUNCH;
+  if (slices > 1) {
+    e = fa::launch_bwd_reduce_slices(a, d, bf16, s);
+    if (e != hipSuccess) return FA_ERR_LAUNCH;
+  }
   e = bf16 ? fa::launch_bwd_dq_bf16(a, d, causal != 0, s)
            : fa::launch_bwd_dq_f32(a, d, causal != 0, s);
   return status_of(e);
@@ -210,6 +248,11 @@ int fa_forward_gqa(const void* q, const void* k, const void* v, void* o, float* 
 size_t fa_backward_workspace_size(int B, int H, int n_q, int n_k, int d, int dtype) {
   if (check_sizes(B, H, n_q, n_k, d, dtype) != FA_OK) return 0;
   return ws_bytes(B, H, n_q);
+}
+
+size_t fa_backward_gqa_workspace_size(int B, int H, int H_kv, int n_q, int n_k, int d, int dtype) {
+  if (check_sizes(B, H, n_q, n_k, d, dtype) != FA_OK || check_kv_heads(H, H_kv) != FA_OK) return 0;
+  return gqa_ws_bytes(B, H, H_kv, n_q, n_k, d);
 }
 
 int fa_backward_preprocess(const void* o, const void* dO, const float* lse, void* workspace,

@@ -113,11 +113,15 @@ struct DkdvCfg {
   static constexpr int kRowVecBytes = kBQ * 4;   // one stage of LSE2 or D
 };
 
-template <int D, bool CAUSAL, bool GROUPED>
+// MODE 0: one query head per workgroup, no sharing (group 1), final dK/dV;
+// MODE 1: one query head of a shared K/V head, float32 partials;
+// MODE 2: a run of several query heads of a shared K/V head.
+template <int D, bool CAUSAL, int MODE>
 __global__ __launch_bounds__(256) void bwd_dkdv_bf16_kernel(BwdArgs a, int n_ktiles) {
   using C = DkdvCfg<D>;
+  constexpr bool GROUPED = MODE == 2;
   // Query heads per K/V head, a compile-time 1 without sharing.
-  const int group = GROUPED ? a.group : 1;
+  const int group = MODE == 0 ? 1 : a.group;
   __shared__ __attribute__((aligned(1024))) char sq[2][C::QT::kBytes];
   __shared__ __attribute__((aligned(1024))) char sdo[2][C::QT::kBytes];
   __shared__ __attribute__((aligned(16))) float slse[2][C::kBQ];
@@ -125,17 +129,23 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16_kernel(BwdArgs a, int n_kti
 
   // One workgroup per (key tile, batch * K/V head); with shared K/V heads it
   // sums dK and dV over the query heads of its group.
-  int bhkv, kt;
+  // Work item (key tile, K/V head, run of `run` consecutive query heads of
+  // its group); without shared heads one run of one head.
+  const int slices = MODE == 0 ? 1 : a.slices;
+  const int run = GROUPED ? group / slices : 1;
+  int hs, kt;
   if (CAUSAL) {
     // the first key tiles are seen by the most queries: they go first
-    costliest_first(blockIdx.x, gridDim.x, n_ktiles, bhkv, kt);
+    costliest_first(blockIdx.x, gridDim.x, n_ktiles, hs, kt);
   } else {
     const int work = xcd_remap(blockIdx.x, gridDim.x);
-    bhkv = work / n_ktiles;
-    kt = work - bhkv * n_ktiles;
+    hs = work / n_ktiles;
+    kt = work - hs * n_ktiles;
   }
+  const int bhkv = hs / slices;
+  const int sl = hs - bhkv * slices;
   const int h_kv = a.H / group;
-  const int bh0 = GROUPED ? (bhkv / h_kv) * a.H + (bhkv % h_kv) * group : bhkv;  // first query head
+  const int bh0 = (bhkv / h_kv) * a.H + (bhkv % h_kv) * group + sl * run;  // first query head
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -432,7 +442,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16_kernel(BwdArgs a, int n_kti
   if constexpr (!GROUPED) {
     if (nblocks > 0) one_head();
   } else {
-    for (int g = 0; g < group && nblocks > 0; ++g) {
+    for (int g = 0; g < run && nblocks > 0; ++g) {
       if (g > 0) {
         qp += (size_t)n_q * D;
         dop += (size_t)n_q * D;
@@ -445,6 +455,26 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16_kernel(BwdArgs a, int n_kti
     }
   }
 
+  if (MODE == 1 || (MODE == 2 && slices > 1)) {
+    // float32 partial sums of this run, added up by the reduction
+    if (key < n_k) {
+      const size_t off = (((size_t)sl * (a.BH / group) + bhkv) * n_k + key) * D;
+#pragma unroll
+      for (int db = 0; db < C::kDB; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          f32x4 rk, rv;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            rk[e] = dk[db][4 * g4 + e] * a.scale;
+            rv[e] = dv[db][4 * g4 + e];
+          }
+          *reinterpret_cast<f32x4*>(a.part_dk + off + 32 * db + 8 * g4 + 4 * hi) = rk;
+          *reinterpret_cast<f32x4*>(a.part_dv + off + 32 * db + 8 * g4 + 4 * hi) = rv;
+        }
+    }
+    return;
+  }
   if (key < n_k) {
     __bf16* dkp = static_cast<__bf16*>(a.dk) + ((size_t)bhkv * n_k + key) * D;
     __bf16* dvp = static_cast<__bf16*>(a.dv) + ((size_t)bhkv * n_k + key) * D;
@@ -651,17 +681,21 @@ __global__ __launch_bounds__(256) void bwd_dkdv_f32_kernel(BwdArgs a, int n_ktil
 
   // One workgroup per (key tile, batch * K/V head), summing over the query
   // heads that share the K/V head.
-  int bhkv, kt;
+  // Work item (key tile, K/V head, run of `run` consecutive query heads).
+  const int run = a.group / a.slices;
+  int hs, kt;
   if (CAUSAL) {
     // the first key tiles are seen by the most queries: they go first
-    costliest_first(blockIdx.x, gridDim.x, n_ktiles, bhkv, kt);
+    costliest_first(blockIdx.x, gridDim.x, n_ktiles, hs, kt);
   } else {
     const int work = xcd_remap(blockIdx.x, gridDim.x);
-    bhkv = work / n_ktiles;
-    kt = work - bhkv * n_ktiles;
+    hs = work / n_ktiles;
+    kt = work - hs * n_ktiles;
   }
+  const int bhkv = hs / a.slices;
+  const int sl = hs - bhkv * a.slices;
   const int h_kv = a.H / a.group;
-  const int bh0 = (bhkv / h_kv) * a.H + (bhkv % h_kv) * a.group;
+  const int bh0 = (bhkv / h_kv) * a.H + (bhkv % h_kv) * a.group + sl * run;
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
@@ -737,7 +771,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_f32_kernel(BwdArgs a, int n_ktil
 #pragma unroll
   for (int db = 0; db < C::kDB; ++db) { dk[db] = f32x16{}; dv[db] = f32x16{}; }
 
-  for (int g = 0; g < a.group; ++g) {
+  for (int g = 0; g < run; ++g) {
   const size_t bh = (size_t)(bh0 + g);
   qp = static_cast<const float*>(a.q) + bh * n_q * D;
   dop = static_cast<const float*>(a.dO) + bh * n_q * D;
@@ -791,8 +825,12 @@ __global__ __launch_bounds__(256) void bwd_dkdv_f32_kernel(BwdArgs a, int n_ktil
   }  // query heads of the group
 
   if (key < n_k) {
-    float* dkp = static_cast<float*>(a.dk) + ((size_t)bhkv * n_k + key) * D;
-    float* dvp = static_cast<float*>(a.dv) + ((size_t)bhkv * n_k + key) * D;
+    // with several runs, float32 partial sums added up by the reduction
+    const bool part = a.slices > 1;
+    const size_t off = part ? (((size_t)sl * (a.BH / a.group) + bhkv) * n_k + key) * D
+                            : ((size_t)bhkv * n_k + key) * D;
+    float* dkp = (part ? a.part_dk : static_cast<float*>(a.dk)) + off;
+    float* dvp = (part ? a.part_dv : static_cast<float*>(a.dv)) + off;
 #pragma unroll
     for (int db = 0; db < C::kDB; ++db)
 #pragma unroll
@@ -958,10 +996,12 @@ hipError_t dkdv_bf16_t(const BwdArgs& a, hipStream_t s) {
   BwdArgs args = a;
   int nt = n_ktiles;
   void* params[] = {&args, &nt};
-  const void* kernel = a.group == 1
-                           ? reinterpret_cast<const void*>(bwd_dkdv_bf16_kernel<D, CAUSAL, false>)
-                           : reinterpret_cast<const void*>(bwd_dkdv_bf16_kernel<D, CAUSAL, true>);
-  return launch_raw(kernel, n_ktiles * (a.BH / a.group), C::kThreads, params, s);
+  // runs of one query head need no head loop (and its registers)
+  const void* kernel =
+      a.group == 1 ? reinterpret_cast<const void*>(bwd_dkdv_bf16_kernel<D, CAUSAL, 0>)
+      : a.group == a.slices ? reinterpret_cast<const void*>(bwd_dkdv_bf16_kernel<D, CAUSAL, 1>)
+                            : reinterpret_cast<const void*>(bwd_dkdv_bf16_kernel<D, CAUSAL, 2>);
+  return launch_raw(kernel, n_ktiles * (a.BH / a.group) * a.slices, C::kThreads, params, s);
 }
 
 template <int D, bool CAUSAL>
@@ -982,7 +1022,7 @@ hipError_t dkdv_f32_t(const BwdArgs& a, hipStream_t s) {
   int nt = n_ktiles;
   void* params[] = {&args, &nt};
   return launch_raw(reinterpret_cast<const void*>(bwd_dkdv_f32_kernel<D, CAUSAL>),
-                    n_ktiles * (a.BH / a.group), F32BwdCfg<D>::kThreads, params, s);
+                    n_ktiles * (a.BH / a.group) * a.slices, F32BwdCfg<D>::kThreads, params, s);
 }
 
 template <int D, bool CAUSAL>
@@ -1009,6 +1049,27 @@ hipError_t preprocess_t(const BwdArgs& a, hipStream_t s) {
   void* params[] = {&o, &g, &lse, &delta, &lse2, &r};
   return hipLaunchKernel(reinterpret_cast<const void*>(bwd_preprocess_kernel<D, TT>),
                          dim3((unsigned)grid), dim3(256), params, 0, s);
+}
+
+// dK, dV = sum over the runs of the float32 partials, in run order (so the
+// result does not depend on scheduling); four values per thread.
+template <typename TO>
+__global__ __launch_bounds__(256) void bwd_reduce_slices_kernel(BwdArgs a, long long n4) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n4) return;
+  const size_t per = (size_t)n4 * 4;  // floats per run
+  f32x4 sk = f32x4{}, sv = f32x4{};
+  for (int r = 0; r < a.slices; ++r) {
+    sk += *reinterpret_cast<const f32x4*>(a.part_dk + r * per + 4 * i);
+    sv += *reinterpret_cast<const f32x4*>(a.part_dv + r * per + 4 * i);
+  }
+  TO* dk = static_cast<TO*>(a.dk) + 4 * i;
+  TO* dv = static_cast<TO*>(a.dv) + 4 * i;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    dk[e] = (TO)sk[e];
+    dv[e] = (TO)sv[e];
+  }
 }
 
 #define FA_DISPATCH_D(fn, d, causal, a, s)                                          \
@@ -1041,6 +1102,15 @@ hipError_t launch_bwd_dkdv_f32(const BwdArgs& a, int d, bool causal, hipStream_t
 }
 hipError_t launch_bwd_dq_f32(const BwdArgs& a, int d, bool causal, hipStream_t s) {
   FA_DISPATCH_D(dq_f32_t, d, causal, a, s)
+}
+hipError_t launch_bwd_reduce_slices(const BwdArgs& a, int d, bool bf16, hipStream_t s) {
+  BwdArgs args = a;
+  long long n4 = (long long)(a.BH / a.group) * a.n_k * d / 4;
+  void* params[] = {&args, &n4};
+  const int grid = (int)((n4 + 255) / 256);
+  return launch_raw(bf16 ? reinterpret_cast<const void*>(bwd_reduce_slices_kernel<__bf16>)
+                         : reinterpret_cast<const void*>(bwd_reduce_slices_kernel<float>),
+                    grid, 256, params, s);
 }
 
 }  // namespace fa

@@ -47,6 +47,13 @@ struct BwdArgs {
   int window;
   float scale;
   float scale_log2;
+  // Shared K/V heads: the group's query heads are split into `slices`
+  // consecutive runs, one dK/dV workgroup per (key tile, K/V head, run); with
+  // more than one run each writes float32 partial sums (slices, B*H_kv, n_k, d)
+  // that a reduction adds up in a fixed order.
+  int slices;
+  float* part_dk;
+  float* part_dv;
 };
 
 // (batch, K/V head) index of the query head bh = b * H + h.  Query heads are
@@ -172,6 +179,8 @@ hipError_t launch_bwd_dkdv_bf16(const BwdArgs& a, int d, bool causal, hipStream_
 hipError_t launch_bwd_dq_bf16(const BwdArgs& a, int d, bool causal, hipStream_t stream);
 hipError_t launch_bwd_dkdv_f32(const BwdArgs& a, int d, bool causal, hipStream_t stream);
 hipError_t launch_bwd_dq_f32(const BwdArgs& a, int d, bool causal, hipStream_t stream);
+// dK, dV (the input dtype) = the sum over the slices of the float32 partials.
+hipError_t launch_bwd_reduce_slices(const BwdArgs& a, int d, bool bf16, hipStream_t stream);
 
 // Key block of the decoding kernel: chunks are whole multiples of it.
 constexpr int kDecodeBlock = 128;

@@ -141,8 +141,15 @@ int fa_forward_gqa(const void* q, const void* k, const void* v, void* o, float* 
 
 /* Backward pass of fa_forward_gqa.  dk and dv are (B,H_kv,n_k,d): the
  * gradient of a shared K/V head is the sum over the query heads of its
- * group (the adjoint of the repetition).  dq, workspace and errors as for
- * fa_backward (the workspace is sized for the H query heads). */
+ * group (the adjoint of the repetition).  So that few K/V heads still give
+ * enough parallel work, a group's query heads may be split into runs whose
+ * float32 partial sums the workspace holds and a final pass adds up in a
+ * fixed order (results are repeatable bit for bit).  The workspace must
+ * hold fa_backward_gqa_workspace_size(B, H, H_kv, n_q, n_k, d, dtype) bytes
+ * (equal to fa_backward_workspace_size when H_kv = H), else
+ * FA_ERR_WORKSPACE; dq and other errors as for fa_backward. */
+size_t fa_backward_gqa_workspace_size(int B, int H, int H_kv, int n_q, int n_k, int d, int dtype);
+
 int fa_backward_gqa(const void* q, const void* k, const void* v, const void* o,
                     const void* dO, const float* lse, void* dq, void* dk, void* dv,
                     void* workspace, size_t workspace_bytes,
@@ -164,7 +171,8 @@ int fa_forward_ext(const void* q, const void* k, const void* v, void* o, float* 
                    int B, int H, int H_kv, int n_q, int n_k, int d, float scale,
                    int causal, int q_offset, int window, int dtype, void* stream);
 
-/* Backward pass of fa_forward_ext (same q_offset and window). */
+/* Backward pass of fa_forward_ext (same q_offset and window); workspace as
+ * for fa_backward_gqa. */
 int fa_backward_ext(const void* q, const void* k, const void* v, const void* o,
                     const void* dO, const float* lse, void* dq, void* dk, void* dv,
                     void* workspace, size_t workspace_bytes,

@@ -226,3 +226,36 @@ def merge(op=P, lp=P2, o=P, lse=P2, n_parts=2, rows=16, d=64, pdt=0, odt=1):
 ])
 def test_lse_merge_rejects(kw, code):
     assert merge(**kw) == code
+
+
+def test_gqa_backward_workspace_size():
+    L = fa.lib()
+    base = L.fa_backward_workspace_size(1, 32, 4096, 4096, 128, 1)
+    # one run per K/V head when there is no sharing
+    assert L.fa_backward_gqa_workspace_size(1, 32, 32, 4096, 4096, 128, 1) == base
+    # one K/V head: each of the 32 query heads is a run of its own, and each
+    # run's float32 partial dK and dV are kept
+    part = 32 * 1 * 4096 * 128 * 4
+    assert L.fa_backward_gqa_workspace_size(1, 32, 1, 4096, 4096, 128, 1) == base + 2 * part
+    # 8 K/V heads, 4 query heads each: 4 runs per K/V head
+    part8 = 4 * 8 * 4096 * 128 * 4
+    assert L.fa_backward_gqa_workspace_size(1, 32, 8, 4096, 4096, 128, 0) == base + 2 * part8
+    assert L.fa_backward_gqa_workspace_size(1, 32, 3, 64, 64, 64, 1) == 0
+
+
+def test_gqa_backward_rejects_a_workspace_without_room_for_the_runs():
+    L = fa.lib()
+    base = L.fa_backward_workspace_size(1, 8, 256, 256, 64, 1)
+    st = L.fa_backward_gqa(P, P, P, P, P, P2, P2, P2, P2, ctypes.c_void_p(0x400000), base,
+                           1, 8, 2, 256, 256, 64, 0.125, 0, 1, None)
+    assert st == fa.FA_ERR_WORKSPACE
+
+
+def test_gqa_runs_grow_when_the_partials_would_pass_4_gib():
+    L = fa.lib()
+    # 64 query heads on one K/V head at n_k = 131072: one-head runs would need
+    # 2 * 64 * 131072 * 128 * 4 B = 8 GiB; runs of two heads need 4 GiB
+    base = L.fa_backward_workspace_size(1, 64, 16, 131072, 128, 1)
+    got = L.fa_backward_gqa_workspace_size(1, 64, 1, 16, 131072, 128, 1)
+    assert got == base + 2 * 32 * 131072 * 128 * 4
+

@@ -109,3 +109,26 @@ def test_gqa_workload_size_sampled_heads(dev):
         ro, rl = oracle.attention_fwd(np64(q[0, h]), np64(k[0, j]), np64(v[0, j]), 1 / math.sqrt(d), True)
         assert_close(f"O head {h}", o[0, h], ro, 2e-2)
         assert_close(f"LSE head {h}", lse[0, h], rl, TOL_LSE)
+
+
+def test_gqa_backward_with_multi_head_runs(dev):
+    # One K/V head for 64 query heads at n_k = 65664: one-head runs would need
+    # more than 4 GiB of partial sums, so the dK/dV workgroups take runs of two
+    # heads (the head-loop variant).  Checked against the sum over heads of the
+    # plain multi-head backward (a separate kernel variant).
+    B, H, n_q, n_k, d = 1, 64, 16, 65664, 128
+    assert fa.lib().fa_backward_gqa_workspace_size(B, H, 1, n_q, n_k, d, 1) < \
+        fa.backward_workspace_size(B, H, n_q, n_k, d, torch.bfloat16) + 2 * 64 * n_k * d * 4
+    q, k, v, do = draw(3300, B, H, 1, n_q, n_k, d, torch.bfloat16)
+    qd, kd, vd, dod = (t.to(dev) for t in (q, k, v, do))
+    o, lse = fa.forward(qd, kd, vd)
+    dq, dk, dv = fa.backward(qd, kd, vd, o, dod, lse)
+    ke, ve = kd.expand(B, H, n_k, d).contiguous(), vd.expand(B, H, n_k, d).contiguous()
+    dq2, dke, dve = fa.backward(qd, ke, ve, o, dod, lse)
+    torch.cuda.synchronize()
+    assert torch.equal(dq, dq2)
+    for name, got, per_head in (("dK", dk, dke), ("dV", dv, dve)):
+        ref = per_head.float().sum(1, keepdim=True)
+        mag = per_head.float().abs().sum(1, keepdim=True)
+        assert_close(f"{name} runs of two heads", got.float().cpu(), np64(ref.cpu()), 1e-3, RTOL_BF16_TERMS,
+                     mag=np64(mag.cpu()))
