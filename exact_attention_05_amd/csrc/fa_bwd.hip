@@ -178,6 +178,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16_kernel(BwdArgs a, int n_kti
 
   // Query stages holding rows that see some key of this workgroup.
   const Band band = band_of(a, CAUSAL);
+  int qvlo, qvspan;  // rows that see this lane's key: [qvlo, qvlo + qvspan]
+  band.query_range(key, qvlo, qvspan);
   const int k1 = min(n_k, k0 + C::kBK);
   const int q_first = band.q_lo(k0), q_last = band.q_hi(k1);
   const int qb_first = q_first / C::kBQ;
@@ -232,8 +234,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16_kernel(BwdArgs a, int n_kti
     const int g4 = i >> 2, e = i & 3;
     float p = fast_exp2(fmaf(s[i], sl2, -lv[g4][e]));
     if constexpr (decltype(mask_tag)::value) {
-      const int q = qrow0 + 8 * g4 + 4 * hi + e;
-      if (q >= n_q || band.hidden(q, key)) p = 0.f;
+      if (!Band::in_range(qrow0 + 4 * hi - qvlo + 8 * g4 + e, 0, qvspan)) p = 0.f;
     }
     ex[i] = p;
     dd[i] = dp[i] - dl[g4][e];
@@ -565,6 +566,8 @@ __global__ __launch_bounds__(512) void bwd_dq_bf16_kernel(BwdArgs a, int n_qtile
   const int t_hi = max(t_lo, (band.key_hi(q_end) + C::kBN - 1) / C::kBN);
   const int f_lo = min(t_hi, max(t_lo, (band.key_full_lo(q_end) + C::kBN - 1) / C::kBN));
   const int f_hi = max(f_lo, min(t_hi, band.key_full_hi(q0) / C::kBN));
+  int vlo, vspan;  // keys this lane's query sees: [vlo, vlo + vspan]
+  band.key_range(qi, vlo, vspan);
 
   TileDma<D, C::kBN, C::kWaves> dma;
   dma.init(wave, lane);
@@ -606,9 +609,9 @@ __global__ __launch_bounds__(512) void bwd_dq_bf16_kernel(BwdArgs a, int n_qtile
         float p0 = fast_exp2(fmaf(s[i], sl2, -lse2));
         float p1 = fast_exp2(fmaf(s[i + 1], sl2, -lse2));
         if constexpr (MASK) {
-          const int kj = k0 + kb * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
-          if (band.hidden(qi, kj)) p0 = 0.f;
-          if (band.hidden(qi, kj + 1)) p1 = 0.f;
+          const int rel = k0 + kb * 32 + 4 * hi - vlo + 8 * (i >> 2) + (i & 3);  // key - vlo
+          if (!Band::in_range(rel, 0, vspan)) p0 = 0.f;
+          if (!Band::in_range(rel + 1, 0, vspan)) p1 = 0.f;
         }
         dsb[i >> 3][(i & 7) >> 1] = pack_bf16x2(p0 * (dp[i] - dlt), p1 * (dp[i + 1] - dlt));
       }

@@ -118,6 +118,8 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecArgs a) {
   const int n_steps = max(0, (s_hi - s_lo - wave + C::kWaves - 1) / C::kWaves);
   const int full_lo = band.key_full_lo(i_hi);
   const int full_hi = band.key_full_hi(i_lo);
+  int vlo, vspan;  // keys this lane's query sees: [vlo, vlo + vspan]
+  band.key_range(qi, vlo, vspan);
 
   // Global -> register loads of one step (row-major 16-byte pieces, each
   // lane's piece at the same place in every row group), then register -> LDS
@@ -164,10 +166,8 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecArgs a) {
     for (int c = 0; c < C::kDC; ++c) s = mfma_bf16(T::read_rows(kt, 0, c, lane), qf[c], s);
     if (masked) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = k0 + 8 * (i >> 2) + 4 * hi + (i & 3);
-        if (band.hidden(qi, key)) s[i] = -INFINITY;
-      }
+      for (int i = 0; i < 16; ++i)
+        if (!Band::in_range(k0 + 4 * hi - vlo + 8 * (i >> 2) + (i & 3), 0, vspan)) s[i] = -INFINITY;
     }
     float mx = -INFINITY;
 #pragma unroll

@@ -116,6 +116,8 @@ void fwd_bf16_kernel(FwdArgs a, int n_qtiles) {
   const int t_hi = max(t_lo, (band.key_hi(q_end) + C::kBN - 1) / C::kBN);
   const int f_lo = min(t_hi, max(t_lo, (band.key_full_lo(q_end) + C::kBN - 1) / C::kBN));
   const int f_hi = max(f_lo, min(t_hi, band.key_full_hi(q0) / C::kBN));
+  int vlo, vspan;  // keys this lane's query sees: [vlo, vlo + vspan]
+  band.key_range(qi, vlo, vspan);
 
   TileDma<D, C::kBN, C::kWaves> dma;
   dma.init(wave, lane);
@@ -172,15 +174,14 @@ void fwd_bf16_kernel(FwdArgs a, int n_qtiles) {
 
     __builtin_amdgcn_s_setprio(0);
     if constexpr (MASK) {
-      // Hidden entries (key past the end, or after the query when causal)
-      // leave the maximum alone and get probability 0.
+      // Hidden entries (key past the end, after the query when causal,
+      // outside the window) leave the maximum alone and get probability 0.
+      const int rel = k0 + 4 * hi - vlo;  // key - vlo of element 0
 #pragma unroll
       for (int kb = 0; kb < C::kKB; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = k0 + kb * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
-          if (band.hidden(qi, key)) s[kb][i] = -INFINITY;
-        }
+        for (int i = 0; i < 16; ++i)
+          if (!Band::in_range(rel + kb * 32 + 8 * (i >> 2) + (i & 3), 0, vspan)) s[kb][i] = -INFINITY;
     }
     // Row maximum of the block (raw scores), then the lazy reference update.
     float mx = -INFINITY;
@@ -372,6 +373,8 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdArgs a, int n_qtiles) {
   const int q_end = min(n_q, q0 + C::kBM);
   const int t_lo = band.key_lo(q0) / C::kBN;
   const int t_hi = max(t_lo, (band.key_hi(q_end) + C::kBN - 1) / C::kBN);
+  int vlo, vspan;  // keys this lane's query sees: [vlo, vlo + vspan]
+  band.key_range(qi, vlo, vspan);
   // Keys every row of this wave sees.
   const int wfull_lo = band.key_full_lo(qw + 32), wfull_hi = band.key_full_hi(qw);
 
@@ -434,8 +437,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdArgs a, int n_qtiles) {
       uint32_t bits = 0;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int key = k0 + 8 * (i >> 2) + 4 * hi + (i & 3);
-        const bool h = band.hidden(qi, key);
+        const bool h = !Band::in_range(k0 + 4 * hi - vlo + 8 * (i >> 2) + (i & 3), 0, vspan);
         bits |= (h ? 1u : 0u) << i;
       }
       alpha = softmax_block<1, true>(s, m, l, a.scale_log2, &bits);

@@ -98,6 +98,37 @@ struct Band {
     if (window >= 0) h = min(h, r0 + q_offset + window + 1);
     return max(h, 0);
   }
+  // The keys row q sees as one interval [lo, lo + span]: key is visible iff
+  // (unsigned)(key - lo) <= (unsigned)span -- one subtraction and one
+  // comparison per element in the kernels.  A row that sees nothing gets
+  // lo = 2^30, span = 0 (every index here is below 2^30).
+  __host__ __device__ void key_range(int q, int& lo, int& span) const {
+    const int p = q + q_offset;
+    int l = 0, h = n_k - 1;
+    if (causal) h = min(h, p);
+    if (window >= 0) {
+      l = max(l, p - window);
+      h = min(h, p + window);
+    }
+    lo = h < l ? (1 << 30) : l;
+    span = h < l ? 0 : h - l;
+  }
+  // The rows that see key as one interval, the same way (a key past n_k is
+  // seen by none).
+  __host__ __device__ void query_range(int key, int& lo, int& span) const {
+    int l = 0, h = n_q - 1;
+    if (causal) l = max(l, key - q_offset);
+    if (window >= 0) {
+      l = max(l, key - q_offset - window);
+      h = min(h, key - q_offset + window);
+    }
+    if (key >= n_k) h = -1;
+    lo = h < l ? (1 << 30) : l;
+    span = h < l ? 0 : h - l;
+  }
+  __host__ __device__ static bool in_range(int x, int lo, int span) {
+    return (unsigned)(x - lo) <= (unsigned)span;
+  }
   // Query rows that see some key of [k0, k1) (k0 < k1 <= n_k).
   __host__ __device__ int q_lo(int k0) const {
     int l = 0;
