@@ -63,6 +63,12 @@ struct Bf16FwdCfg {
 // the reference (and the rescaling of the output) only changes when a block
 // raises the row maximum by more than this.
 constexpr float kLazyRescale = 8.0f;
+// Largest sum of one lane's probabilities in a block accepted without
+// looking at the block maximum.  Below it every probability is at most
+// 2^16, so the fp32 output and row sum cannot overflow; a block whose
+// maximum stays within kLazyRescale of the reference never exceeds it
+// (32 values of at most 2^8), so passing it always moves the reference.
+constexpr float kFastSum = 65536.0f;
 
 template <int D, bool CAUSAL, int WAVES>
 __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -159,20 +165,70 @@ void fwd_bf16_kernel(FwdArgs a, int n_qtiles) {
     // priority: of the two waves on a SIMD, the one still issuing matrix
     // operations wins the issue port, so one wave's softmax overlaps the
     // other's products instead of both waves alternating in lock step.
-    __builtin_amdgcn_s_setprio(1);
-    // S^T = K Q^T for kBN keys x 32 queries.
     f32x16 s[C::kKB];
+    auto scores = [&]() __attribute__((always_inline)) {
+      // S^T = K Q^T for kBN keys x 32 queries.
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-    for (int kb = 0; kb < C::kKB; ++kb) s[kb] = f32x16{};
+      for (int kb = 0; kb < C::kKB; ++kb) s[kb] = f32x16{};
 #pragma unroll
-    for (int c = 0; c < C::kDC; ++c) {
+      for (int c = 0; c < C::kDC; ++c) {
 #pragma unroll
-      for (int kb = 0; kb < C::kKB; ++kb) {
-        s[kb] = mfma_bf16(C::KV::read_rows(ks, kb * 32, c, lane), qf[c], s[kb]);
+        for (int kb = 0; kb < C::kKB; ++kb) {
+          s[kb] = mfma_bf16(C::KV::read_rows(ks, kb * 32, c, lane), qf[c], s[kb]);
+        }
       }
-    }
+      __builtin_amdgcn_s_setprio(0);
+    };
+    // Row maximum of the block (raw scores), then the lazy reference update.
+    auto raise_ref = [&]() __attribute__((always_inline)) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < C::kKB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(s[kb][i], s[kb][i + 1]));
+      mx = max_halves(mx);
+      const float mt = (mx == -INFINITY) ? -INFINITY : mx * sl2;
+      if (__builtin_amdgcn_ballot_w64(mt > m + kLazyRescale) != 0) {
+        const float m_new = fmaxf(m, mt);
+        const float ref = (m_new == -INFINITY) ? 0.f : m_new;
+        const float alpha = fast_exp2(m - ref);
+        l *= alpha;
+#pragma unroll
+        for (int db = 0; db < C::kDB; ++db) oacc[db] *= alpha;
+        m = m_new;
+      }
+    };
+    // P = exp2(scale_log2 * S - ref), rounded to bf16 as the B operand of
+    // the P V product; returns the lane's sum of the unrounded values (the
+    // LSE needs them: a sum of bf16-rounded terms is off by up to 2^-9).
+    u32x4 pw[C::kKB][2];
+    auto probs = [&]() __attribute__((always_inline)) -> float {
+      const float ref = (m == -INFINITY) ? 0.f : m;
+      float rs0 = 0.f, rs1 = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < C::kKB; ++kb)
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2) {
+#pragma unroll
+          for (int e = 0; e < 8; e += 2) {
+            float p0 = fast_exp2(fmaf(s[kb][8 * c2 + e], sl2, -ref));
+            float p1 = fast_exp2(fmaf(s[kb][8 * c2 + e + 1], sl2, -ref));
+            if constexpr (MASK) {
+              // exp2(-inf) is 0 already unless the scale is 0.
+              if (s[kb][8 * c2 + e] == -INFINITY) p0 = 0.f;
+              if (s[kb][8 * c2 + e + 1] == -INFINITY) p1 = 0.f;
+            }
+            pw[kb][c2][e >> 1] = pack_bf16x2(p0, p1);
+            rs0 += p0;
+            rs1 += p1;
+          }
+        }
+      return rs0 + rs1;
+    };
 
-    __builtin_amdgcn_s_setprio(0);
+    scores();
+    float rs;
     if constexpr (MASK) {
       // Hidden entries (key past the end, after the query when causal,
       // outside the window) leave the maximum alone and get probability 0.
@@ -182,50 +238,21 @@ void fwd_bf16_kernel(FwdArgs a, int n_qtiles) {
 #pragma unroll
         for (int i = 0; i < 16; ++i)
           if (!Band::in_range(rel + kb * 32 + 8 * (i >> 2) + (i & 3), 0, vspan)) s[kb][i] = -INFINITY;
-    }
-    // Row maximum of the block (raw scores), then the lazy reference update.
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < C::kKB; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(s[kb][i], s[kb][i + 1]));
-    mx = max_halves(mx);
-    const float mt = (mx == -INFINITY) ? -INFINITY : mx * sl2;
-    if (__builtin_amdgcn_ballot_w64(mt > m + kLazyRescale) != 0) {
-      const float m_new = fmaxf(m, mt);
-      const float ref = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = fast_exp2(m - ref);
-      l *= alpha;
-#pragma unroll
-      for (int db = 0; db < C::kDB; ++db) oacc[db] *= alpha;
-      m = m_new;
-    }
-    const float ref = (m == -INFINITY) ? 0.f : m;
-
-    // P = exp2(scale_log2 * S - ref), rounded to bf16 as the B operand of
-    // the P V product.  The row sum l adds the unrounded float values: the
-    // LSE needs them (a sum of bf16-rounded terms is off by up to 2^-9).
-    u32x4 pw[C::kKB][2];
-    float rs0 = 0.f, rs1 = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < C::kKB; ++kb)
-#pragma unroll
-      for (int c2 = 0; c2 < 2; ++c2) {
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          float p0 = fast_exp2(fmaf(s[kb][8 * c2 + e], sl2, -ref));
-          float p1 = fast_exp2(fmaf(s[kb][8 * c2 + e + 1], sl2, -ref));
-          if constexpr (MASK) {
-            // exp2(-inf) is 0 already unless the scale is 0.
-            if (s[kb][8 * c2 + e] == -INFINITY) p0 = 0.f;
-            if (s[kb][8 * c2 + e + 1] == -INFINITY) p1 = 0.f;
-          }
-          pw[kb][c2][e >> 1] = pack_bf16x2(p0, p1);
-          rs0 += p0;
-          rs1 += p1;
-        }
+      raise_ref();
+      rs = probs();
+    } else {
+      // Without a mask the block maximum is needed only when the reference
+      // must move: exponentiate against the current one, and only if some
+      // lane's sum passes kFastSum (so might a probability) or a row has no
+      // reference yet, recompute the scores, raise the reference and redo.
+      rs = probs();
+      if (__builtin_amdgcn_ballot_w64(!(rs <= kFastSum) || m == -INFINITY) != 0) {
+        scores();
+        raise_ref();
+        rs = probs();
       }
-    l += rs0 + rs1;
+    }
+    l += rs;
 
     // O^T += V^T P^T, 16 keys per matrix-core step.
     __builtin_amdgcn_s_setprio(1);
