@@ -187,6 +187,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16_kernel(BwdArgs a, int n_kti
 
   TileDma<D, C::kBQ, C::kWaves> dma;
   dma.init(wave, lane);
+  TileLane<D, C::kBQ> tqt;
+  tqt.init(lane);
   const uint32_t sq_addr = lds_address(&sq[0][0]);
   const uint32_t sdo_addr = lds_address(&sdo[0][0]);
   const uint32_t slse_addr = lds_address(&slse[0][0]);
@@ -275,8 +277,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16_kernel(BwdArgs a, int n_kti
     s = f32x16{};
     dp = f32x16{};
     static_for<0, (C::kS1 < C::kAhead ? C::kS1 : C::kAhead)>([&](auto i) __attribute__((always_inline)) {
-      fa[decltype(i)::value] = C::QT::read_rows(qt, R0, decltype(i)::value, lane);
-      fb[decltype(i)::value] = C::QT::read_rows(gt, R0, decltype(i)::value, lane);
+      fa[decltype(i)::value] = tqt.read_rows(qt, R0, decltype(i)::value);
+      fb[decltype(i)::value] = tqt.read_rows(gt, R0, decltype(i)::value);
     });
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
@@ -286,8 +288,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16_kernel(BwdArgs a, int n_kti
     static_for<0, C::kS1>([&](auto c_tag) __attribute__((always_inline)) {
       constexpr int c = decltype(c_tag)::value;
       if constexpr (c + C::kAhead < C::kS1) {
-        fa[(c + C::kAhead) % C::kRing] = C::QT::read_rows(qt, R0, c + C::kAhead, lane);
-        fb[(c + C::kAhead) % C::kRing] = C::QT::read_rows(gt, R0, c + C::kAhead, lane);
+        fa[(c + C::kAhead) % C::kRing] = tqt.read_rows(qt, R0, c + C::kAhead);
+        fb[(c + C::kAhead) % C::kRing] = tqt.read_rows(gt, R0, c + C::kAhead);
       }
       s = mfma_bf16(fa[c % C::kRing], kf[c], s);
       dp = mfma_bf16(fb[c % C::kRing], vf[c], dp);
@@ -297,8 +299,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16_kernel(BwdArgs a, int n_kti
       if constexpr (c == C::kS1 - 1) {
         static_for<0, (C::kS2 < C::kAhead ? C::kS2 : C::kAhead)>([&](auto i) __attribute__((always_inline)) {
           constexpr int f = decltype(i)::value;
-          fa[f] = C::QT::read_cols_tr(sdo[BP], RP + 16 * (f / C::kDB), 32 * (f % C::kDB), lane);
-          fb[f] = C::QT::read_cols_tr(sq[BP], RP + 16 * (f / C::kDB), 32 * (f % C::kDB), lane);
+          fa[f] = tqt.read_cols_tr(sdo[BP], RP + 16 * (f / C::kDB), 32 * (f % C::kDB));
+          fb[f] = tqt.read_cols_tr(sq[BP], RP + 16 * (f / C::kDB), 32 * (f % C::kDB));
         });
       }
       step_order();
@@ -308,8 +310,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16_kernel(BwdArgs a, int n_kti
       constexpr int c2 = f / C::kDB, db = f % C::kDB;
       if constexpr (f + C::kAhead < C::kS2) {
         constexpr int g = f + C::kAhead;
-        fa[g % C::kRing] = C::QT::read_cols_tr(sdo[BP], RP + 16 * (g / C::kDB), 32 * (g % C::kDB), lane);
-        fb[g % C::kRing] = C::QT::read_cols_tr(sq[BP], RP + 16 * (g / C::kDB), 32 * (g % C::kDB), lane);
+        fa[g % C::kRing] = tqt.read_cols_tr(sdo[BP], RP + 16 * (g / C::kDB), 32 * (g % C::kDB));
+        fb[g % C::kRing] = tqt.read_cols_tr(sq[BP], RP + 16 * (g / C::kDB), 32 * (g % C::kDB));
       }
       dv[db] = mfma_bf16(fa[f % C::kRing], bf16x8_of(pb[c2]), dv[db]);
       dk[db] = mfma_bf16(fb[f % C::kRing], bf16x8_of(dsb[c2]), dk[db]);
@@ -377,8 +379,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16_kernel(BwdArgs a, int n_kti
       dp = f32x16{};
 #pragma unroll
       for (int c = 0; c < C::kDC; ++c) {
-        s = mfma_bf16(C::QT::read_rows(qt, r0, c, lane), kf[c], s);
-        dp = mfma_bf16(C::QT::read_rows(gt, r0, c, lane), vf[c], dp);
+        s = mfma_bf16(tqt.read_rows(qt, r0, c), kf[c], s);
+        dp = mfma_bf16(tqt.read_rows(gt, r0, c), vf[c], dp);
       }
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
@@ -391,8 +393,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16_kernel(BwdArgs a, int n_kti
 #pragma unroll
       for (int f = 0; f < C::kS2; ++f) {
         const int c2 = f / C::kDB, db = f % C::kDB;
-        dv[db] = mfma_bf16(C::QT::read_cols_tr(gt, r0 + 16 * c2, 32 * db, lane), bf16x8_of(pb[c2]), dv[db]);
-        dk[db] = mfma_bf16(C::QT::read_cols_tr(qt, r0 + 16 * c2, 32 * db, lane), bf16x8_of(dsb[c2]), dk[db]);
+        dv[db] = mfma_bf16(tqt.read_cols_tr(gt, r0 + 16 * c2, 32 * db), bf16x8_of(pb[c2]), dv[db]);
+        dk[db] = mfma_bf16(tqt.read_cols_tr(qt, r0 + 16 * c2, 32 * db), bf16x8_of(dsb[c2]), dk[db]);
       }
     }
   };
@@ -405,8 +407,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16_kernel(BwdArgs a, int n_kti
 #pragma unroll
     for (int f = 0; f < C::kS2; ++f) {
       const int c2 = f / C::kDB, db = f % C::kDB;
-      dv[db] = mfma_bf16(C::QT::read_cols_tr(sdo[BUF], 32 + 16 * c2, 32 * db, lane), bf16x8_of(pb[c2]), dv[db]);
-      dk[db] = mfma_bf16(C::QT::read_cols_tr(sq[BUF], 32 + 16 * c2, 32 * db, lane), bf16x8_of(dsb[c2]), dk[db]);
+      dv[db] = mfma_bf16(tqt.read_cols_tr(sdo[BUF], 32 + 16 * c2, 32 * db), bf16x8_of(pb[c2]), dv[db]);
+      dk[db] = mfma_bf16(tqt.read_cols_tr(sq[BUF], 32 + 16 * c2, 32 * db), bf16x8_of(dsb[c2]), dk[db]);
     }
   };
 
@@ -571,6 +573,8 @@ __global__ __launch_bounds__(512) void bwd_dq_bf16_kernel(BwdArgs a, int n_qtile
 
   TileDma<D, C::kBN, C::kWaves> dma;
   dma.init(wave, lane);
+  TileLane<D, C::kBN> tkv;
+  tkv.init(lane);
   const uint32_t sk_addr = lds_address(&sk[0][0]);
   const uint32_t sv_addr = lds_address(&sv[0][0]);
   auto load_tile = [&](int t, int buf) {
@@ -600,8 +604,8 @@ __global__ __launch_bounds__(512) void bwd_dq_bf16_kernel(BwdArgs a, int n_qtile
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
       for (int c = 0; c < C::kDC; ++c) {
-        s = mfma_bf16(C::KV::read_rows(ks, kb * 32, c, lane), qf[c], s);
-        dp = mfma_bf16(C::KV::read_rows(vs, kb * 32, c, lane), gf[c], dp);
+        s = mfma_bf16(tkv.read_rows(ks, kb * 32, c), qf[c], s);
+        dp = mfma_bf16(tkv.read_rows(vs, kb * 32, c), gf[c], dp);
       }
       u32x4 dsb[2];
 #pragma unroll
@@ -619,7 +623,7 @@ __global__ __launch_bounds__(512) void bwd_dq_bf16_kernel(BwdArgs a, int n_qtile
       for (int c2 = 0; c2 < 2; ++c2)
 #pragma unroll
         for (int db = 0; db < C::kDB; ++db)
-          dq[db] = mfma_bf16(C::KV::read_cols_tr(ks, kb * 32 + 16 * c2, 32 * db, lane),
+          dq[db] = mfma_bf16(tkv.read_cols_tr(ks, kb * 32 + 16 * c2, 32 * db),
                              bf16x8_of(dsb[c2]), dq[db]);
     }
   };

@@ -140,6 +140,8 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecArgs a) {
   };
   char* const kt = smem + wave * 2 * T::kBytes;
   char* const vt = kt + T::kBytes;
+  TileLane<D, C::kSub> tl;
+  tl.init(lane);
   auto stage = [&](auto slot) __attribute__((always_inline)) {
     constexpr int S = decltype(slot)::value;
 #pragma unroll
@@ -163,7 +165,7 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecArgs a) {
     const bool masked = k0 < full_lo || k0 + C::kSub > full_hi;
     f32x16 s = f32x16{};
 #pragma unroll
-    for (int c = 0; c < C::kDC; ++c) s = mfma_bf16(T::read_rows(kt, 0, c, lane), qf[c], s);
+    for (int c = 0; c < C::kDC; ++c) s = mfma_bf16(tl.read_rows(kt, 0, c), qf[c], s);
     if (masked) {
 #pragma unroll
       for (int i = 0; i < 16; ++i)
@@ -202,7 +204,7 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecArgs a) {
     for (int c2 = 0; c2 < 2; ++c2)
 #pragma unroll
       for (int db = 0; db < C::kDB; ++db)
-        oacc[db] = mfma_bf16(T::read_cols_tr(vt, 16 * c2, 32 * db, lane), bf16x8_of(pw[c2]), oacc[db]);
+        oacc[db] = mfma_bf16(tl.read_cols_tr(vt, 16 * c2, 32 * db), bf16x8_of(pw[c2]), oacc[db]);
     settle_acc(oacc);
   };
 

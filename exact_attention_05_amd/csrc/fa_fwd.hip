@@ -11,8 +11,10 @@
 // query rows) and owns 32 consecutive query rows of one (batch, head) per
 // wave.  Key and value blocks of 64 rows stream
 // through double-buffered LDS by direct global -> LDS copies: the copies of
-// block t+1 are in flight while block t is computed, and one barrier per
-// block separates the two buffers.
+// block t+1 (in the pipelined path: K of block t+2, V of block t+1) are in
+// flight while block t is computed, and one barrier per block separates the
+// two buffers.  LDS addresses are a per-lane constant XOR the operand's
+// chunk offset (TileLane).
 //
 // The wave computes the transposed score tile S^T = K Q^T on the
 // 32x32x16 bf16 matrix cores, with K read from LDS as the A operand and Q
@@ -29,8 +31,11 @@
 // workgroups of one head run on the same XCD and share its L2; with the
 // causal mask the longest query tiles are issued first.  A workgroup visits
 // only the key blocks some of its rows see (causal mask, query offset,
-// sliding window; see Band); blocks that every row sees entirely run through
-// an unmasked code path, two at a time with fixed LDS buffers.
+// sliding window; see Band).  Blocks that every row sees entirely run
+// through an unmasked, software-pipelined path (fixed LDS buffers, two
+// blocks per loop turn): the score products of block t+1 are issued in the
+// same instruction stream as the exponentials of block t, and those blocks
+// skip the block maximum unless the probabilities grow too large.
 //
 // fp32 kernel
 // -----------
@@ -127,6 +132,8 @@ void fwd_bf16_kernel(FwdArgs a, int n_qtiles) {
 
   TileDma<D, C::kBN, C::kWaves> dma;
   dma.init(wave, lane);
+  TileLane<D, C::kBN> tl;
+  tl.init(lane);
   const uint32_t sk_addr = lds_address(&sk[0][0]);
   const uint32_t sv_addr = lds_address(&sv[0][0]);
   auto load_tile = [&](int t, int buf) {
@@ -175,7 +182,7 @@ void fwd_bf16_kernel(FwdArgs a, int n_qtiles) {
       for (int c = 0; c < C::kDC; ++c) {
 #pragma unroll
         for (int kb = 0; kb < C::kKB; ++kb) {
-          s[kb] = mfma_bf16(C::KV::read_rows(ks, kb * 32, c, lane), qf[c], s[kb]);
+          s[kb] = mfma_bf16(tl.read_rows(ks, kb * 32, c), qf[c], s[kb]);
         }
       }
       __builtin_amdgcn_s_setprio(0);
@@ -262,7 +269,7 @@ void fwd_bf16_kernel(FwdArgs a, int n_qtiles) {
       for (int c2 = 0; c2 < 2; ++c2)
 #pragma unroll
         for (int db = 0; db < C::kDB; ++db)
-          oacc[db] = mfma_bf16(C::KV::read_cols_tr(vs, kb * 32 + 16 * c2, 32 * db, lane),
+          oacc[db] = mfma_bf16(tl.read_cols_tr(vs, kb * 32 + 16 * c2, 32 * db),
                                bf16x8_of(pw[kb][c2]), oacc[db]);
     __builtin_amdgcn_s_setprio(0);
   };
@@ -276,15 +283,118 @@ void fwd_bf16_kernel(FwdArgs a, int n_qtiles) {
   if (t_lo < t_hi) load_tile(t_lo, t_lo & 1);
   int t = t_lo;
   for (; t < f_lo; ++t) block(T{}, BR{}, t);
-  if (t < f_hi && (t & 1)) {
-    block(F{}, BR{}, t);
+
+  // Unmasked blocks, software-pipelined inside each wave: iteration t
+  // issues the score products of block t+1 while the vector unit
+  // exponentiates block t, then adds block t's P V.  K runs one block ahead
+  // of V through the same two buffers (K_t, V_t in buffer t % 2): at
+  // iteration t's barrier K_{t+1} and V_t have landed, and the copies of
+  // K_{t+2} and V_{t+1} start.
+  if (f_lo < f_hi) {
+    f32x16 sc[C::kKB], sn[C::kKB];
+    auto pscores = [&](const char* ks, f32x16 (&s)[C::kKB]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int kb = 0; kb < C::kKB; ++kb) s[kb] = f32x16{};
+#pragma unroll
+      for (int c = 0; c < C::kDC; ++c)
+#pragma unroll
+        for (int kb = 0; kb < C::kKB; ++kb)
+          s[kb] = mfma_bf16(tl.read_rows(ks, kb * 32, c), qf[c], s[kb]);
+    };
+    auto pprobs = [&](u32x4 (&pw)[C::kKB][2]) __attribute__((always_inline)) -> float {
+      const float ref = (m == -INFINITY) ? 0.f : m;
+      float rs0 = 0.f, rs1 = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < C::kKB; ++kb)
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+          for (int e = 0; e < 8; e += 2) {
+            const float p0 = fast_exp2(fmaf(sc[kb][8 * c2 + e], sl2, -ref));
+            const float p1 = fast_exp2(fmaf(sc[kb][8 * c2 + e + 1], sl2, -ref));
+            pw[kb][c2][e >> 1] = pack_bf16x2(p0, p1);
+            rs0 += p0;
+            rs1 += p1;
+          }
+      return rs0 + rs1;
+    };
+    auto praise = [&]() __attribute__((always_inline)) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < C::kKB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(sc[kb][i], sc[kb][i + 1]));
+      mx = max_halves(mx);
+      const float mt = mx * sl2;
+      if (__builtin_amdgcn_ballot_w64(mt > m + kLazyRescale) != 0) {
+        const float m_new = fmaxf(m, mt);
+        const float alpha = fast_exp2(m - m_new);
+        l *= alpha;
+#pragma unroll
+        for (int db = 0; db < C::kDB; ++db) oacc[db] *= alpha;
+        m = m_new;
+      }
+    };
+    auto iter = [&](auto buf_tag, auto next_tag, int t) __attribute__((always_inline)) {
+      constexpr int B = decltype(buf_tag)::value;
+      constexpr bool NEXT = decltype(next_tag)::value;
+      wait_lds_dma();
+      __syncthreads();
+      if (NEXT && t + 2 < t_hi) {
+        const int k2 = (t + 2) * C::kBN;
+        dma.load(kp + (size_t)k2 * D, n_k - k2, sk_addr + B * C::KV::kBytes);
+      }
+      if (t + 1 < t_hi) {
+        const int k1 = (t + 1) * C::kBN;
+        dma.load(vp + (size_t)k1 * D, n_k - k1, sv_addr + (B ^ 1) * C::KV::kBytes);
+      }
+      if constexpr (NEXT) pscores(sk[B ^ 1], sn);
+      u32x4 pw[C::kKB][2];
+      float rs = pprobs(pw);
+      if (__builtin_amdgcn_ballot_w64(!(rs <= kFastSum) || m == -INFINITY) != 0) {
+        praise();
+        rs = pprobs(pw);
+      }
+      l += rs;
+#pragma unroll
+      for (int kb = 0; kb < C::kKB; ++kb)
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+          for (int db = 0; db < C::kDB; ++db)
+            oacc[db] = mfma_bf16(tl.read_cols_tr(sv[B], kb * 32 + 16 * c2, 32 * db),
+                                 bf16x8_of(pw[kb][c2]), oacc[db]);
+      if constexpr (NEXT) {
+#pragma unroll
+        for (int kb = 0; kb < C::kKB; ++kb) sc[kb] = sn[kb];
+      }
+    };
+    // Prologue: K_{f_lo} and V_{f_lo} were started by the previous block (or
+    // the first load); start K_{f_lo + 1} and compute block f_lo's scores.
+    wait_lds_dma();
+    __syncthreads();
+    if (f_lo + 1 < t_hi) {
+      const int k1 = (f_lo + 1) * C::kBN;
+      dma.load(kp + (size_t)k1 * D, n_k - k1, sk_addr + ((f_lo + 1) & 1) * C::KV::kBytes);
+    }
+    pscores(sk[f_lo & 1], sc);
+    using B0 = std::integral_constant<int, 0>;
+    using B1 = std::integral_constant<int, 1>;
+    if (t < f_hi - 1 && (t & 1)) {
+      iter(B1{}, T{}, t);
+      ++t;
+    }
+    for (; t + 1 < f_hi - 1; t += 2) {
+      iter(B0{}, T{}, t);
+      iter(B1{}, T{}, t + 1);
+    }
+    if (t < f_hi - 1) {
+      iter(B0{}, T{}, t);
+      ++t;
+    }
+    if (t & 1) iter(B1{}, F{}, t); else iter(B0{}, F{}, t);
     ++t;
   }
-  for (; t + 1 < f_hi; t += 2) {
-    block(F{}, std::integral_constant<int, 0>{}, t);
-    block(F{}, std::integral_constant<int, 1>{}, t + 1);
-  }
-  for (; t < f_hi; ++t) block(F{}, BR{}, t);
   for (; t < t_hi; ++t) block(T{}, BR{}, t);
 
   // Epilogue: normalise, store O (bf16) and LSE (natural log).  A row that

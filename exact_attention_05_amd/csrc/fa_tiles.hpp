@@ -71,6 +71,41 @@ struct Tile {
   }
 };
 
+// The same two operand reads with the lane's part of the address computed
+// once.  The swizzle XORs chunk bits that lie below one row, so
+//   offset(row, chunk) = (row * kRowBytes + 16 chunk) ^ (16 swizzle(row)),
+// and for a row block starting at a multiple of 16 rows (the swizzle period)
+// and a chunk split into a lane part and a multiple of the lane part's range,
+// the address is the block's row offset plus (lane constant ^ chunk part):
+// one XOR per read instead of a per-read register or recomputation.
+template <int D, int ROWS>
+struct TileLane {
+  using T = Tile<D, ROWS>;
+  int rows;   // read_rows: lane part for row0 = 0, c = 0
+  int tr0;    // read_cols_tr, first 8 bytes: lane part for r0 = 0, col0 = 0
+  int tr1;    // second 8 bytes (rows + 8)
+
+  __device__ __forceinline__ void init(int lane) {
+    rows = T::offset(lane & 31, lane >> 5);
+    const int row = 4 * (lane >> 5) + ((lane & 15) >> 2);
+    const int col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    tr0 = T::offset(row, col >> 3) + 2 * (col & 7);
+    tr1 = T::offset(row + 8, col >> 3) + 2 * (col & 7);
+  }
+  // read_rows(tile, row0, c, lane) for row0 a multiple of 32.
+  __device__ __forceinline__ bf16x8 read_rows(const char* tile, int row0, int c) const {
+    return *reinterpret_cast<const bf16x8*>(tile + row0 * T::kRowBytes + (rows ^ (32 * c)));
+  }
+  // read_cols_tr(tile, r0, col0, lane) for r0 a multiple of 16 and col0 a
+  // multiple of 32.
+  __device__ __forceinline__ bf16x8 read_cols_tr(const char* tile, int r0, int col0) const {
+    const char* base = tile + r0 * T::kRowBytes;
+    const bf16x4 a = lds_read_tr16(reinterpret_cast<const __bf16*>(base + (tr0 ^ (2 * col0))));
+    const bf16x4 b = lds_read_tr16(reinterpret_cast<const __bf16*>(base + (tr1 ^ (2 * col0))));
+    return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  }
+};
+
 // Per-lane state for filling Tile<D, ROWS> tiles by direct copies.  The
 // KiB blocks of one wave lie WAVES KiB apart, a whole number of 16-row
 // swizzle periods, so every copy of a lane uses the same chunk position and
