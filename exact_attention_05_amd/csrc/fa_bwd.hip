@@ -28,7 +28,10 @@
 // overlap the next one's exponentials; operand fragments are read from LDS
 // four products ahead.  Stages that need a mask (causal diagonal, window
 // edges, ragged ends) take a plain, unpipelined path.  With shared K/V heads
-// the workgroup loops over the query heads of its group and sums.
+// each workgroup takes one query head of the group (a "run") and writes
+// float32 partial dK, dV; a reduction kernel adds the runs in a fixed order.
+// Runs of several heads, summed inside the workgroup, are used only when
+// the partials of one-head runs would not fit the workspace limit.
 //
 // bf16 stage 3 (dQ): mirrors the forward kernel.  8 waves own 32 queries
 // each and keep Q and dO in registers; key blocks of 64 rows (K, V) stream
