@@ -502,9 +502,9 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16_kernel(BwdArgs a, int n_kti
 
 // ------------------------------------------------------ stage 3 (bf16)
 
-template <int D>
+template <int D, int WAVES>
 struct DqCfg {
-  static constexpr int kWaves = 8;
+  static constexpr int kWaves = WAVES;           // 8: two per SIMD; 4 with a sliding window
   static constexpr int kThreads = kWaves * 64;
   static constexpr int kBM = kWaves * 32;        // queries per workgroup, 32 per wave
   static constexpr int kBN = 64;                 // keys per block
@@ -514,9 +514,10 @@ struct DqCfg {
   using KV = Tile<D, kBN>;
 };
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(512) void bwd_dq_bf16_kernel(BwdArgs a, int n_qtiles) {
-  using C = DqCfg<D>;
+template <int D, bool CAUSAL, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_dq_bf16_kernel(BwdArgs a, int n_qtiles) {
+  using C = DqCfg<D, WAVES>;
   __shared__ __attribute__((aligned(1024))) char sk[2][C::KV::kBytes];
   __shared__ __attribute__((aligned(1024))) char sv[2][C::KV::kBytes];
 
@@ -1014,15 +1015,22 @@ hipError_t dkdv_bf16_t(const BwdArgs& a, hipStream_t s) {
   return launch_raw(kernel, n_ktiles * (a.BH / a.group) * a.slices, C::kThreads, params, s);
 }
 
-template <int D, bool CAUSAL>
-hipError_t dq_bf16_t(const BwdArgs& a, hipStream_t s) {
-  using C = DqCfg<D>;
+template <int D, bool CAUSAL, int WAVES>
+hipError_t dq_bf16_w(const BwdArgs& a, hipStream_t s) {
+  using C = DqCfg<D, WAVES>;
   const int n_qtiles = (a.n_q + C::kBM - 1) / C::kBM;
   BwdArgs args = a;
   int nt = n_qtiles;
   void* params[] = {&args, &nt};
-  return launch_raw(reinterpret_cast<const void*>(bwd_dq_bf16_kernel<D, CAUSAL>),
+  return launch_raw(reinterpret_cast<const void*>(bwd_dq_bf16_kernel<D, CAUSAL, WAVES>),
                     n_qtiles * a.BH, C::kThreads, params, s);
+}
+
+// With a sliding window a 256-row workgroup visits about window + 256 keys
+// while each of its waves needs window + 32: 128-row workgroups waste less.
+template <int D, bool CAUSAL>
+hipError_t dq_bf16_t(const BwdArgs& a, hipStream_t s) {
+  return a.window >= 0 ? dq_bf16_w<D, CAUSAL, 4>(a, s) : dq_bf16_w<D, CAUSAL, 8>(a, s);
 }
 
 template <int D, bool CAUSAL>

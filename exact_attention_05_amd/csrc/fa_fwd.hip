@@ -636,12 +636,16 @@ hipError_t fwd_bf16_w(const FwdArgs& a, hipStream_t stream) {
 // Up to this many query rows per head, 128-row workgroups (4 waves) beat the
 // 256-row ones: less padding and twice the workgroups in flight (measured at
 // B=16, H=32, d=128: 17.7 vs 23.4 us at n=128, 96.6 vs 109 us at n=512, equal
-// at n=1024, 3 % slower at n=4096).
+// at n=1024, 3 % slower at n=4096).  With a sliding window a 256-row
+// workgroup visits about window + 256 keys while each wave needs window + 32,
+// so windows take 128-row workgroups at any length (H=32, n=4096, d=128:
+// causal w=512 65.6 -> 56.1 us, w=2048 127 -> 116 us).
 constexpr int kShortRows = 512;
 
 template <int D, bool CAUSAL>
 hipError_t fwd_bf16_t(const FwdArgs& a, hipStream_t stream) {
-  return a.n_q <= kShortRows ? fwd_bf16_w<D, CAUSAL, 4>(a, stream) : fwd_bf16_w<D, CAUSAL, 8>(a, stream);
+  return (a.n_q <= kShortRows || a.window >= 0) ? fwd_bf16_w<D, CAUSAL, 4>(a, stream)
+                                                : fwd_bf16_w<D, CAUSAL, 8>(a, stream);
 }
 
 template <int D, bool CAUSAL>
