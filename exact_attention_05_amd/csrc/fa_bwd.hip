@@ -270,11 +270,15 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16_kernel(BwdArgs a, int n_kti
   // software-pipelined with the sub-block before it (rows RP of buffer BP):
   //   region 1: S, dP of this sub-block   with dS and bf16 rounding of the previous
   //   region 2: dV, dK of the previous one with P, dP - D of this one
-  // qrow0 is the absolute index of row R0.
-  auto iteration = [&](auto mask_tag, auto buf_tag, auto r0_tag, auto bp_tag, auto rp_tag, int qrow0)
-      __attribute__((always_inline)) {
+  // qrow0 is the absolute index of row R0.  FIRST: there is no previous
+  // sub-block (the first iteration of a pass); region 2 then has no products,
+  // so nothing reads the other buffer, which may hold no data yet (stale LDS
+  // bits times a zero probability could be 0 * NaN).
+  auto iteration = [&](auto mask_tag, auto buf_tag, auto r0_tag, auto bp_tag, auto rp_tag, auto first_tag,
+                       int qrow0) __attribute__((always_inline)) {
     constexpr int BUF = decltype(buf_tag)::value, R0 = decltype(r0_tag)::value;
     constexpr int BP = decltype(bp_tag)::value, RP = decltype(rp_tag)::value;
+    constexpr bool FIRST = decltype(first_tag)::value;
     const char* qt = sq[BUF];
     const char* gt = sdo[BUF];
     s = f32x16{};
@@ -299,7 +303,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16_kernel(BwdArgs a, int n_kti
       static_for<c * 8 / C::kS1, (c + 1) * 8 / C::kS1>([&](auto pr) __attribute__((always_inline)) {
         stage_b(decltype(pr)::value);
       });
-      if constexpr (c == C::kS1 - 1) {
+      if constexpr (c == C::kS1 - 1 && !FIRST) {
         static_for<0, (C::kS2 < C::kAhead ? C::kS2 : C::kAhead)>([&](auto i) __attribute__((always_inline)) {
           constexpr int f = decltype(i)::value;
           fa[f] = tqt.read_cols_tr(sdo[BP], RP + 16 * (f / C::kDB), 32 * (f % C::kDB));
@@ -311,13 +315,15 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16_kernel(BwdArgs a, int n_kti
     static_for<0, C::kS2>([&](auto f_tag) __attribute__((always_inline)) {
       constexpr int f = decltype(f_tag)::value;
       constexpr int c2 = f / C::kDB, db = f % C::kDB;
-      if constexpr (f + C::kAhead < C::kS2) {
-        constexpr int g = f + C::kAhead;
-        fa[g % C::kRing] = tqt.read_cols_tr(sdo[BP], RP + 16 * (g / C::kDB), 32 * (g % C::kDB));
-        fb[g % C::kRing] = tqt.read_cols_tr(sq[BP], RP + 16 * (g / C::kDB), 32 * (g % C::kDB));
+      if constexpr (!FIRST) {
+        if constexpr (f + C::kAhead < C::kS2) {
+          constexpr int g = f + C::kAhead;
+          fa[g % C::kRing] = tqt.read_cols_tr(sdo[BP], RP + 16 * (g / C::kDB), 32 * (g % C::kDB));
+          fb[g % C::kRing] = tqt.read_cols_tr(sq[BP], RP + 16 * (g / C::kDB), 32 * (g % C::kDB));
+        }
+        dv[db] = mfma_bf16(fa[f % C::kRing], bf16x8_of(pb[c2]), dv[db]);
+        dk[db] = mfma_bf16(fb[f % C::kRing], bf16x8_of(dsb[c2]), dk[db]);
       }
-      dv[db] = mfma_bf16(fa[f % C::kRing], bf16x8_of(pb[c2]), dv[db]);
-      dk[db] = mfma_bf16(fb[f % C::kRing], bf16x8_of(dsb[c2]), dk[db]);
       static_for<f * 16 / C::kS2, (f + 1) * 16 / C::kS2>([&](auto i) __attribute__((always_inline)) {
         stage_a(mask_tag, decltype(i)::value, qrow0);
       });
@@ -329,7 +335,9 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16_kernel(BwdArgs a, int n_kti
   // with the second sub-block of the previous stage (buffer BUF ^ 1).  The
   // stage was copied during the previous stage; after the first sub-block
   // every wave is past the previous stage, whose buffer then takes the next.
-  auto do_stage = [&](auto mask_tag, auto buf_tag, int b) __attribute__((always_inline)) {
+  // FIRST: the first stage of a pass (its first sub-block has no
+  // predecessor).
+  auto do_stage = [&](auto mask_tag, auto buf_tag, int b, auto first_tag) __attribute__((always_inline)) {
     constexpr int BUF = decltype(buf_tag)::value;
     using IB = std::integral_constant<int, BUF>;
     using IP = std::integral_constant<int, BUF ^ 1>;
@@ -338,10 +346,10 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16_kernel(BwdArgs a, int n_kti
     const int qrow0 = (qb_first + b) * C::kBQ;
     wait_lds_dma();
     phase_barrier();
-    iteration(mask_tag, IB{}, R0{}, IP{}, R32{}, qrow0);
+    iteration(mask_tag, IB{}, R0{}, IP{}, R32{}, first_tag, qrow0);
     phase_barrier();
     if (b + 1 < nblocks) load_block(b + 1, BUF ^ 1);
-    iteration(mask_tag, IB{}, R32{}, IB{}, R0{}, qrow0 + 32);
+    iteration(mask_tag, IB{}, R32{}, IB{}, R0{}, F{}, qrow0 + 32);
   };
 
   // Stages [b_lo, b_hi) need no mask: every row sees every key of the
@@ -427,16 +435,19 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16_kernel(BwdArgs a, int n_kti
       if (b < b_hi) {
   #pragma unroll
         for (int i = 0; i < 16; ++i) { ex[i] = 0.f; dd[i] = 0.f; }
-        if (b & 1) {
-          do_stage(F{}, B1{}, b);
+        if (b & 1) do_stage(F{}, B1{}, b, T{});
+        else do_stage(F{}, B0{}, b, T{});
+        ++b;
+        if (b < b_hi && (b & 1)) {
+          do_stage(F{}, B1{}, b, F{});
           ++b;
         }
         for (; b + 1 < b_hi; b += 2) {
-          do_stage(F{}, B0{}, b);
-          do_stage(F{}, B1{}, b + 1);
+          do_stage(F{}, B0{}, b, F{});
+          do_stage(F{}, B1{}, b + 1, F{});
         }
         if (b < b_hi) {
-          do_stage(F{}, B0{}, b);
+          do_stage(F{}, B0{}, b, F{});
           ++b;
         }
         if ((b - 1) & 1) finish(B1{});
