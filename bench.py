@@ -39,6 +39,7 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 matrix cores
 PEAK_HBM_GBS = 8000.0
+PEAK_SCLK_MHZ = 2400.0      # shader clock the peak figures assume
 METRIC = "attention fwd/bwd TFLOP/s (4·B·H·n²·d/t) and % bf16 MFMA peak at n=4096,d=128"
 
 KERNEL_SOURCES = {
@@ -294,7 +295,10 @@ def _median_us(torch, fn, reps: int, warmup: int = 3, batch: int = 10):
 
 def _sclk_sampler():
     """Best-effort sampling of the GPU's shader clock (amd-smi) in a thread;
-    returns (start, stop) where stop() gives the mean MHz or None."""
+    returns (start, stop, count) where stop(t0, t1) gives the mean MHz of the
+    samples taken entirely inside [t0, t1] (perf_counter times) or None, and
+    count(t0) the number of samples completed that began at or after t0 (-1
+    when amd-smi is missing or failed)."""
     import subprocess
     import threading
 
@@ -303,8 +307,10 @@ def _sclk_sampler():
     def run():
         while not done.is_set():
             try:
+                t_a = time.perf_counter()
                 r = subprocess.run(["amd-smi", "metric", "-g", "0", "--clock", "--json"],
                                    capture_output=True, text=True, timeout=5)
+                t_b = time.perf_counter()
                 data = json.loads(r.stdout)
                 node = data["gpu_data"][0] if isinstance(data, dict) and "gpu_data" in data else (
                     data[0] if isinstance(data, list) else data)
@@ -313,19 +319,48 @@ def _sclk_sampler():
                         if k.startswith("gfx_") and isinstance(v, dict) and isinstance(v.get("clk"), dict)
                         and v["clk"].get("value") not in (None, "N/A")]
                 if vals:
-                    samples.append(sum(vals) / len(vals))  # mean over the XCDs
+                    samples.append((t_a, t_b, sum(vals) / len(vals)))  # mean over the XCDs
             except Exception:  # noqa: BLE001
                 return
             done.wait(0.05)
 
     t = threading.Thread(target=run, daemon=True)
 
-    def stop():
+    def stop(t0=float("-inf"), t1=float("inf")):
         done.set()
         t.join(timeout=10)
-        return round(sum(samples) / len(samples), 1) if samples else None
+        inside = [v for a, b, v in samples if a >= t0 and b <= t1]
+        return round(sum(inside) / len(inside), 1) if inside else None
 
-    return t.start, stop
+    def count(t0):
+        """Samples begun at or after t0; -1 once the sampler has given up."""
+        if not t.is_alive():
+            return -1
+        return sum(1 for a, _, _ in list(samples) if a >= t0)
+
+    return t.start, stop, count
+
+
+def _sclk_under_load(launch, torch, settle_s=1.5, min_s=1.0, max_s=8.0, want=3):
+    """Mean shader clock (MHz) over amd-smi samples taken while `launch()`
+    (a batch of GPU work) runs back to back.  The driver refreshes the value
+    about once a second, so samples are only counted after settle_s seconds
+    of load, for at least min_s more seconds and until `want` of them are
+    in, or max_s seconds of load in all."""
+    start, stop, count = _sclk_sampler()
+    start()
+    launch()
+    torch.cuda.synchronize()  # the GPU is busy from here on
+    t_busy = time.perf_counter()
+    t0 = t_busy + settle_s
+    while True:
+        launch()
+        torch.cuda.synchronize()
+        now = time.perf_counter()
+        c = count(t0)
+        if c < 0 or now - t_busy >= max_s or (now >= t0 + min_s and c >= want):
+            break
+    return stop(t0, time.perf_counter())
 
 
 def run_configs(args, torch, fa, workloads, dev):
@@ -367,15 +402,15 @@ def run_configs(args, torch, fa, workloads, dev):
                                "pct_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2), "n_splits": sp}
     del q2, k2, v2, o2, l2, ws2
     res["c3_noncausal"] = fwd_entry(workloads.c3(False))
-    # the shader clock while the c3 forward runs back to back for about a second
-    start, stop = _sclk_sampler()
+    # the shader clock while the c3 forward runs back to back
     w3 = workloads.c3(False)
     q3, k3, v3 = (t.to(dev) for t in (w3.q, w3.k, w3.v))
-    start()
-    for _ in range(4000):
-        fa.forward(q3, k3, v3, scale=w3.scale)
-    torch.cuda.synchronize()
-    sclk = stop()
+
+    def c3_batch():
+        for _ in range(40):
+            fa.forward(q3, k3, v3, scale=w3.scale)
+
+    sclk = _sclk_under_load(c3_batch, torch)
     del q3, k3, v3
     res["c3_causal"] = fwd_entry(workloads.c3(True))
     res["c4_causal"] = fwd_entry(workloads.c4(), reps=5)
@@ -459,6 +494,9 @@ def main(argv=None):
     ap.add_argument("--causal", action="store_true", help="causal mask (default: non-causal)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle CPU work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip sampling the shader clock (amd-smi) while the forward runs back to "
+                         "back after the timed steps (about 3 s)")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="after the timed steps, run one elementwise copy of 512 MiB (fp32 x*1 into "
                          "a second buffer) so that a counter run sees a kernel of known traffic")
@@ -521,6 +559,16 @@ def main(argv=None):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
+    sclk = None
+    if not args.no_clock:
+        # Outside the timed region: the mean shader clock while the forward
+        # runs back to back, to state the peak fraction at the running clock.
+        def fwd_batch():
+            for _ in range(40):
+                fa.forward(q, k, v, causal=causal, scale=w.scale, out=o, lse=lse)
+
+        sclk = _sclk_under_load(fwd_batch, torch)
+
     if args.calibration_copy:
         calibration_copy(torch, dev)
 
@@ -551,6 +599,7 @@ def main(argv=None):
     achieved = flops[dominant] / dom_t / 1e12
     traffic = load_traffic(dominant)
     fwd_lit = 4 * B * H * n * n * d / (per_stage["fwd"] * 1e-3) / 1e12
+    fwd_pct = 100 * flops["fwd"] / (per_stage["fwd"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS
 
     out = {
         "metric": METRIC,
@@ -568,7 +617,9 @@ def main(argv=None):
         "config": {"workload": w.name, "B": B, "H": H, "n": n, "d": d, "causal": causal,
                    "scale": w.scale, "step": "fa_forward + fa_backward stages"},
         "fwd_tflops_literal": round(fwd_lit, 2),
-        "fwd_pct_bf16_peak": round(100 * flops["fwd"] / (per_stage["fwd"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+        "fwd_pct_bf16_peak": round(fwd_pct, 2),
+        "sclk_mhz_mean_fwd": sclk,
+        "fwd_pct_bf16_peak_at_sclk": round(fwd_pct * PEAK_SCLK_MHZ / sclk, 2) if sclk else None,
         "kernels": kernels,
         "roofline": {
             "kernel": dominant,
