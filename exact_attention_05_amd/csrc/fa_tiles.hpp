@@ -37,21 +37,24 @@ struct Tile {
   static_assert(kKiB * 1024 == kBytes, "a tile is a whole number of KiB");
 
   // Chunk permutation of row `row` (see the layout note above).
-  __device__ static __forceinline__ int swizzle(int row) {
+  __host__ __device__ static __forceinline__ int swizzle(int row) {
     if constexpr (D == 128) return 4 * (row & 3) + ((row >> 2) & 3);
     else if constexpr (D == 64) return 4 * ((row >> 1) & 1) + ((row >> 2) & 3);
     else return (row >> 2) & 3;
   }
 
   // Byte offset of (row, 16-byte logical chunk) within the tile.
-  __device__ static __forceinline__ int offset(int row, int chunk) {
+  __host__ __device__ static __forceinline__ int offset(int row, int chunk) {
     return row * kRowBytes + ((chunk ^ swizzle(row)) << 4);
   }
 
   // A-operand read for v_mfma_f32_32x32x16_bf16 from rows row0 .. row0+31:
   // lane l gets row row0 + l%32, columns 16c + 8(l/32) .. +7.
+  __host__ __device__ static __forceinline__ int rows_offset(int row0, int c, int lane) {
+    return offset(row0 + (lane & 31), 2 * c + (lane >> 5));
+  }
   __device__ static __forceinline__ bf16x8 read_rows(const char* tile, int row0, int c, int lane) {
-    return *reinterpret_cast<const bf16x8*>(tile + offset(row0 + (lane & 31), 2 * c + (lane >> 5)));
+    return *reinterpret_cast<const bf16x8*>(tile + rows_offset(row0, c, lane));
   }
 
   // A-operand read of the TRANSPOSED tile for v_mfma_f32_32x32x16_bf16:
@@ -61,12 +64,17 @@ struct Tile {
   // i.e. the 16-row chunk r0 .. r0+15 in the order the 32x32 accumulator
   // layout lists its rows (element i of lane l is row 8(i/4) + 4(l/32) + i%4),
   // so an accumulator converted to bf16 can be the matching B operand.
-  __device__ static __forceinline__ bf16x8 read_cols_tr(const char* tile, int r0, int col0, int lane) {
-    const int row = r0 + 4 * (lane >> 5) + ((lane & 15) >> 2);
+  // Byte offset of the lane's 8-byte piece `half` (0: rows r0 + 4(l/32) +
+  // 0..3, 1: the same rows + 8) of that read; the transposing read takes
+  // 4 columns of 4 consecutive rows from each lane group of 4.
+  __host__ __device__ static __forceinline__ int tr_offset(int r0, int col0, int lane, int half) {
+    const int row = r0 + 4 * (lane >> 5) + ((lane & 15) >> 2) + 8 * half;
     const int col = col0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-    const int byte_in_chunk = 2 * (col & 7);
-    const bf16x4 a = lds_read_tr16(reinterpret_cast<const __bf16*>(tile + offset(row, col >> 3) + byte_in_chunk));
-    const bf16x4 b = lds_read_tr16(reinterpret_cast<const __bf16*>(tile + offset(row + 8, col >> 3) + byte_in_chunk));
+    return offset(row, col >> 3) + 2 * (col & 7);
+  }
+  __device__ static __forceinline__ bf16x8 read_cols_tr(const char* tile, int r0, int col0, int lane) {
+    const bf16x4 a = lds_read_tr16(reinterpret_cast<const __bf16*>(tile + tr_offset(r0, col0, lane, 0)));
+    const bf16x4 b = lds_read_tr16(reinterpret_cast<const __bf16*>(tile + tr_offset(r0, col0, lane, 1)));
     return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
   }
 };
@@ -85,23 +93,26 @@ struct TileLane {
   int tr0;    // read_cols_tr, first 8 bytes: lane part for r0 = 0, col0 = 0
   int tr1;    // second 8 bytes (rows + 8)
 
-  __device__ __forceinline__ void init(int lane) {
-    rows = T::offset(lane & 31, lane >> 5);
-    const int row = 4 * (lane >> 5) + ((lane & 15) >> 2);
-    const int col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-    tr0 = T::offset(row, col >> 3) + 2 * (col & 7);
-    tr1 = T::offset(row + 8, col >> 3) + 2 * (col & 7);
+  __host__ __device__ __forceinline__ void init(int lane) {
+    rows = T::rows_offset(0, 0, lane);
+    tr0 = T::tr_offset(0, 0, lane, 0);
+    tr1 = T::tr_offset(0, 0, lane, 1);
   }
-  // read_rows(tile, row0, c, lane) for row0 a multiple of 32.
-  __device__ __forceinline__ bf16x8 read_rows(const char* tile, int row0, int c) const {
-    return *reinterpret_cast<const bf16x8*>(tile + row0 * T::kRowBytes + (rows ^ (32 * c)));
+  // T::rows_offset(row0, c, lane) for row0 a multiple of 32.
+  __host__ __device__ __forceinline__ int rows_at(int row0, int c) const {
+    return row0 * T::kRowBytes + (rows ^ (32 * c));
   }
-  // read_cols_tr(tile, r0, col0, lane) for r0 a multiple of 16 and col0 a
+  // T::tr_offset(r0, col0, lane, half) for r0 a multiple of 16 and col0 a
   // multiple of 32.
+  __host__ __device__ __forceinline__ int tr_at(int r0, int col0, int half) const {
+    return r0 * T::kRowBytes + ((half ? tr1 : tr0) ^ (2 * col0));
+  }
+  __device__ __forceinline__ bf16x8 read_rows(const char* tile, int row0, int c) const {
+    return *reinterpret_cast<const bf16x8*>(tile + rows_at(row0, c));
+  }
   __device__ __forceinline__ bf16x8 read_cols_tr(const char* tile, int r0, int col0) const {
-    const char* base = tile + r0 * T::kRowBytes;
-    const bf16x4 a = lds_read_tr16(reinterpret_cast<const __bf16*>(base + (tr0 ^ (2 * col0))));
-    const bf16x4 b = lds_read_tr16(reinterpret_cast<const __bf16*>(base + (tr1 ^ (2 * col0))));
+    const bf16x4 a = lds_read_tr16(reinterpret_cast<const __bf16*>(tile + tr_at(r0, col0, 0)));
+    const bf16x4 b = lds_read_tr16(reinterpret_cast<const __bf16*>(tile + tr_at(r0, col0, 1)));
     return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
   }
 };
