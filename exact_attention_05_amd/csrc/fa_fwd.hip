@@ -168,14 +168,9 @@ void fwd_bf16_kernel(FwdArgs a, int n_qtiles) {
     // diagonal above the wave, a window edge) changes nothing for it.
     if (MASK && (qw >= n_q || band.key_hi(qw + 32) <= k0 || band.key_lo(qw) >= k0 + C::kBN)) return;
 
-    // Matrix-core phases run at raised wave priority, the softmax at normal
-    // priority: of the two waves on a SIMD, the one still issuing matrix
-    // operations wins the issue port, so one wave's softmax overlaps the
-    // other's products instead of both waves alternating in lock step.
     f32x16 s[C::kKB];
     auto scores = [&]() __attribute__((always_inline)) {
       // S^T = K Q^T for kBN keys x 32 queries.
-      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int kb = 0; kb < C::kKB; ++kb) s[kb] = f32x16{};
 #pragma unroll
@@ -185,7 +180,6 @@ void fwd_bf16_kernel(FwdArgs a, int n_qtiles) {
           s[kb] = mfma_bf16(tl.read_rows(ks, kb * 32, c), qf[c], s[kb]);
         }
       }
-      __builtin_amdgcn_s_setprio(0);
     };
     // Row maximum of the block (raw scores), then the lazy reference update.
     auto raise_ref = [&]() __attribute__((always_inline)) {
@@ -262,7 +256,6 @@ void fwd_bf16_kernel(FwdArgs a, int n_qtiles) {
     l += rs;
 
     // O^T += V^T P^T, 16 keys per matrix-core step.
-    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int kb = 0; kb < C::kKB; ++kb)
 #pragma unroll
@@ -271,7 +264,6 @@ void fwd_bf16_kernel(FwdArgs a, int n_qtiles) {
         for (int db = 0; db < C::kDB; ++db)
           oacc[db] = mfma_bf16(tl.read_cols_tr(vs, kb * 32 + 16 * c2, 32 * db),
                                bf16x8_of(pw[kb][c2]), oacc[db]);
-    __builtin_amdgcn_s_setprio(0);
   };
 
   // Blocks that need no mask for any row of the workgroup go two at a time
