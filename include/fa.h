@@ -84,7 +84,11 @@ typedef enum fa_dtype {
 } fa_dtype;
 
 /* Forward pass.  Writes o (B,H,n_q,d; dtype) and lse (B,H,n_q; float32).
- * One kernel launch on `stream`. */
+ * One kernel launch on `stream`.  bf16 shapes with few query rows per key
+ * (n_k >= 1024 and B*H*ceil(n_q/256) <= 32, or <= 64 for d <= 64) run on the
+ * split-key kernel of fa_decode with one chunk, which spreads each row
+ * block's keys over several waves (no workspace); all others on the forward
+ * kernel.  Both compute the same function and agree within rounding. */
 int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse,
                int B, int H, int n_q, int n_k, int d, float scale, int causal,
                int dtype, void* stream);

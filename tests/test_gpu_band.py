@@ -120,3 +120,24 @@ def test_sliding_window_workload_size(dev):
         ro, rl = oracle.attention_fwd_band(np64(q[0, h]), np64(k[0, h]), np64(v[0, h]), 1 / math.sqrt(d), True, 0, w)
         assert_close(f"O head {h}", o[0, h], ro, 2e-2)
         assert_close(f"LSE head {h}", lse[0, h], rl, TOL_LSE)
+
+
+# Few query tiles but many keys: fa_forward_ext runs these on the split-key
+# kernel (one chunk, keys spread over the waves of a workgroup and merged in
+# LDS) instead of the forward kernel; the backward is unchanged.
+STARVED = [  # B, H, H_kv, n_q, n_k, causal, q_offset, window, d
+    (1, 1, 1, 2048, 2048, True, 0, -1, 128),
+    (1, 2, 2, 1000, 3000, False, 500, 300, 64),
+    (1, 4, 1, 700, 1500, True, 800, -1, 32),
+    (2, 1, 1, 300, 4100, False, 0, -1, 128),
+    (1, 2, 1, 33, 2500, True, 2467, 700, 64),
+]
+
+
+@pytest.mark.parametrize("case", STARVED, ids=lambda c: "B{}H{}kv{}_{}x{}_c{}_off{}_w{}_d{}".format(*c))
+def test_starved_shapes_parity(dev, case):
+    B, H, h_kv, n_q, n_k, causal, off, w, d = case
+    q, k, v, do = draw(4700 + n_q + n_k + d, B, H, h_kv, n_q, n_k, d, torch.bfloat16)
+    scale = 1 / math.sqrt(d)
+    got = run(dev, q, k, v, do, scale, causal, off, w)
+    check(f"{case}", got, q, k, v, do, scale, causal, off, w, torch.bfloat16)
