@@ -80,6 +80,15 @@ __device__ __forceinline__ void lds_dma16(uint32_t lds_addr, const void* base, u
 // compiler's own wait tracking knows that its earlier loads are done too.
 __device__ __forceinline__ void wait_lds_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// s_waitcnt vmcnt(N): all but the last N vector-memory loads of this wave
+// have completed (they complete in issue order), e.g. one block's copies
+// done while the next block's N are still in flight.
+template <int N>
+__device__ __forceinline__ void wait_lds_dma_but() {
+  static_assert(N >= 0 && N < 64, "vmcnt holds 6 bits");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
 // Workgroup barrier that leaves vector-memory loads (the LDS copies above)
 // in flight.  It waits only for this wave's own LDS reads (lgkmcnt(0)), so
 // that a buffer read before the barrier may be refilled after it; the asm

@@ -272,7 +272,14 @@ void fwd_bf16_kernel(FwdArgs a, int n_qtiles) {
   using F = std::false_type;
   using T = std::true_type;
   using BR = std::integral_constant<int, -1>;
+  // When the first two blocks are both unmasked (the pipeline starts at
+  // once), both buffers are free and both blocks' copies go out together, so
+  // the workgroup waits for memory once before it starts.  (Workgroups that
+  // start on masked blocks, window edges, keep one block of look-ahead:
+  // measured faster there.)
+  const bool early = f_lo == t_lo && t_lo + 1 < f_hi;
   if (t_lo < t_hi) load_tile(t_lo, t_lo & 1);
+  if (early) load_tile(t_lo + 1, (t_lo + 1) & 1);
   int t = t_lo;
   for (; t < f_lo; ++t) block(T{}, BR{}, t);
 
@@ -336,7 +343,7 @@ void fwd_bf16_kernel(FwdArgs a, int n_qtiles) {
         const int k2 = (t + 2) * C::kBN;
         dma.load(kp + (size_t)k2 * D, n_k - k2, sk_addr + B * C::KV::kBytes);
       }
-      if (t + 1 < t_hi) {
+      if (t + 1 < t_hi && !(early && t == f_lo)) {
         const int k1 = (t + 1) * C::kBN;
         dma.load(vp + (size_t)k1 * D, n_k - k1, sv_addr + (B ^ 1) * C::KV::kBytes);
       }
@@ -362,10 +369,12 @@ void fwd_bf16_kernel(FwdArgs a, int n_qtiles) {
       }
     };
     // Prologue: K_{f_lo} and V_{f_lo} were started by the previous block (or
-    // the first load); start K_{f_lo + 1} and compute block f_lo's scores.
-    wait_lds_dma();
+    // the first load); start K_{f_lo + 1} (unless started with them) and
+    // compute block f_lo's scores.
+    if (early) wait_lds_dma_but<2 * decltype(dma)::kMine>();  // block f_lo + 1 may still be in flight
+    else wait_lds_dma();
     __syncthreads();
-    if (f_lo + 1 < t_hi) {
+    if (f_lo + 1 < t_hi && !early) {
       const int k1 = (f_lo + 1) * C::kBN;
       dma.load(kp + (size_t)k1 * D, n_k - k1, sk_addr + ((f_lo + 1) & 1) * C::KV::kBytes);
     }

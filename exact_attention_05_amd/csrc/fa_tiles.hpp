@@ -126,6 +126,9 @@ struct TileDma {
   using T = Tile<D, ROWS>;
   static constexpr int kMine = (T::kKiB + WAVES - 1) / WAVES;  // KiB copies per wave
   static constexpr int kRowStep = WAVES * 1024 / T::kRowBytes;  // rows between a lane's copies
+  // Every wave issues kMine copies per tile, or none (so that a count of
+  // outstanding copies is the same for every wave that has any).
+  static_assert(T::kKiB % WAVES == 0 || T::kKiB < WAVES, "uneven copies per wave");
   static_assert(kRowStep % 16 == 0, "a wave's copies must be whole swizzle periods apart");
   int row0;       // tile row of the lane's first copy
   int col_bytes;  // byte offset of its 16-byte chunk within a row (swizzled)
