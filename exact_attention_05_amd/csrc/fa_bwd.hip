@@ -601,6 +601,11 @@ void bwd_dq_bf16_kernel(BwdArgs a, int n_qtiles) {
   f32x16 dq[C::kDB];
 #pragma unroll
   for (int db = 0; db < C::kDB; ++db) dq[db] = f32x16{};
+  // dP^T accumulates from -D (one query per lane), so the products give
+  // dP - D for dS = P o (dP - D) directly.
+  f32x16 neg_d;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) neg_d[i] = -dlt;
 
   auto block = [&](auto mask_tag, auto buf_tag, int t) {
     constexpr bool MASK = decltype(mask_tag)::value;
@@ -616,7 +621,7 @@ void bwd_dq_bf16_kernel(BwdArgs a, int n_qtiles) {
     for (int kb = 0; kb < C::kKB; ++kb) {
       // every key of the sub-block hidden from this wave
       if (MASK && (k0 + kb * 32 >= band.key_hi(qw + 32) || k0 + kb * 32 + 32 <= band.key_lo(qw))) continue;
-      f32x16 s = f32x16{}, dp = f32x16{};
+      f32x16 s = f32x16{}, dp = neg_d;
 #pragma unroll
       for (int c = 0; c < C::kDC; ++c) {
         s = mfma_bf16(tkv.read_rows(ks, kb * 32, c), qf[c], s);
@@ -632,7 +637,7 @@ void bwd_dq_bf16_kernel(BwdArgs a, int n_qtiles) {
           if (!Band::in_range(rel, 0, vspan)) p0 = 0.f;
           if (!Band::in_range(rel + 1, 0, vspan)) p1 = 0.f;
         }
-        dsb[i >> 3][(i & 7) >> 1] = pack_bf16x2(p0 * (dp[i] - dlt), p1 * (dp[i + 1] - dlt));
+        dsb[i >> 3][(i & 7) >> 1] = pack_bf16x2(p0 * dp[i], p1 * dp[i + 1]);
       }
 #pragma unroll
       for (int c2 = 0; c2 < 2; ++c2)
