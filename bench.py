@@ -432,6 +432,23 @@ def run_configs(args, torch, fa, workloads, dev):
     del q, k, v, do, o, lse, ws, dq, dk, dv
     torch.cuda.empty_cache()
 
+    # LSE merge of 8 bf16 parts of the c3 shape (the results of 8 key chunks,
+    # as a sequence-sharded step combines them): HBM-bound, algorithmic bytes
+    # = the parts (o and lse) read once and the result written once; 302 MB
+    # per call, more than the 256 MB last-level cache.
+    P, B, H, n, d = 8, 1, 32, 4096, 128
+    g = torch.Generator(device="cpu").manual_seed(8)
+    o_parts = torch.randn(P, B, H, n, d, generator=g).to(torch.bfloat16).to(dev)
+    lse_parts = (torch.randn(P, B, H, n, generator=g) * 2.0).to(dev)
+    mo = torch.empty((B, H, n, d), dtype=torch.bfloat16, device=dev)
+    ml = torch.empty((B, H, n), dtype=torch.float32, device=dev)
+    us = _median_us(torch, lambda: fa.lse_merge(o_parts, lse_parts, out=mo, lse=ml), 20)
+    nbytes = P * B * H * n * (d * 2 + 4) + B * H * n * (d * 2 + 4)
+    res["merge8_c3_bf16"] = {"us": round(us, 1), "gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
+                             "pct_hbm": round(100 * nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 2)}
+    del o_parts, lse_parts, mo, ml
+    torch.cuda.empty_cache()
+
     # Short-sequence sweep: B=16, H=32, d=128 bf16 non-causal forward, input
     # sets rotated so that the bytes touched between two calls of the same
     # set exceed the 256 MB last-level cache.

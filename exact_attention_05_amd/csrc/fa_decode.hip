@@ -330,13 +330,28 @@ struct Vec4<__bf16> {
   }
 };
 
+// One 16-byte load of a part: 4 float32 or 8 bfloat16 values of a row.
+template <typename T>
+struct Part16 {
+  static constexpr int kCols = 16 / (int)sizeof(T);
+  __device__ static __forceinline__ void load(const T* p, float (&x)[kCols]) {
+#pragma unroll
+    for (int j = 0; j < kCols; j += 4) {
+      const f32x4 v = Vec4<T>::load(p + j);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[j + e] = v[e];
+    }
+  }
+};
+
 template <int D, typename TI, typename TO>
 __global__ __launch_bounds__(256) void lse_merge_kernel(MergeArgs a) {
-  constexpr int kTpr = D / 4;          // threads per row
-  constexpr int kRows = 256 / kTpr;    // rows per workgroup
+  constexpr int kCols = Part16<TI>::kCols;  // columns per thread: one 16-byte load per part
+  constexpr int kTpr = D / kCols;           // threads per row
+  constexpr int kRows = 256 / kTpr;         // rows per workgroup
   const long long row = (long long)blockIdx.x * kRows + threadIdx.x / kTpr;
   if (row >= a.rows) return;
-  const int c = (threadIdx.x % kTpr) * 4;
+  const int c = (threadIdx.x % kTpr) * kCols;
   const TI* op = static_cast<const TI*>(a.o_parts);
   const float* lp = a.lse_parts;
 
@@ -352,26 +367,32 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(MergeArgs a) {
     for (int u = 0; u < kU; ++u) mx = fmaxf(mx, lv[u]);
   }
   const float ref = mx == -INFINITY ? 0.f : mx;
-  f32x4 acc = f32x4{};
+  float acc[kCols];
+#pragma unroll
+  for (int j = 0; j < kCols; ++j) acc[j] = 0.f;
   float s = 0.f;
   for (int p0 = 0; p0 < a.n_parts; p0 += kU) {
     float w[kU];
-    f32x4 x[kU];
+    float x[kU][kCols];
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       const bool in = p0 + u < a.n_parts;
       const size_t pr = (size_t)(in ? p0 + u : p0) * a.rows + row;
       w[u] = in ? fast_exp2((lp[pr] - ref) * kLog2e) : 0.f;  // 0 for a part without keys
-      x[u] = Vec4<TI>::load(op + pr * D + c);
+      Part16<TI>::load(op + pr * D + c, x[u]);
     }
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      acc += w[u] * x[u];
+#pragma unroll
+      for (int j = 0; j < kCols; ++j) acc[j] += w[u] * x[u][j];
       s += w[u];
     }
   }
   const float inv = s > 0.f ? 1.f / s : 0.f;
-  Vec4<TO>::store(static_cast<TO*>(a.o) + (size_t)row * D + c, acc * inv);
+  TO* dst = static_cast<TO*>(a.o) + (size_t)row * D + c;
+#pragma unroll
+  for (int j = 0; j < kCols; j += 4)
+    Vec4<TO>::store(dst + j, f32x4{acc[j] * inv, acc[j + 1] * inv, acc[j + 2] * inv, acc[j + 3] * inv});
   if (c == 0) a.lse[row] = s > 0.f ? ref + fast_log2(s) * kLn2 : -INFINITY;
 }
 
@@ -388,7 +409,7 @@ template <int D, typename TI, typename TO>
 hipError_t merge_t(const MergeArgs& a, hipStream_t stream) {
   MergeArgs args = a;
   void* params[] = {&args};
-  constexpr int kRows = 256 / (D / 4);
+  constexpr int kRows = 256 / (D / Part16<TI>::kCols);
   const int grid = (int)((a.rows + kRows - 1) / kRows);
   return hipLaunchKernel(reinterpret_cast<const void*>(lse_merge_kernel<D, TI, TO>), dim3(grid), dim3(256),
                          params, 0, stream);
