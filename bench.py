@@ -521,7 +521,7 @@ def main(argv=None):
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(heads shard across GPUs with no exchange; see DESIGN.md)", file=sys.stderr)
+              "(heads would shard across GPUs with no exchange)", file=sys.stderr)
         return 2
 
     import torch
