@@ -205,12 +205,13 @@ def run_decode(args, torch, fa, workloads, dev):
     lse = torch.empty((B, H, n_q), dtype=torch.float32, device=dev)
     splits = fa.decode_splits(B, H, h_kv, n_q, n_k)
     ws = torch.empty(max(1, fa.decode_workspace_size(B, H, n_q, d, splits)), dtype=torch.uint8, device=dev)
-    steps = args.steps if args.steps != 20 else 200   # a call is ~0.1 ms: time more of them
+    steps = args.steps if args.steps is not None else 200   # a call is ~0.1 ms: time more of them
+    warmup = args.warmup if args.warmup is not None else 1000  # ~0.1 s: let the clock settle
 
     def step():
         fa.decode(q, k, v, causal=True, scale=w.scale, n_splits=splits, out=o, lse=lse, workspace=ws)
 
-    for _ in range(max(args.warmup, 5)):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
@@ -234,7 +235,7 @@ def run_decode(args, torch, fa, workloads, dev):
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": steps,
-        "warmup": max(args.warmup, 5),
+        "warmup": warmup,
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -273,13 +274,20 @@ def run_decode(args, torch, fa, workloads, dev):
 PEAK_FP32_TFLOPS = 157.3   # MI355X fp32 matrix / vector peak
 
 
-def _median_us(torch, fn, reps: int, warmup: int = 3, batch: int = 10):
+def _median_us(torch, fn, reps: int, warmup: int = 3, batch: int = 10, settle_s: float = 0.3):
     """Per-call time of fn() in microseconds: the median over ``reps`` HIP-event
     measurements of ``batch`` back-to-back calls each (calls issued one at a
-    time with an idle GPU in between run at a lower clock)."""
+    time with an idle GPU in between run at a lower clock), after at least
+    ``warmup`` calls and ``settle_s`` seconds of back-to-back calls, so that
+    the shader clock has settled under the load."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < settle_s:
+        for _ in range(batch):
+            fn()
+        torch.cuda.synchronize()
     ts = []
     for _ in range(reps):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -503,8 +511,11 @@ def run_configs(args, torch, fa, workloads, dev):
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default: 50 training steps, 200 decoding calls)")
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps first (default: 100 training steps, 1000 decoding calls, "
+                         "about 0.1 s, so that the timed steps run at the settled shader clock)")
     ap.add_argument("--workload", choices=["train", "decode", "configs"], default="train",
                     help="train: forward + backward at n=4096 (default); decode: split-KV decoding; "
                          "configs: every workload's hot call plus the short-sequence HBM sweep")
@@ -535,6 +546,10 @@ def main(argv=None):
     dev = torch.device("cuda:0")
     if args.workload == "decode":
         return run_decode(args, torch, fa, workloads, dev)
+    if args.steps is None:
+        args.steps = 50
+    if args.warmup is None:
+        args.warmup = 100
     if args.workload == "configs":
         return run_configs(args, torch, fa, workloads, dev)
     w = workloads.c3_train(args.causal)
