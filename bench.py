@@ -82,14 +82,15 @@ def kernel_bytes(B, H, n, d, e=2):
     }
 
 
-def load_traffic(kernel: str):
+def load_traffic(kernel: str, workload: str):
     """HBM bytes per launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE,
-    if recorded for the current source of that kernel; else None."""
+    if recorded for the current source of that kernel on this workload (the
+    tag of the profile summary); else None."""
     path = os.path.join(ROOT, "profiles", f"traffic_{kernel}.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("source_sha256") != kernel_source_digest(kernel):
+    if rec.get("workload") != workload or rec.get("source_sha256") != kernel_source_digest(kernel):
         return None
     return rec.get("bytes_per_launch")
 
@@ -253,7 +254,7 @@ def run_decode(args, torch, fa, workloads, dev):
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
-            "traffic": load_traffic("decode"),
+            "traffic": load_traffic("decode", f"decode_b{B}h{H}hkv{h_kv}_nk{n_k}_d{d}"),
         },
     }
     if not args.no_cpu_baseline:
@@ -629,7 +630,7 @@ def main(argv=None):
     dominant = max(stages, key=lambda s: per_stage[s])
     dom_t = per_stage[dominant] * 1e-3
     achieved = flops[dominant] / dom_t / 1e12
-    traffic = load_traffic(dominant)
+    traffic = load_traffic(dominant, f"c3_fwdbwd_{'causal' if causal else 'noncausal'}_b{B}h{H}n{n}d{d}")
     fwd_lit = 4 * B * H * n * n * d / (per_stage["fwd"] * 1e-3) / 1e12
     fwd_pct = 100 * flops["fwd"] / (per_stage["fwd"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS
 
