@@ -33,8 +33,8 @@
 // Runs of several heads, summed inside the workgroup, are used only when
 // the partials of one-head runs would not fit the workspace limit.
 //
-// bf16 stage 3 (dQ): mirrors the forward kernel.  8 waves own 32 queries
-// each and keep Q and dO in registers; key blocks of 64 rows (K, V) stream
+// bf16 stage 3 (dQ): mirrors the forward kernel.  8 waves (4 with a sliding
+// window) own 32 queries each and keep Q and dO in registers; key blocks of 64 rows (K, V) stream
 // through LDS.  S^T = K Q^T and dP^T = V dO^T put one query per lane, so
 // LSE_i and D_i are one register each, and dQ^T += K^T dS^T reads K^T
 // through the transposing read.  Key blocks that need no mask for any row of
@@ -212,13 +212,6 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16_kernel(BwdArgs a, int n_kti
       lds_dma16(dst, src, (uint32_t)((4 * lane < valid ? 4 * lane : 0) * 4));
     }
   };
-
-  // Stage buffer 1 starts as zeros: the first iteration's output update
-  // reads it with zero probabilities.
-  for (int i = tid; i < C::QT::kBytes / 16; i += C::kThreads) {
-    reinterpret_cast<u32x4*>(sq[1])[i] = u32x4{};
-    reinterpret_cast<u32x4*>(sdo[1])[i] = u32x4{};
-  }
 
   f32x16 dk[C::kDB], dv[C::kDB];
 #pragma unroll
