@@ -1037,9 +1037,15 @@ hipError_t dq_bf16_w(const BwdArgs& a, hipStream_t s) {
 
 // With a sliding window a 256-row workgroup visits about window + 256 keys
 // while each of its waves needs window + 32: 128-row workgroups waste less.
+// A causal pass with fewer than two 256-row workgroups per compute unit of
+// the 256-CU chip is set by its longest tile: 128-row workgroups balance
+// better there.
+constexpr long long kDqCausalBalanceWgs = 512;
 template <int D, bool CAUSAL>
 hipError_t dq_bf16_t(const BwdArgs& a, hipStream_t s) {
-  return a.window >= 0 ? dq_bf16_w<D, CAUSAL, 4>(a, s) : dq_bf16_w<D, CAUSAL, 8>(a, s);
+  const long long wide_wgs = (long long)a.BH * ((a.n_q + DqCfg<D, 8>::kBM - 1) / DqCfg<D, 8>::kBM);
+  const bool narrow = a.window >= 0 || (CAUSAL && wide_wgs < kDqCausalBalanceWgs);
+  return narrow ? dq_bf16_w<D, CAUSAL, 4>(a, s) : dq_bf16_w<D, CAUSAL, 8>(a, s);
 }
 
 template <int D, bool CAUSAL>

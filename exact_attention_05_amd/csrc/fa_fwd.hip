@@ -642,11 +642,18 @@ hipError_t fwd_bf16_w(const FwdArgs& a, hipStream_t stream) {
 // so windows take 128-row workgroups at any length (H=32, n=4096, d=128:
 // causal w=512 65.6 -> 56.1 us, w=2048 127 -> 116 us).
 constexpr int kShortRows = 512;
+// A causal pass gives its workgroups unequal work (the last query tiles see
+// the most keys).  With fewer than two 256-row workgroups per compute unit of
+// the 256-CU chip the longest tile sets the time, and 128-row workgroups
+// balance better (B=1, H=32, d=128 causal: n=1024 31.5 -> 22.4 us, n=2048
+// 58.1 -> 46.3 us, n=3072 86.9 -> 85.5 us; n=4096, 512 workgroups, equal).
+constexpr long long kCausalBalanceWgs = 512;
 
 template <int D, bool CAUSAL>
 hipError_t fwd_bf16_t(const FwdArgs& a, hipStream_t stream) {
-  return (a.n_q <= kShortRows || a.window >= 0) ? fwd_bf16_w<D, CAUSAL, 4>(a, stream)
-                                                : fwd_bf16_w<D, CAUSAL, 8>(a, stream);
+  const long long wide_wgs = (long long)a.BH * ((a.n_q + Bf16FwdCfg<D, 8>::kBM - 1) / Bf16FwdCfg<D, 8>::kBM);
+  const bool narrow = a.n_q <= kShortRows || a.window >= 0 || (CAUSAL && wide_wgs < kCausalBalanceWgs);
+  return narrow ? fwd_bf16_w<D, CAUSAL, 4>(a, stream) : fwd_bf16_w<D, CAUSAL, 8>(a, stream);
 }
 
 template <int D, bool CAUSAL>
