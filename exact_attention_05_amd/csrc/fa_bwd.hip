@@ -1039,12 +1039,14 @@ hipError_t dq_bf16_w(const BwdArgs& a, hipStream_t s) {
 // while each of its waves needs window + 32: 128-row workgroups waste less.
 // A causal pass with fewer than two 256-row workgroups per compute unit of
 // the 256-CU chip is set by its longest tile: 128-row workgroups balance
-// better there.
+// better there.  Without the mask they pay off only when 256-row workgroups
+// would leave at least half the compute units idle.
 constexpr long long kDqCausalBalanceWgs = 512;
+constexpr long long kDqIdleHalfWgs = 128;
 template <int D, bool CAUSAL>
 hipError_t dq_bf16_t(const BwdArgs& a, hipStream_t s) {
   const long long wide_wgs = (long long)a.BH * ((a.n_q + DqCfg<D, 8>::kBM - 1) / DqCfg<D, 8>::kBM);
-  const bool narrow = a.window >= 0 || (CAUSAL && wide_wgs < kDqCausalBalanceWgs);
+  const bool narrow = a.window >= 0 || (CAUSAL ? wide_wgs < kDqCausalBalanceWgs : wide_wgs <= kDqIdleHalfWgs);
   return narrow ? dq_bf16_w<D, CAUSAL, 4>(a, s) : dq_bf16_w<D, CAUSAL, 8>(a, s);
 }
 

@@ -647,12 +647,18 @@ constexpr int kShortRows = 512;
 // the 256-CU chip the longest tile sets the time, and 128-row workgroups
 // balance better (B=1, H=32, d=128 causal: n=1024 31.5 -> 22.4 us, n=2048
 // 58.1 -> 46.3 us, n=3072 86.9 -> 85.5 us; n=4096, 512 workgroups, equal).
+// Without the mask they pay off only when 256-row workgroups would leave at
+// least half the compute units idle (B=1, d=128: H=32 n=1024 33.1 -> 24.5
+// us, H=8 n=4096 101 -> 74 us; but H=32 n=1536, 192 workgroups, 48.7 ->
+// 51.0 us).
 constexpr long long kCausalBalanceWgs = 512;
+constexpr long long kIdleHalfWgs = 128;
 
 template <int D, bool CAUSAL>
 hipError_t fwd_bf16_t(const FwdArgs& a, hipStream_t stream) {
   const long long wide_wgs = (long long)a.BH * ((a.n_q + Bf16FwdCfg<D, 8>::kBM - 1) / Bf16FwdCfg<D, 8>::kBM);
-  const bool narrow = a.n_q <= kShortRows || a.window >= 0 || (CAUSAL && wide_wgs < kCausalBalanceWgs);
+  const bool narrow = a.n_q <= kShortRows || a.window >= 0 ||
+                      (CAUSAL ? wide_wgs < kCausalBalanceWgs : wide_wgs <= kIdleHalfWgs);
   return narrow ? fwd_bf16_w<D, CAUSAL, 4>(a, stream) : fwd_bf16_w<D, CAUSAL, 8>(a, stream);
 }
 
