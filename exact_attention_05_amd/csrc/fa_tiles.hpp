@@ -118,27 +118,29 @@ struct TileLane {
 };
 
 // Per-lane state for filling Tile<D, ROWS> tiles by direct copies.  The
-// KiB blocks of one wave lie WAVES KiB apart, a whole number of 16-row
-// swizzle periods, so every copy of a lane uses the same chunk position and
-// only its row advances.
+// KiB blocks of one wave lie WAVES KiB apart.  When that is a whole number of
+// 16-row swizzle periods every copy of a lane uses the same chunk position
+// and only its row advances; otherwise (two waves) each copy keeps its own.
 template <int D, int ROWS, int WAVES>
 struct TileDma {
   using T = Tile<D, ROWS>;
   static constexpr int kMine = (T::kKiB + WAVES - 1) / WAVES;  // KiB copies per wave
   static constexpr int kRowStep = WAVES * 1024 / T::kRowBytes;  // rows between a lane's copies
+  static constexpr bool kSamePhase = kRowStep % 16 == 0;
   // Every wave issues kMine copies per tile, or none (so that a count of
   // outstanding copies is the same for every wave that has any).
   static_assert(T::kKiB % WAVES == 0 || T::kKiB < WAVES, "uneven copies per wave");
-  static_assert(kRowStep % 16 == 0, "a wave's copies must be whole swizzle periods apart");
-  int row0;       // tile row of the lane's first copy
-  int col_bytes;  // byte offset of its 16-byte chunk within a row (swizzled)
+  int row0;                                // tile row of the lane's first copy
+  int col_bytes[kSamePhase ? 1 : kMine];   // byte offset of its 16-byte chunk (swizzled)
   int wave;
 
   __device__ __forceinline__ void init(int wave_, int lane) {
     wave = wave_;
     const int off = wave * 1024 + 16 * lane;
     row0 = off / T::kRowBytes;
-    col_bytes = (((off % T::kRowBytes) >> 4) ^ T::swizzle(row0)) * 16;
+#pragma unroll
+    for (int i = 0; i < (kSamePhase ? 1 : kMine); ++i)
+      col_bytes[i] = (((off % T::kRowBytes) >> 4) ^ T::swizzle(row0 + i * kRowStep)) * 16;
   }
 
   // Copy rows [0, ROWS) starting at `src` (row 0 of the tile in global
@@ -149,7 +151,8 @@ struct TileDma {
     for (int i = 0; i < kMine; ++i) {
       const int L = wave + i * WAVES;
       if (T::kKiB % WAVES == 0 || L < T::kKiB) {
-        const uint32_t voff = (uint32_t)(min(row0 + i * kRowStep, valid - 1) * T::kRowBytes + col_bytes);
+        const uint32_t voff =
+            (uint32_t)(min(row0 + i * kRowStep, valid - 1) * T::kRowBytes + col_bytes[kSamePhase ? 0 : i]);
         lds_dma16(lds + L * 1024, src, voff);
       }
     }
@@ -162,7 +165,7 @@ struct TileDma {
     for (int i = 0; i < kMine; ++i) {
       const int L = wave + i * WAVES;
       if (T::kKiB % WAVES == 0 || L < T::kKiB) {
-        const uint32_t voff = (uint32_t)((row0 + i * kRowStep) * T::kRowBytes + col_bytes);
+        const uint32_t voff = (uint32_t)((row0 + i * kRowStep) * T::kRowBytes + col_bytes[kSamePhase ? 0 : i]);
         lds_dma16(lds + L * 1024, src, voff);
       }
     }

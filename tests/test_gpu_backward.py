@@ -46,6 +46,29 @@ def test_c5_bwd_b2_h16_n4096_d128_causal(dev):
                    w.q[b, h], w.k[b, h], w.v[b, h], w.do[b, h], w.scale, True, 2e-2)
 
 
+def test_dkdv_workgroup_widths_agree_bitwise(dev):
+    """dK/dV runs 64-key workgroups (two waves) for causal passes of up to
+    1024 workgroups of 128 keys and 128-key ones above; both give the same
+    bits.  160 heads of n=1024 (1280 workgroups) take the wide kernel, the
+    same heads in two calls of 80 (640) the narrow one.  The wide call is
+    also checked against the oracle on two units."""
+    B, H, n, d = 1, 160, 1024, 64
+    q, k, v, do = workloads.random_qkv(4242, B, H, n, n, d, torch.bfloat16, with_do=True)
+    scale = 1 / math.sqrt(d)
+    qd, kd, vd, dod = (t.to(dev) for t in (q, k, v, do))
+    o, lse = fa.forward(qd, kd, vd, causal=True, scale=scale)
+    _, dk, dv = fa.backward(qd, kd, vd, o, dod, lse, causal=True, scale=scale)
+    halves = [fa.backward(*(t[:, s].contiguous() for t in (qd, kd, vd, o, dod, lse)), causal=True, scale=scale)
+              for s in (slice(0, H // 2), slice(H // 2, H))]
+    torch.cuda.synchronize()
+    for i, name, full in ((1, "dK", dk), (2, "dV", dv)):
+        assert torch.equal(torch.cat([h[i] for h in halves], dim=1), full), name
+    dq = fa.backward(qd, kd, vd, o, dod, lse, causal=True, scale=scale)[0].cpu()
+    for h in (0, H - 1):
+        check_unit(f"wide dK/dV head {h}", (dq[0, h], dk[0, h].cpu(), dv[0, h].cpu()),
+                   q[0, h], k[0, h], v[0, h], do[0, h], scale, True, 2e-2)
+
+
 SHAPES = [(1, 1, 1, 1), (1, 2, 17, 17), (2, 1, 63, 65), (1, 1, 65, 63), (1, 2, 129, 129),
           (1, 1, 257, 300), (1, 1, 300, 257), (1, 1, 5, 600), (1, 1, 600, 5), (1, 1, 1000, 1000)]
 
