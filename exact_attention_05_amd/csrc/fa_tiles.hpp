@@ -134,7 +134,7 @@ struct TileDma {
   int col_bytes[kSamePhase ? 1 : kMine];   // byte offset of its 16-byte chunk (swizzled)
   int wave;
 
-  __device__ __forceinline__ void init(int wave_, int lane) {
+  __host__ __device__ __forceinline__ void init(int wave_, int lane) {
     wave = wave_;
     const int off = wave * 1024 + 16 * lane;
     row0 = off / T::kRowBytes;

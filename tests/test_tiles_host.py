@@ -1,7 +1,8 @@
 """LDS tile addressing (fa_tiles.hpp) checked on the host: the per-lane XOR
 form of TileLane gives the same byte offsets as the swizzled Tile::offset for
 every lane, row block, chunk and head dimension; offsets stay inside the tile
-and the swizzle is a permutation of each row's 16-byte chunks; and the two
+and the swizzle is a permutation of each row's 16-byte chunks; the direct
+copies of 2, 4 or 8 waves put every 16-byte chunk where the offsets say; and the two
 operand reads are free of LDS bank conflicts (16 lanes of a row read cover 16
 distinct 16-byte bank groups, 32 lanes of a transposing read 32 distinct
 8-byte bank pairs).  Compiled with hipcc, no GPU needed."""
@@ -74,10 +75,37 @@ void check() {
         }
 }
 
+// Direct tile copies: the 16 bytes a lane's copy i fetches (row, chunk) land
+// at the byte the lane writes (KiB block L, lane position), which must be
+// Tile::offset(row, chunk); together the waves fill every byte once.
+template <int D, int ROWS, int WAVES>
+void check_dma() {
+  using T = fa::Tile<D, ROWS>;
+  using M = fa::TileDma<D, ROWS, WAVES>;
+  std::set<int> dst;
+  for (int w = 0; w < WAVES; ++w)
+    for (int lane = 0; lane < 64; ++lane) {
+      M m;
+      m.init(w, lane);
+      for (int i = 0; i < M::kMine; ++i) {
+        const int L = w + i * WAVES;
+        if (!(T::kKiB % WAVES == 0 || L < T::kKiB)) continue;
+        const int row = m.row0 + i * M::kRowStep;
+        const int chunk = m.col_bytes[M::kSamePhase ? 0 : i] / 16;
+        EXPECT(row < ROWS && T::offset(row, chunk) == L * 1024 + 16 * lane);
+        dst.insert(L * 1024 + 16 * lane);
+      }
+    }
+  EXPECT((int)dst.size() == T::kBytes / 16);
+}
+
 int main() {
   check<32, 32>(); check<32, 64>();
   check<64, 32>(); check<64, 64>();
   check<128, 32>(); check<128, 64>();
+  check_dma<32, 64, 2>(); check_dma<32, 64, 4>(); check_dma<32, 64, 8>();
+  check_dma<64, 64, 2>(); check_dma<64, 64, 4>(); check_dma<64, 64, 8>();
+  check_dma<128, 64, 2>(); check_dma<128, 64, 4>(); check_dma<128, 64, 8>();
   std::printf("%ld %ld\n", checked, bad);
   return bad != 0;
 }
