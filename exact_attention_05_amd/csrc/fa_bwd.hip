@@ -1058,14 +1058,19 @@ hipError_t dq_bf16_w(const BwdArgs& a, hipStream_t s) {
 // while each of its waves needs window + 32: 128-row workgroups waste less.
 // A causal pass with fewer than two 256-row workgroups per compute unit of
 // the 256-CU chip is set by its longest tile: 128-row workgroups balance
-// better there.  Without the mask they pay off only when 256-row workgroups
-// would leave at least half the compute units idle.
+// better there.  Without the mask they pay off when 256-row workgroups
+// would leave at least half the compute units idle, and for heads of up to
+// 1024 rows (less padding, twice the workgroups: B=16 H=32 d=128 n=512
+// 141.7 -> 121.5 us, n=1024 416.5 -> 393.1 us; but B=1 H=32 n=2048 94.1 ->
+// 97.1 us and n=4096 338 -> 353 us).
 constexpr long long kDqCausalBalanceWgs = 512;
 constexpr long long kDqIdleHalfWgs = 128;
+constexpr int kDqShortRows = 1024;
 template <int D, bool CAUSAL>
 hipError_t dq_bf16_t(const BwdArgs& a, hipStream_t s) {
   const long long wide_wgs = (long long)a.BH * ((a.n_q + DqCfg<D, 8>::kBM - 1) / DqCfg<D, 8>::kBM);
-  const bool narrow = a.window >= 0 || (CAUSAL ? wide_wgs < kDqCausalBalanceWgs : wide_wgs <= kDqIdleHalfWgs);
+  const bool narrow = a.n_q <= kDqShortRows || a.window >= 0 ||
+                      (CAUSAL ? wide_wgs < kDqCausalBalanceWgs : wide_wgs <= kDqIdleHalfWgs);
   return narrow ? dq_bf16_w<D, CAUSAL, 4>(a, s) : dq_bf16_w<D, CAUSAL, 8>(a, s);
 }
 
