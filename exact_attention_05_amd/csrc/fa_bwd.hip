@@ -15,7 +15,8 @@
 // fused multiply-add and can copy both rows straight into LDS.
 //
 // bf16 stage 2 (dK, dV): 4 waves (one per SIMD, 512 registers each; 2 for
-// smaller causal passes and nearly empty grids); each wave owns 32 keys and keeps their K and V rows in registers as matrix-core
+// causal and sliding-window passes and nearly empty grids); each wave owns
+// 32 keys and keeps their K and V rows in registers as matrix-core
 // B operands for the whole pass.  Query stages of 64 rows (Q, dO, and the two
 // row vectors) stream through double-buffered LDS by direct global -> LDS
 // copies.  S = Q K^T and dP = dO V^T land in the accumulator layout with one
@@ -1027,19 +1028,18 @@ hipError_t dkdv_bf16_w(const BwdArgs& a, hipStream_t s) {
 // 64-key workgroups (two waves) balance a causal pass better — its first key
 // tiles see the most queries — visit fewer masked stages under a sliding
 // window, and fill a chip that 128-key workgroups would leave half idle;
-// elsewhere they stream each query stage through LDS for half as many keys
-// and lose 2-3 %.  Measured at d=128 (outputs bitwise equal): causal B=1
-// H=32 n=1024 39.1 -> 37.5 us, n=4096 280.2 -> 277.6 us; whole backward at
-// B=1 H=32 n=4096 with a window of 256, 191.9 -> 179.3 us; full B=1 H=4
-// n=4096 (128 workgroups) 107.7 -> 98.4 us, H=32 512.1 -> 522.6 us.  Masked
-// passes larger than the measured 1024 workgroups keep four waves.
-constexpr long long kDkdvCausalNarrowWgs = 1024;
+// on full passes that fill the chip they stream each query stage through
+// LDS for half as many keys and lose 2-3 %.  Measured at d=128 (outputs
+// bitwise equal): causal B=1 H=32 n=1024 39.1 -> 37.5 us, n=4096 280.2 ->
+// 277.6 us, n=16384 4162 -> 4099 us, B=4 n=4096 1244 -> 1190 us; whole
+// backward at B=1 H=32 n=4096 with a window of 256, 191.9 -> 179.3 us; full
+// B=1 H=4 n=4096 (128 workgroups) 107.7 -> 98.4 us, H=32 512.1 -> 522.6 us.
 constexpr long long kDkdvIdleHalfWgs = 128;
 template <int D, bool CAUSAL>
 hipError_t dkdv_bf16_t(const BwdArgs& a, hipStream_t s) {
   using C4 = DkdvCfg<D, 4>;
   const long long wgs = (long long)((a.n_k + C4::kBK - 1) / C4::kBK) * (a.BH / a.group) * a.slices;
-  const bool narrow = (CAUSAL || a.window >= 0) ? wgs <= kDkdvCausalNarrowWgs : wgs <= kDkdvIdleHalfWgs;
+  const bool narrow = CAUSAL || a.window >= 0 || wgs <= kDkdvIdleHalfWgs;
   return narrow ? dkdv_bf16_w<D, CAUSAL, 2>(a, s) : dkdv_bf16_w<D, CAUSAL, 4>(a, s);
 }
 
