@@ -228,15 +228,22 @@ __global__ __launch_bounds__(WAVES * 64) void bwd_dkdv_bf16_kernel(BwdArgs a, in
   // Probability step for element i of the current sub-block (section
   // "Recomputation": P = exp(scale S - LSE), and dP - D for dS = P o (dP - D)).
   // With MASK, hidden pairs (query past n_q, key past n_k, key after query
-  // when causal) get P = 0.
+  // when causal) get P = 0 and dP - D = 0: a row past n_q reads its LSE and D
+  // from whatever follows the last row vector (the next head's rows, or
+  // workspace slack that nothing writes), so neither may reach dS, not even
+  // as 0 * (dP - D), which is NaN when that slack holds NaN bits.
   auto stage_a = [&](auto mask_tag, int i, int qrow0) __attribute__((always_inline)) {
     const int g4 = i >> 2, e = i & 3;
     float p = fast_exp2(fmaf(s[i], sl2, -lv[g4][e]));
+    float r = dp[i] - dl[g4][e];
     if constexpr (decltype(mask_tag)::value) {
-      if (!Band::in_range(qrow0 + 4 * hi - qvlo + 8 * g4 + e, 0, qvspan)) p = 0.f;
+      if (!Band::in_range(qrow0 + 4 * hi - qvlo + 8 * g4 + e, 0, qvspan)) {
+        p = 0.f;
+        r = 0.f;
+      }
     }
     ex[i] = p;
-    dd[i] = dp[i] - dl[g4][e];
+    dd[i] = r;
     pin(ex[i]);
     pin(dd[i]);
   };
@@ -829,16 +836,39 @@ __global__ __launch_bounds__(256) void bwd_dkdv_f32_kernel(BwdArgs a, int n_ktil
         ds[i] = pv * (dp[i] - sdel[buf][r]);
       }
       // dV^T[d][key] += dO^T P: A = dO^T (row d, k = query), B = P (k = query).
+      // The block's 32 query rows are summed from zero and the block sum is
+      // then added to the running total: a key's gradient over many query
+      // rows (600 rows on 5 keys: values near 15) otherwise carries the
+      // rounding of every addition into a large running sum, about
+      // sqrt(n_q) half-ulps of the result.  One set of block sums serves dV,
+      // then dK (two sets would spill at d = 128).
+      f32x16 bs[C::kDB];
+#pragma unroll
+      for (int db = 0; db < C::kDB; ++db) bs[db] = f32x16{};
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int r = 8 * (i >> 2) + 4 * hi + (i & 3);
 #pragma unroll
-        for (int db = 0; db < C::kDB; ++db) {
-          dv[db] = mfma_f32(sdo[buf][r * C::kStride + 32 * db + l32], p[i], dv[db]);
-          dk[db] = mfma_f32(sq[buf][r * C::kStride + 32 * db + l32], ds[i], dk[db]);
-        }
+        for (int db = 0; db < C::kDB; ++db)
+          bs[db] = mfma_f32(sdo[buf][r * C::kStride + 32 * db + l32], p[i], bs[db]);
       }
-      settle_acc(dv, dk);
+      settle_acc(bs);
+#pragma unroll
+      for (int db = 0; db < C::kDB; ++db) {
+        dv[db] += bs[db];
+        bs[db] = f32x16{};
+      }
+      // dK^T[d][key] += Q^T dS, the same way.
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int r = 8 * (i >> 2) + 4 * hi + (i & 3);
+#pragma unroll
+        for (int db = 0; db < C::kDB; ++db)
+          bs[db] = mfma_f32(sq[buf][r * C::kStride + 32 * db + l32], ds[i], bs[db]);
+      }
+      settle_acc(bs);
+#pragma unroll
+      for (int db = 0; db < C::kDB; ++db) dk[db] += bs[db];
     }
     if (b + 1 < nblocks) swrite(buf ^ 1);
     __syncthreads();

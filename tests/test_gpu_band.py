@@ -9,7 +9,7 @@ import torch
 import exact_attention_05_amd as fa
 import oracle
 import workloads
-from parity import RTOL_BF16_TERMS, TOL_LSE, assert_close, np64, require_gpu, tol_for
+from parity import TOL_LSE, assert_close, bf16_grad_rtol, np64, require_gpu, tol_for
 
 pytestmark = pytest.mark.gpu
 
@@ -64,9 +64,9 @@ def check(tag, got, q, k, v, do, scale, causal, off, w, dtype):
 
         mags = (scale * np.abs(ds) @ np.abs(ke), fold(scale * t(np.abs(ds)) @ np.abs(q64)),
                 fold(t(p) @ np.abs(do64)))
-        tol, rtol = tol_for(dtype), RTOL_BF16_TERMS
+        tol, rtol = tol_for(dtype), bf16_grad_rtol(dtype, q64.shape[2], k64.shape[2], g)
     else:
-        tol, rtol, mags = 2e-5, 0.0, (None, None, None)
+        tol, rtol, mags = tol_for(dtype), 0.0, (None, None, None)
     for name, g, r, m in zip(("dQ", "dK", "dV"), (dq, dk, dv), (rq, rk, rv), mags):
         assert_close(f"{name} {tag}", g, r, tol, rtol, mag=m)
 

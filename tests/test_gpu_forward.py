@@ -50,30 +50,18 @@ def test_c2_single_head_n4096_d64(dev, dtype):
         assert torch.equal(ls_, lse[:, :, start:start + 128])
 
 
-def _sampled_rows(n_heads, n, count, seed):
-    g = torch.Generator().manual_seed(seed)
-    r = torch.randperm(n_heads * n, generator=g)[:count].tolist()
-    rows = [(0, x // n, x % n) for x in r]
-    # always include the first and last rows of a head
-    return rows + [(0, 0, 0), (0, n_heads - 1, n - 1)]
-
-
 @pytest.mark.parametrize("causal", [False, True])
 def test_c3_b1_h32_n4096_d128(dev, causal):
+    # Every head, element by element against the full fp64 oracle (its
+    # 4096 x 4096 score matrix materialised per head).
     w = workloads.c3(causal)
     o, lse = run_fwd(dev, w.q, w.k, w.v, w.scale, causal)
-    rows = _sampled_rows(32, 4096, 512, 303 + int(causal))
-    ro, rl = oracle.attention_rows(w.q.float().numpy(), w.k.float().numpy(), w.v.float().numpy(),
-                                   rows, w.scale, causal)
-    got_o = np.stack([np64(o[b, h, i]) for b, h, i in rows])
-    got_l = np.array([float(lse[b, h, i]) for b, h, i in rows])
-    assert_close(f"O rows {w.name}", got_o, ro, tol_for(w.q.dtype))
-    assert_close(f"LSE rows {w.name}", got_l, rl, TOL_LSE)
-    # One whole head against the full oracle.
-    h = 17
-    fo, fl = oracle.attention_fwd(np64(w.q[0, h]), np64(w.k[0, h]), np64(w.v[0, h]), w.scale, causal)
-    assert_close(f"O head {h}", o[0, h], fo, tol_for(w.q.dtype))
-    assert_close(f"LSE head {h}", lse[0, h], fl, TOL_LSE)
+    worst_o = worst_l = 0.0
+    for h in range(w.q.shape[1]):
+        fo, fl = oracle.attention_fwd(np64(w.q[0, h]), np64(w.k[0, h]), np64(w.v[0, h]), w.scale, causal)
+        worst_o = max(worst_o, assert_close(f"O {w.name} head {h}", o[0, h], fo, tol_for(w.q.dtype)))
+        worst_l = max(worst_l, assert_close(f"LSE {w.name} head {h}", lse[0, h], fl, TOL_LSE))
+    print(f"{w.name}: all 32 heads, max |err| O {worst_o:.3e}, LSE {worst_l:.3e}")
 
 
 def test_c4_long_context_causal_n16384(dev):
@@ -84,7 +72,7 @@ def test_c4_long_context_causal_n16384(dev):
                                    rows, w.scale, True)
     got_o = np.stack([np64(o[b, h, i]) for b, h, i in rows])
     got_l = np.array([float(lse[b, h, i]) for b, h, i in rows])
-    assert_close("O rows c4", got_o, ro, tol_for(w.q.dtype))
+    assert_close("O rows c4", got_o, ro, tol_for(w.q.dtype), rounded_bf16=True)
     assert_close("LSE rows c4", got_l, rl, TOL_LSE)
 
 
