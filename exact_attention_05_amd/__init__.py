@@ -4,7 +4,8 @@ The computation runs in hand-written HIP kernels behind the C ABI declared in
 ``include/fa.h`` (library ``lib/libfa.so``); this package is its Python
 binding.  See ``forward`` and ``backward``; ``decode`` (split-KV decoding
 against a long K/V cache) and ``lse_merge`` (attention results over disjoint
-key sets combined into the result over all keys).
+key sets combined into the result over all keys) and ``forward_merge`` (a
+forward pass that merges into a prior result in its epilogue).
 """
 from .binding import (  # noqa: F401
     FA_DTYPE_BF16,
@@ -26,6 +27,7 @@ from .binding import (  # noqa: F401
     decode_splits,
     decode_workspace_size,
     forward,
+    forward_merge,
     lse_merge,
     lib,
     library_path,

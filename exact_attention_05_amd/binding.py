@@ -18,7 +18,7 @@ __all__ = [
     "FA_ERR_ALIGNMENT", "FA_DTYPE_FP32", "FA_DTYPE_BF16", "FaError", "library_path", "lib",
     "forward", "backward", "backward_workspace_size", "backward_workspace", "workspace_delta",
     "backward_preprocess", "backward_dkdv", "backward_dq", "status_string", "version",
-    "lse_merge", "decode", "decode_splits", "decode_workspace_size",
+    "lse_merge", "decode", "decode_splits", "decode_workspace_size", "forward_merge",
 ]
 
 FA_OK = 0
@@ -79,6 +79,8 @@ def lib() -> ctypes.CDLL:
         L.fa_backward_ext.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
                                       i, i, i, i, i, i, f, i, i, i, i, vp]
         L.fa_backward_ext.restype = i
+        L.fa_forward_merge.argtypes = [vp, vp, vp, vp, vp, i, vp, vp, i, i, i, i, i, i, i, f, i, i, i, i, vp]
+        L.fa_forward_merge.restype = i
         ll = ctypes.c_longlong
         L.fa_lse_merge.argtypes = [vp, vp, vp, vp, i, ll, i, i, i, vp]
         L.fa_lse_merge.restype = i
@@ -183,6 +185,40 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None,
                                   n_k, d, _scale(scale, d), int(bool(causal)), _DTYPES[q.dtype],
                                   _stream(q.device))
         _check(st, "fa_forward_gqa")
+    return out, lse
+
+
+def forward_merge(q, k, v, o_prior, lse_prior, causal: bool = False, scale: float | None = None,
+                  q_offset: int = 0, window: int | None = None, out=None, lse=None,
+                  out_dtype: torch.dtype | None = None):
+    """Attention of q over this call's k, v merged into a prior result over
+    other keys (fa_forward_merge): returns (o, lse) over both key sets.
+
+    o_prior (B,H,n_q,d) float32 or q's dtype and lse_prior (B,H,n_q) float32
+    hold the result so far (lse_prior = -inf: no prior for that row).  ``out``
+    and ``lse`` may be o_prior and lse_prior themselves (in-place
+    accumulation); otherwise they are allocated with ``out_dtype`` (default
+    o_prior's dtype).  Masks as forward()."""
+    B, H, n_q, n_k, d = _check_qkv(q, k, v)
+    if o_prior.shape != q.shape or o_prior.dtype not in (torch.float32, q.dtype) or \
+            not o_prior.is_contiguous() or o_prior.device != q.device:
+        raise ValueError("o_prior must be a contiguous (B, H, n_q, d) float32 or q-dtype tensor on q's device")
+    if lse_prior.shape != (B, H, n_q) or lse_prior.dtype != torch.float32 or not lse_prior.is_contiguous():
+        raise ValueError("lse_prior must be a contiguous float32 (B, H, n_q) tensor")
+    if out is None:
+        out = torch.empty(q.shape, dtype=o_prior.dtype if out_dtype is None else out_dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, n_q), dtype=torch.float32, device=q.device)
+    if out.shape != q.shape or out.dtype not in (torch.float32, q.dtype) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous (B, H, n_q, d) float32 or q-dtype tensor")
+    if lse.shape != (B, H, n_q) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 (B, H, n_q) tensor")
+    st = lib().fa_forward_merge(_ptr(q), _ptr(k), _ptr(v), _ptr(o_prior), _ptr(lse_prior),
+                                _DTYPES[o_prior.dtype], _ptr(out), _ptr(lse), _DTYPES[out.dtype],
+                                B, H, k.shape[1], n_q, n_k, d, _scale(scale, d), int(bool(causal)),
+                                int(q_offset), -1 if window is None else int(window), _DTYPES[q.dtype],
+                                _stream(q.device))
+    _check(st, "fa_forward_merge")
     return out, lse
 
 

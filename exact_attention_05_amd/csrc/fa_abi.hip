@@ -121,6 +121,21 @@ fa::BwdArgs make_bwd(const void* q, const void* k, const void* v, const void* o,
 
 int status_of(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH; }
 
+fa::FwdArgs make_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                     int H_kv, int n_q, int n_k, float scale, int q_offset, int window) {
+  fa::FwdArgs a;
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+  a.BH = B * H; a.H = H; a.group = H / H_kv; a.n_q = n_q; a.n_k = n_k;
+  a.q_offset = q_offset; a.window = window;
+  a.scale = scale;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.o_prior = nullptr;
+  a.lse_prior = nullptr;
+  a.prior_f32 = 0;
+  a.out_f32 = 0;
+  return a;
+}
+
 // Split-KV decoding.  Chunks hold whole key blocks and at least
 // kDecodeMinChunk keys; the default aims at kDecodeTargetWgs workgroups (one
 // per compute unit).
@@ -210,15 +225,45 @@ int forward_impl(const void* q, const void* k, const void* v, void* o, float* ls
   if (dtype == FA_DTYPE_BF16 && starved(B, H, n_q, n_k, d))
     return decode_launch(q, k, v, o, lse, nullptr, 0, B, H, H_kv, n_q, n_k, d, scale, causal,
                          q_offset, window, 1, stream);
-  fa::FwdArgs a;
-  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
-  a.BH = B * H; a.H = H; a.group = H / H_kv; a.n_q = n_q; a.n_k = n_k;
-  a.q_offset = q_offset; a.window = window;
-  a.scale = scale;
-  a.scale_log2 = scale * 1.4426950408889634f;
+  fa::FwdArgs a = make_fwd(q, k, v, o, lse, B, H, H_kv, n_q, n_k, scale, q_offset, window);
   hipStream_t s = static_cast<hipStream_t>(stream);
   return status_of(dtype == FA_DTYPE_BF16 ? fa::launch_fwd_bf16(a, d, causal != 0, s)
                                           : fa::launch_fwd_f32(a, d, causal != 0, s));
+}
+
+// Byte ranges [p, p + n) and [r, r + m) overlap.
+bool overlap(const void* p, size_t n, const void* r, size_t m) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p), b = reinterpret_cast<uintptr_t>(r);
+  return a < b + m && b < a + n;
+}
+
+int forward_merge_impl(const void* q, const void* k, const void* v, const void* o_prior,
+                       const float* lse_prior, int prior_dtype, void* o, float* lse, int out_dtype,
+                       int B, int H, int H_kv, int n_q, int n_k, int d, float scale, int causal,
+                       int q_offset, int window, int dtype, void* stream) {
+  int st = first_error(check_sizes(B, H, n_q, n_k, d, dtype), check_kv_heads(H, H_kv),
+                       check_band(n_q, n_k, q_offset, window), check_scale_causal(scale, causal),
+                       check_tensor(q), check_tensor(k), check_tensor(v), check_tensor(o_prior),
+                       check_rowvec(lse_prior), check_tensor(o), check_rowvec(lse));
+  if (st != FA_OK) return st;
+  // The running result is float32 or the input dtype (float32 inputs: float32 only).
+  const auto acc_ok = [dtype](int t) { return t == FA_DTYPE_FP32 || t == dtype; };
+  if (!acc_ok(prior_dtype) || !acc_ok(out_dtype)) return FA_ERR_UNSUPPORTED;
+  // o may be o_prior itself (same dtype) and lse may be lse_prior; any other
+  // overlap between them is refused.
+  const size_t rows = (size_t)B * H * n_q;
+  const size_t pb = rows * d * (prior_dtype == FA_DTYPE_FP32 ? 4 : 2);
+  const size_t ob = rows * d * (out_dtype == FA_DTYPE_FP32 ? 4 : 2);
+  if (o == o_prior ? prior_dtype != out_dtype : overlap(o, ob, o_prior, pb)) return FA_ERR_INVALID_ARG;
+  if (lse != lse_prior && overlap(lse, rows * 4, lse_prior, rows * 4)) return FA_ERR_INVALID_ARG;
+  fa::FwdArgs a = make_fwd(q, k, v, o, lse, B, H, H_kv, n_q, n_k, scale, q_offset, window);
+  a.o_prior = o_prior;
+  a.lse_prior = lse_prior;
+  a.prior_f32 = prior_dtype == FA_DTYPE_FP32;
+  a.out_f32 = out_dtype == FA_DTYPE_FP32;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return status_of(dtype == FA_DTYPE_BF16 ? fa::launch_fwd_merge_bf16(a, d, causal != 0, s)
+                                          : fa::launch_fwd_merge_f32(a, d, causal != 0, s));
 }
 
 int backward_impl(const void* q, const void* k, const void* v, const void* o, const void* dO,
@@ -348,6 +393,14 @@ int fa_forward_ext(const void* q, const void* k, const void* v, void* o, float* 
                    int window, int dtype, void* stream) {
   return forward_impl(q, k, v, o, lse, B, H, H_kv, n_q, n_k, d, scale, causal, dtype, stream,
                       q_offset, window);
+}
+
+int fa_forward_merge(const void* q, const void* k, const void* v, const void* o_prior,
+                     const float* lse_prior, int prior_dtype, void* o, float* lse, int out_dtype,
+                     int B, int H, int H_kv, int n_q, int n_k, int d, float scale, int causal,
+                     int q_offset, int window, int dtype, void* stream) {
+  return forward_merge_impl(q, k, v, o_prior, lse_prior, prior_dtype, o, lse, out_dtype, B, H, H_kv,
+                            n_q, n_k, d, scale, causal, q_offset, window, dtype, stream);
 }
 
 int fa_backward(const void* q, const void* k, const void* v, const void* o, const void* dO,

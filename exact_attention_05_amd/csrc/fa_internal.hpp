@@ -23,6 +23,14 @@ struct FwdArgs {
   int window;       // sliding-window half-width, or -1 for none (see Band)
   float scale;      // softmax scale on q . k
   float scale_log2; // scale * log2(e): scores are exponentiated base 2
+  // Merge launches only: the rows' prior result over other keys, o_prior
+  // (B,H,n_q,d) and its natural-log lse_prior (B,H,n_q); o and lse receive
+  // the result over both key sets.  prior_f32 / out_f32: o_prior / o hold
+  // float32 (else bf16; the fp32 kernel takes float32 only).
+  const void* o_prior;
+  const float* lse_prior;
+  int prior_f32;
+  int out_f32;
 };
 
 // Arguments of the backward stages.
@@ -204,6 +212,9 @@ struct MergeArgs {
 // of the launch.  Shapes were validated by the caller.
 hipError_t launch_fwd_bf16(const FwdArgs& a, int d, bool causal, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdArgs& a, int d, bool causal, hipStream_t stream);
+// The same passes with the epilogue merging into a.o_prior, a.lse_prior.
+hipError_t launch_fwd_merge_bf16(const FwdArgs& a, int d, bool causal, hipStream_t stream);
+hipError_t launch_fwd_merge_f32(const FwdArgs& a, int d, bool causal, hipStream_t stream);
 
 hipError_t launch_bwd_preprocess(const BwdArgs& a, int d, bool bf16, hipStream_t stream);
 hipError_t launch_bwd_dkdv_bf16(const BwdArgs& a, int d, bool causal, hipStream_t stream);

@@ -175,8 +175,41 @@ int fa_forward_ext(const void* q, const void* k, const void* v, void* o, float* 
                    int B, int H, int H_kv, int n_q, int n_k, int d, float scale,
                    int causal, int q_offset, int window, int dtype, void* stream);
 
+/* Forward pass merged into a prior result: one step of attention whose keys
+ * arrive in chunks ("Attention Mechanism", section 16 "Ring Attention": each
+ * worker holds a slice of the keys and the query rows visit every slice),
+ * with the online softmax's rescaling ("Attention Mechanism", section 13:
+ * the old output is weighted by the exponential of the change of the running
+ * maximum) applied to whole results in the kernel's epilogue, so a step needs
+ * no separate merge pass.
+ *   o_prior, lse_prior  the rows' result over the keys seen so far:
+ *                       (B,H,n_q,d) in prior_dtype and (B,H,n_q) float32
+ *                       natural-log LSE; a row with lse_prior = -inf has no
+ *                       prior (its o_prior is never read and may hold anything)
+ *   o, lse              receive the result over those keys and this call's
+ *                       k, v: (B,H,n_q,d) in out_dtype and (B,H,n_q) float32
+ * With this call's own result (O_n, LSE_n) -- what fa_forward_ext would
+ * return for the same arguments -- lse = ln(exp(lse_prior) + exp(LSE_n)) and
+ * o = exp(lse_prior - lse) o_prior + exp(LSE_n - lse) O_n; a row without keys
+ * on either side gets o = 0, lse = -inf.  Chaining calls over key chunks
+ * [a, b) with query offset q_offset - a, starting from lse_prior = -inf,
+ * gives the result over all keys.  prior_dtype and out_dtype are each
+ * FA_DTYPE_FP32 or dtype (bf16 inputs may keep a float32 running result);
+ * else FA_ERR_UNSUPPORTED.  o may be o_prior itself when the two dtypes
+ * match and lse may be lse_prior (in-place accumulation); any other overlap
+ * between them is FA_ERR_INVALID_ARG.  The other arguments, alignment and
+ * errors as fa_forward_ext; always the forward kernel (never the split-key
+ * route), one launch on `stream`. */
+int fa_forward_merge(const void* q, const void* k, const void* v, const void* o_prior,
+                     const float* lse_prior, int prior_dtype, void* o, float* lse, int out_dtype,
+                     int B, int H, int H_kv, int n_q, int n_k, int d, float scale, int causal,
+                     int q_offset, int window, int dtype, void* stream);
+
 /* Backward pass of fa_forward_ext (same q_offset and window); workspace as
- * for fa_backward_gqa. */
+ * for fa_backward_gqa.  For attention over key chunks (fa_forward_merge),
+ * the call for one chunk with the final o and lse over all keys gives that
+ * chunk's exact dk, dv and its share of dq: the full dq is the sum over the
+ * chunks. */
 int fa_backward_ext(const void* q, const void* k, const void* v, const void* o,
                     const void* dO, const float* lse, void* dq, void* dk, void* dv,
                     void* workspace, size_t workspace_bytes,

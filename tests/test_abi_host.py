@@ -259,3 +259,32 @@ def test_gqa_runs_grow_when_the_partials_would_pass_4_gib():
     got = L.fa_backward_gqa_workspace_size(1, 64, 1, 16, 131072, 128, 1)
     assert got == base + 2 * 32 * 131072 * 128 * 4
 
+
+
+def fmerge(q=P, k=P, v=P, op=ctypes.c_void_p(0x300000), lp=ctypes.c_void_p(0x380000), pdt=1,
+           o=ctypes.c_void_p(0x400000), lse=ctypes.c_void_p(0x480000), odt=1, B=1, H=2, H_kv=2,
+           n_q=8, n_k=8, d=64, scale=0.125, causal=0, q_offset=0, window=-1, dtype=1):
+    return fa.lib().fa_forward_merge(q, k, v, op, lp, pdt, o, lse, odt, B, H, H_kv, n_q, n_k, d, scale,
+                                     causal, q_offset, window, dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(op=None), fa.FA_ERR_INVALID_ARG),
+    (dict(lp=None), fa.FA_ERR_INVALID_ARG),
+    (dict(o=None), fa.FA_ERR_INVALID_ARG),
+    (dict(op=MIS), fa.FA_ERR_ALIGNMENT),
+    (dict(lp=ctypes.c_void_p(0x380002)), fa.FA_ERR_ALIGNMENT),
+    (dict(pdt=2), fa.FA_ERR_UNSUPPORTED),
+    (dict(odt=5), fa.FA_ERR_UNSUPPORTED),
+    (dict(dtype=0, pdt=1, odt=0), fa.FA_ERR_UNSUPPORTED),   # float32 inputs keep a float32 result
+    (dict(dtype=0, pdt=0, odt=1), fa.FA_ERR_UNSUPPORTED),
+    (dict(o=ctypes.c_void_p(0x300000), odt=0), fa.FA_ERR_INVALID_ARG),  # in place, dtypes differ
+    (dict(o=ctypes.c_void_p(0x300010)), fa.FA_ERR_INVALID_ARG),         # partial overlap of o and o_prior
+    (dict(lse=ctypes.c_void_p(0x380004)), fa.FA_ERR_INVALID_ARG),       # partial overlap of the LSE rows
+    (dict(d=48), fa.FA_ERR_UNSUPPORTED),
+    (dict(H_kv=3), fa.FA_ERR_INVALID_ARG),
+    (dict(window=-2), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), fa.FA_ERR_INVALID_ARG),
+])
+def test_forward_merge_rejects(kw, code):
+    assert fmerge(**kw) == code
