@@ -1,10 +1,12 @@
 """Build the HIP library ``libfa.so`` in-tree for gfx950.
 
     python -m exact_attention_05_amd.build      # or: python exact_attention_05_amd/build.py
+    python -m exact_attention_05_amd.build --incremental
 
 Compiles every ``csrc/*.hip`` with hipcc (in parallel) and links them into
 ``exact_attention_05_amd/lib/libfa.so``.  Packed-fp32 VALU instructions are
-disabled for all device code.
+disabled for all device code.  With ``--incremental`` an object newer than
+its source and every header is kept.
 """
 from __future__ import annotations
 
@@ -55,8 +57,22 @@ def compile_flags() -> list[str]:
 FILE_FLAGS: dict[str, list[str]] = {}
 
 
-def _compile(src: str) -> str:
+def _headers() -> list[str]:
+    hs = [os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hpp")]
+    return hs + [os.path.join(INCLUDE, f) for f in os.listdir(INCLUDE) if f.endswith(".h")]
+
+
+def _up_to_date(src: str, obj: str) -> bool:
+    if not os.path.exists(obj):
+        return False
+    t = os.path.getmtime(obj)
+    return all(os.path.getmtime(f) < t for f in [src, *_headers(), os.path.abspath(__file__)])
+
+
+def _compile(src: str, incremental: bool = False) -> str:
     obj = os.path.join(OBJ_DIR, os.path.basename(src) + ".o")
+    if incremental and _up_to_date(src, obj):
+        return obj
     extra = FILE_FLAGS.get(os.path.basename(src), [])
     cmd = [hipcc(), *compile_flags(), *extra, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -71,13 +87,13 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
+def build(verbose: bool = True, incremental: bool = False) -> str:
     os.makedirs(OBJ_DIR, exist_ok=True)
     os.makedirs(OUT_DIR, exist_ok=True)
     srcs = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
     workers = max(1, min(len(srcs), int(os.environ.get("MAX_JOBS", "8"))))
     with cf.ThreadPoolExecutor(workers) as ex:
-        objs = list(ex.map(_compile, srcs))
+        objs = list(ex.map(lambda f: _compile(f, incremental), srcs))
     tmp = OUT + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -90,4 +106,4 @@ def build(verbose: bool = True) -> str:
 
 
 if __name__ == "__main__":
-    build()
+    build(incremental="--incremental" in sys.argv[1:])
