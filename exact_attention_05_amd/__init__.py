@@ -13,11 +13,13 @@ from .binding import (  # noqa: F401
     FA_ERR_ALIGNMENT,
     FA_ERR_INVALID_ARG,
     FA_ERR_LAUNCH,
+    FA_ERR_TOO_LARGE,
     FA_ERR_UNSUPPORTED,
     FA_ERR_WORKSPACE,
     FA_OK,
     FaError,
     backward,
+    backward_noalloc,
     backward_dkdv,
     backward_dq,
     backward_preprocess,

@@ -15,10 +15,10 @@ import torch
 
 __all__ = [
     "FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_WORKSPACE", "FA_ERR_LAUNCH",
-    "FA_ERR_ALIGNMENT", "FA_DTYPE_FP32", "FA_DTYPE_BF16", "FaError", "library_path", "lib",
+    "FA_ERR_ALIGNMENT", "FA_ERR_TOO_LARGE", "FA_DTYPE_FP32", "FA_DTYPE_BF16", "FaError", "library_path", "lib",
     "forward", "backward", "backward_workspace_size", "backward_workspace", "workspace_delta",
     "backward_preprocess", "backward_dkdv", "backward_dq", "status_string", "version",
-    "lse_merge", "decode", "decode_splits", "decode_workspace_size", "forward_merge",
+    "lse_merge", "decode", "decode_splits", "decode_workspace_size", "forward_merge", "backward_noalloc",
 ]
 
 FA_OK = 0
@@ -27,6 +27,7 @@ FA_ERR_UNSUPPORTED = 2
 FA_ERR_WORKSPACE = 3
 FA_ERR_LAUNCH = 4
 FA_ERR_ALIGNMENT = 5
+FA_ERR_TOO_LARGE = 6
 FA_DTYPE_FP32 = 0
 FA_DTYPE_BF16 = 1
 
@@ -81,6 +82,8 @@ def lib() -> ctypes.CDLL:
         L.fa_backward_ext.restype = i
         L.fa_forward_merge.argtypes = [vp, vp, vp, vp, vp, i, vp, vp, i, i, i, i, i, i, i, f, i, i, i, i, vp]
         L.fa_forward_merge.restype = i
+        L.fa_backward_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp]
+        L.fa_backward_noalloc.restype = i
         ll = ctypes.c_longlong
         L.fa_lse_merge.argtypes = [vp, vp, vp, vp, i, ll, i, i, i, vp]
         L.fa_lse_merge.restype = i
@@ -272,6 +275,23 @@ def backward(q, k, v, o, do, lse, causal: bool = False, scale: float | None = No
                                    B, H, h_kv, n_q, n_k, d, _scale(scale, d), int(bool(causal)),
                                    _DTYPES[q.dtype], _stream(q.device))
         _check(st, "fa_backward_gqa")
+    return dq, dk, dv
+
+
+def backward_noalloc(q, k, v, o, do, lse, dq, dk, dv, causal: bool = False, scale: float | None = None):
+    """fa_backward_noalloc: the backward pass into the caller's dq, dk, dv
+    with the library's fixed device scratch as the workspace (no device
+    allocation by the library or here).  One K/V head per query head."""
+    B, H, n_q, n_k, d = _check_qkv(q, k, v)
+    _require_mha(q, k, "backward_noalloc")
+    for name, t, ref in (("o", o, q), ("do", do, q), ("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        _check_like(name, t, ref)
+    if lse.shape != (B, H, n_q) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 (B, H, n_q) tensor")
+    st = lib().fa_backward_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq),
+                                   _ptr(dk), _ptr(dv), B, H, n_q, n_k, d, _scale(scale, d),
+                                   int(bool(causal)), _DTYPES[q.dtype], _stream(q.device))
+    _check(st, "fa_backward_noalloc")
     return dq, dk, dv
 
 

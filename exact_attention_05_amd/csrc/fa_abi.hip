@@ -10,6 +10,15 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
+
+// Scratch memory of fa_backward_noalloc: the backward workspace (the two
+// float32 row vectors D and LSE * log2(e)) for callers that cannot allocate
+// device memory.  Every GPU the library runs on holds its own copy until the
+// process ends.  Host code never uses this name as an address: the address
+// on a device comes from hipGetSymbolAddress (noalloc_scratch below).
+constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
 
 namespace {
 
@@ -307,6 +316,32 @@ int backward_impl(const void* q, const void* k, const void* v, const void* o, co
   return status_of(e);
 }
 
+// The device address of `scratch` on the device of `stream` (which must be
+// the calling thread's current device), looked up once per device with that
+// device current and kept.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int noalloc_scratch(void* stream, void** out) {
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return FA_ERR_LAUNCH;
+  if (stream != nullptr) {
+    hipDevice_t dev = -1;
+    if (hipStreamGetDevice(static_cast<hipStream_t>(stream), &dev) != hipSuccess || dev != cur)
+      return FA_ERR_INVALID_ARG;
+  }
+  if (cur < 0 || cur >= kMaxDevices) return FA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[cur] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return FA_ERR_LAUNCH;
+    g_scratch_ptr[cur] = p;
+  }
+  *out = g_scratch_ptr[cur];
+  return FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -321,6 +356,7 @@ const char* fa_status_string(int status) {
     case FA_ERR_WORKSPACE: return "workspace missing or too small";
     case FA_ERR_LAUNCH: return "kernel launch failed";
     case FA_ERR_ALIGNMENT: return "tensor pointer misaligned";
+    case FA_ERR_TOO_LARGE: return "sizes exceed the fixed scratch of the non-allocating entry point";
     default: return "unknown status";
   }
 }
@@ -409,6 +445,24 @@ int fa_backward(const void* q, const void* k, const void* v, const void* o, cons
                 int causal, int dtype, void* stream) {
   return backward_impl(q, k, v, o, dO, lse, dq, dk, dv, workspace, workspace_bytes, B, H, H, n_q,
                        n_k, d, scale, causal, dtype, stream);
+}
+
+int fa_backward_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                        const float* lse, void* dq, void* dk, void* dv, int B, int H, int n_q, int n_k,
+                        int d, float scale, int causal, int dtype, void* stream) {
+  // Everything that can be checked without the GPU first, the scratch size
+  // included; the scratch is only looked up for a call that will launch.
+  int st = first_error(check_sizes(B, H, n_q, n_k, d, dtype), check_scale_causal(scale, causal),
+                       check_tensor(q), check_tensor(k), check_tensor(v), check_tensor(o),
+                       check_tensor(dO), check_rowvec(lse), check_tensor(dq), check_tensor(dk),
+                       check_tensor(dv));
+  if (st != FA_OK) return st;
+  if (ws_bytes(B, H, n_q) > kNoAllocScratchBytes) return FA_ERR_TOO_LARGE;
+  void* ws = nullptr;
+  st = noalloc_scratch(stream, &ws);
+  if (st != FA_OK) return st;
+  return backward_impl(q, k, v, o, dO, lse, dq, dk, dv, ws, kNoAllocScratchBytes, B, H, H, n_q, n_k,
+                       d, scale, causal, dtype, stream);
 }
 
 int fa_backward_gqa(const void* q, const void* k, const void* v, const void* o, const void* dO,

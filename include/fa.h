@@ -75,7 +75,8 @@ typedef enum fa_status {
   FA_ERR_UNSUPPORTED = 2,   /* head width d or dtype this build does not provide */
   FA_ERR_WORKSPACE = 3,     /* backward workspace missing or smaller than required */
   FA_ERR_LAUNCH = 4,        /* the HIP runtime refused a kernel launch */
-  FA_ERR_ALIGNMENT = 5      /* a tensor pointer is not aligned as required */
+  FA_ERR_ALIGNMENT = 5,     /* a tensor pointer is not aligned as required */
+  FA_ERR_TOO_LARGE = 6      /* sizes beyond the fixed scratch of fa_backward_noalloc */
 } fa_status;
 
 typedef enum fa_dtype {
@@ -109,6 +110,30 @@ int fa_backward(const void* q, const void* k, const void* v, const void* o,
                 void* workspace, size_t workspace_bytes,
                 int B, int H, int n_q, int n_k, int d, float scale, int causal,
                 int dtype, void* stream);
+
+/* fa_backward without a workspace argument and without allocating anything,
+ * for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.  The
+ * workspace is a fixed scratch array of 16 MiB that the library holds on
+ * each GPU it runs on until the process ends, so B*H*n_q may be at most
+ * about 2 million rows (2 * round_up(4 B*H*n_q + 16, 256) <= 16 MiB);
+ * larger sizes return FA_ERR_TOO_LARGE before anything is launched.  The
+ * first call on each device is its set-up: the library looks up the
+ * scratch's device address (hipGetSymbolAddress), and the HIP runtime may
+ * map the array on that device then -- make one call before a graph capture
+ * or an allocation-free region.  Later calls touch no allocator.  One K/V
+ * head per query head.  Results are bit for bit those of fa_backward.
+ * `stream` must belong to the calling thread's current device (else
+ * FA_ERR_INVALID_ARG).  All calls on one GPU share its scratch: two calls
+ * that overlap in time on one GPU (different streams, or threads) race and
+ * must be ordered by the caller.  The scratch needs no clearing: each call
+ * writes the row vectors before it reads them, and the few entries read past
+ * their end (rows past n_q, masked) never reach a result.  Other arguments
+ * and errors as fa_backward. */
+int fa_backward_noalloc(const void* q, const void* k, const void* v, const void* o,
+                        const void* dO, const float* lse, void* dq, void* dk, void* dv,
+                        int B, int H, int n_q, int n_k, int d, float scale, int causal,
+                        int dtype, void* stream);
 
 /* Backward stage 1: writes into `workspace` the float32 row sums
  * D_i = sum_c dO_ic * o_ic (the row term of the softmax gradient, from the

@@ -40,11 +40,11 @@ def test_library_exports_every_declared_function():
 
 def test_status_strings_cover_every_code():
     seen = set()
-    for code in range(6):
+    for code in range(7):
         s = fa.status_string(code)
         assert s and s != "unknown status"
         seen.add(s)
-    assert len(seen) == 6
+    assert len(seen) == 7
     assert fa.status_string(99) == "unknown status"
     assert fa.status_string(-1) == "unknown status"
 
@@ -288,3 +288,19 @@ def fmerge(q=P, k=P, v=P, op=ctypes.c_void_p(0x300000), lp=ctypes.c_void_p(0x380
 ])
 def test_forward_merge_rejects(kw, code):
     assert fmerge(**kw) == code
+
+
+def test_backward_noalloc_rejects_before_touching_the_gpu():
+    # Sizes whose workspace would pass the fixed 16 MiB scratch are refused
+    # with their own status, as are invalid arguments, all on the host.
+    L = fa.lib()
+
+    def call(B=1, H=2, n_q=8, n_k=8, d=64, dq=P2, causal=0):
+        return L.fa_backward_noalloc(P, P, P, P, P, P2, dq, P2, P2, B, H, n_q, n_k, d, 0.125, causal, 1, None)
+
+    assert call(B=1, H=32, n_q=65536) == fa.FA_ERR_TOO_LARGE   # 2 x 8 MiB + slack
+    assert call(B=64, H=64, n_q=4096) == fa.FA_ERR_TOO_LARGE
+    assert call(dq=None) == fa.FA_ERR_INVALID_ARG
+    assert call(d=80) == fa.FA_ERR_UNSUPPORTED
+    assert call(causal=3) == fa.FA_ERR_INVALID_ARG
+    assert call(dq=MIS) == fa.FA_ERR_ALIGNMENT
