@@ -95,7 +95,11 @@ int check_workspace(const void* ws, size_t bytes, int B, int H, int n_q) {
 // parallel work and keep the dK/dV kernel free of a head loop (which costs it
 // 72 spilled registers); the runs grow only when the partials would pass
 // kBwdPartLimit bytes.
-constexpr int kBwdKeyTile = 128;  // keys per dK/dV workgroup (both dtypes)
+// Keys per dK/dV workgroup at the narrowest routing: the bf16 kernel takes
+// 64 keys (two waves) on causal, windowed and nearly empty passes and 128
+// otherwise, the fp32 kernel 128; the grid-size guard counts 64-key tiles,
+// the most workgroups any routing launches.
+constexpr int kBwdKeyTile = 64;
 constexpr double kBwdPartLimit = 4294967296.0;
 int bwd_slices(int B, int H, int H_kv, int n_k) {
   const int group = H / H_kv;

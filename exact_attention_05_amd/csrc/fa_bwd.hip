@@ -1068,9 +1068,13 @@ constexpr long long kDkdvIdleHalfWgs = 128;
 template <int D, bool CAUSAL>
 hipError_t dkdv_bf16_t(const BwdArgs& a, hipStream_t s) {
   using C4 = DkdvCfg<D, 4>;
-  const long long wgs = (long long)((a.n_k + C4::kBK - 1) / C4::kBK) * (a.BH / a.group) * a.slices;
-  const bool narrow = CAUSAL || a.window >= 0 || wgs <= kDkdvIdleHalfWgs;
-  return narrow ? dkdv_bf16_w<D, CAUSAL, 2>(a, s) : dkdv_bf16_w<D, CAUSAL, 4>(a, s);
+  if constexpr (CAUSAL) {
+    return dkdv_bf16_w<D, true, 2>(a, s);  // causal passes always take two waves
+  } else {
+    const long long wgs = (long long)((a.n_k + C4::kBK - 1) / C4::kBK) * (a.BH / a.group) * a.slices;
+    const bool narrow = a.window >= 0 || wgs <= kDkdvIdleHalfWgs;
+    return narrow ? dkdv_bf16_w<D, false, 2>(a, s) : dkdv_bf16_w<D, false, 4>(a, s);
+  }
 }
 
 template <int D, bool CAUSAL, int WAVES>

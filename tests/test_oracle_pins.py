@@ -330,38 +330,51 @@ def test_backward_constant_values_give_zero_q_k_gradients():
 # ------------------------------------------------- values the pages print
 
 def test_page_script_inputs_and_manual_vs_sdpa_difference():
-    # Provenance of the c1 inputs: the seed-9 stream reproduces the script
-    # output of "Efficient Attention" (manual attention vs SDPA, fp32).
-    g = json.load(open(os.path.join(GOLDEN, "efficient_attention_script_output.json")))
+    # Provenance of the c1 inputs: "Efficient Attention" prints the largest
+    # difference between an fp32 attention computed step by step (scores
+    # divided by sqrt(d), row softmax, weighted sum) and PyTorch's fused
+    # scaled_dot_product_attention on its seed-9 tensors.  Recomputing that
+    # difference on c1's tensors must give the printed value, so c1's tensors
+    # are the page's.  The fp32 reference is taken here with einsum products;
+    # the score count is the oracle's closed form.
+    g = json.load(open(os.path.join(GOLDEN, "efficient_attention_script_output.json")))["manual_vs_sdpa"]
     w = workloads.c1()
-    q, k, v = w.q, w.k, w.v
-    skor = q @ k.transpose(-2, -1) / math.sqrt(32)
-    manual = skor.softmax(dim=-1) @ v
-    sdpa = torch.nn.functional.scaled_dot_product_attention(q, k, v)
-    assert skor.numel() * skor.element_size() == g["manual_vs_sdpa"]["score_bytes"]
-    assert f"{float((manual - sdpa).abs().max()):.2e}" == g["manual_vs_sdpa"]["max_abs_diff_printed"]
-    assert torch.allclose(manual, sdpa, atol=g["manual_vs_sdpa"]["allclose_atol"])
+    B, H, n, d = w.q.shape
+    assert oracle.score_bytes(B, H, n, 4) == g["score_bytes"]
+    weights = torch.softmax(torch.einsum("bhid,bhjd->bhij", w.q, w.k) / math.sqrt(d), dim=-1)
+    stepwise = torch.einsum("bhij,bhjd->bhid", weights, w.v)
+    fused = torch.nn.functional.scaled_dot_product_attention(w.q, w.k, w.v)
+    gap = float((stepwise - fused).abs().max())
+    assert f"{gap:.2e}" == g["max_abs_diff_printed"]
+    assert gap <= g["allclose_atol"]
     # The fp64 oracle sits within the page's fp32 tolerance of both.
-    o, _ = oracle.attention_fwd(q.double().numpy(), k.double().numpy(), v.double().numpy(), w.scale)
-    assert np.max(np.abs(o - manual.double().numpy())) < g["manual_vs_sdpa"]["allclose_atol"]
-    assert np.max(np.abs(o - sdpa.double().numpy())) < g["manual_vs_sdpa"]["allclose_atol"]
+    o, _ = oracle.attention_fwd(w.q.double().numpy(), w.k.double().numpy(), w.v.double().numpy(), w.scale)
+    for name, t in (("step by step", stepwise), ("fused", fused)):
+        assert np.max(np.abs(o - t.double().numpy())) < g["allclose_atol"], name
 
 
 def test_score_memory_closed_forms():
     g = json.load(open(os.path.join(GOLDEN, "efficient_attention_script_output.json")))
     assert oracle.score_bytes(2, 3, 128, 4) == g["manual_vs_sdpa"]["score_bytes"]
+    # The page prints sizes in binary units ("MB" = 2^20 bytes, "GB" = 2^30)
+    # rounded to the digits shown: each printed figure must be the closed
+    # form's byte count in that unit, to within half its last digit.
+    def matches(nbytes, printed):
+        number, unit = printed.split()
+        digits = len(number.split(".")[1]) if "." in number else 0
+        scale = {"MB": 2.0 ** 20, "GB": 2.0 ** 30}[unit]
+        return abs(nbytes / scale - float(number)) <= 0.5 * 10.0 ** -digits
+
     for row in g["score_memory_table_fp32_b1_h1"]:
         assert row["n"] ** 2 == row["elements"]
         b = oracle.score_bytes(1, 1, row["n"], 4)
         assert b == row["bytes"]
-        shown = f"{b / 1024**2:.1f} MB" if b < 1024**3 else f"{b / 1024**3:.1f} GB"
-        assert shown == row["printed"]
+        assert matches(b, row["printed"]), row
     t = g["row_tiling"]
     full = oracle.score_bytes(1, 1, t["n"], 4)
     block = t["block"] * t["n"] * 4
     assert (full, block, full // block) == (t["full_bytes"], t["block_bytes"], t["saving_factor"])
-    assert f"{full / 1024**2:.1f} MB" == t["full_printed"]
-    assert f"{block / 1024**2:.2f} MB" == t["block_printed"]
+    assert matches(full, t["full_printed"]) and matches(block, t["block_printed"])
 
 
 def test_memory_calculator_worked_example():
