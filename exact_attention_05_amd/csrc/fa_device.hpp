@@ -48,6 +48,15 @@ __device__ __forceinline__ bf16x4 lds_read_tr16(const __bf16* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((FA_LDS bf16x4*)(const_cast<__bf16*>(p)));
 }
 
+// The same reads at an LDS byte address held as an integer (a per-lane base
+// plus a constant the compiler folds into the instruction's 16-bit offset).
+__device__ __forceinline__ bf16x8 lds_load16_at(uint32_t addr) {
+  return *reinterpret_cast<const FA_LDS bf16x8*>((uintptr_t)addr);
+}
+__device__ __forceinline__ bf16x4 lds_read_tr16_at(uint32_t addr) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(reinterpret_cast<FA_LDS bf16x4*>((uintptr_t)addr));
+}
+
 // Direct global -> LDS copy of 16 bytes per lane: lane j's 16 bytes at
 // base + voffset land at LDS byte address lds_addr + 16 j.  Issued from
 // inline assembly so that the compiler does not treat the copy as an LDS

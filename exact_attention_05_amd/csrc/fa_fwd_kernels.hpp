@@ -37,6 +37,12 @@
 // same instruction stream as the exponentials of block t, and those blocks
 // skip the block maximum unless the probabilities grow too large.
 //
+// At d = 128 the 8-wave workgroups run the ping-pong variant of this kernel
+// (fwd_bf16_pp_kernel): the two waves of each SIMD alternate between the
+// matrix products of a block and the softmax of the next one, half a step
+// apart, so that one wave's vector work runs beside the other's products
+// (same arithmetic in the same order: bitwise the same results).
+//
 // fp32 kernel
 // -----------
 // Same dataflow with float32 operands on the 32x32x2 f32 matrix cores,
@@ -486,6 +492,344 @@ void fwd_bf16_kernel(FwdArgs a, int n_qtiles) {
   }
 }
 
+// Ping-pong variant of the 8-wave kernel for the blocks every row sees.  The
+// two waves that share a SIMD (wave w and wave w + 4) work one half-step
+// apart: while one issues the matrix products of a block (the P V product
+// of block t - 1 and the scores of block t, 32 products), the other runs the
+// softmax of its scores (about 110 vector instructions), so the matrix cores
+// and the vector unit of each SIMD are busy at the same time; a workgroup
+// barrier separates the half-steps.  A wave's own work alternates
+//   phase A(i): O^T += V_{t-1}^T P_{t-1}^T (if i > 0) and S_t = K_t Q^T
+//               (t = f_lo + i, if i < n)
+//   phase B(i): P_t = exp2(scale_log2 S_t - ref), row sums, bf16 P_t
+// for i = 0 .. n (n unmasked blocks).  Both groups run the same code, step
+// i = [barrier, A(i), barrier, B(i)]; waves 4-7 pass one extra barrier
+// first (barriers rendezvous by count), which puts them one half-step
+// behind, and waves 0-3 one extra at the end.  K and V blocks use two LDS
+// buffers each (block f_lo + i in buffer i mod 2, a compile-time index in
+// the loop, unrolled by two).  Waves 4-7 issue the copies, in their vector
+// phase: issuing a direct copy costs its wave about 50 cycles, which in a
+// product phase delays all 32 products (c3: 239 -> 226 us against copies
+// issued by waves 0-3 at the start of their product phase).  Blocks that
+// need a mask (before f_lo: window edges; from f_hi on: causal diagonal, key
+// tail) take the plain path.
+template <int D, bool CAUSAL, bool MERGE>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fwd_bf16_pp_kernel(FwdArgs a, int n_qtiles) {
+  using C = Bf16FwdCfg<D, 8>;
+  using F = std::false_type;
+  using T = std::true_type;
+  __shared__ __attribute__((aligned(1024))) char sk[2][C::KV::kBytes];
+  __shared__ __attribute__((aligned(1024))) char sv[2][C::KV::kBytes];
+
+  int bh, qt;
+  if (CAUSAL) {
+    costliest_first(blockIdx.x, gridDim.x, n_qtiles, bh, qt);
+    qt = n_qtiles - 1 - qt;
+  } else {
+    const int work = xcd_remap(blockIdx.x, gridDim.x);
+    bh = work / n_qtiles;
+    qt = work - bh * n_qtiles;
+  }
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;  // 0: waves 0-3, 1: waves 4-7, one half-step behind
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+  const int q0 = qt * C::kBM;
+  const int qw = q0 + wave * 32;
+  const int qi = qw + l32;
+  const int n_q = a.n_q, n_k = a.n_k;
+  const float sl2 = a.scale_log2;
+
+  const __bf16* qp = static_cast<const __bf16*>(a.q) + (size_t)bh * n_q * D;
+  const int kvh = kv_head_index(bh, a.H, a.group);
+  const __bf16* kp = static_cast<const __bf16*>(a.k) + (size_t)kvh * n_k * D;
+  const __bf16* vp = static_cast<const __bf16*>(a.v) + (size_t)kvh * n_k * D;
+
+  bf16x8 qf[C::kDC];
+#pragma unroll
+  for (int c = 0; c < C::kDC; ++c) {
+    if (qi < n_q)
+      qf[c] = *reinterpret_cast<const bf16x8*>(qp + (size_t)qi * D + 16 * c + 8 * hi);
+    else
+      qf[c] = bf16x8{};
+  }
+
+  const Band band = band_of(a, CAUSAL);
+  const int q_end = min(n_q, q0 + C::kBM);
+  const int t_lo = band.key_lo(q0) / C::kBN;
+  const int t_hi = max(t_lo, (band.key_hi(q_end) + C::kBN - 1) / C::kBN);
+  const int f_lo = min(t_hi, max(t_lo, (band.key_full_lo(q_end) + C::kBN - 1) / C::kBN));
+  const int f_hi = max(f_lo, min(t_hi, band.key_full_hi(q0) / C::kBN));
+  const int n = f_hi - f_lo;  // blocks of the ping-pong
+  int vlo, vspan;
+  band.key_range(qi, vlo, vspan);
+
+  TileDma<D, C::kBN, C::kWaves> dma;
+  dma.init(wave, lane);
+  TileLane<D, C::kBN> tl;
+  tl.init(lane);
+  const uint32_t sk_addr = lds_address(&sk[0][0]);
+  const uint32_t sv_addr = lds_address(&sv[0][0]);
+  // Block t lives in buffer (t - f_lo) mod 2.
+  auto bufof = [&](int t) { return (t - f_lo) & 1; };
+  auto load_tile = [&](int t) {
+    const int k0 = t * C::kBN;
+    dma.load(kp + (size_t)k0 * D, n_k - k0, sk_addr + bufof(t) * C::KV::kBytes);
+    dma.load(vp + (size_t)k0 * D, n_k - k0, sv_addr + bufof(t) * C::KV::kBytes);
+  };
+
+  f32x16 oacc[C::kDB];
+#pragma unroll
+  for (int db = 0; db < C::kDB; ++db) oacc[db] = f32x16{};
+  float m = -INFINITY, l = 0.f;
+
+  // A masked block (plain path, run-time buffer): wait for block t, barrier,
+  // start the copy of block t + 1 (next_ok: it is not copied yet), then
+  // S^T = K Q^T, masked online softmax with the block maximum, O^T += V^T P^T.
+  auto masked_block = [&](int t, bool next_ok) {
+    wait_lds_dma();
+    __syncthreads();
+    if (next_ok && t + 1 < t_hi) load_tile(t + 1);
+    const int buf = bufof(t);
+    const char* ks = sk[buf];
+    const char* vs = sv[buf];
+    const int k0 = t * C::kBN;
+    if (qw >= n_q || band.key_hi(qw + 32) <= k0 || band.key_lo(qw) >= k0 + C::kBN) return;
+    f32x16 s[C::kKB];
+#pragma unroll
+    for (int kb = 0; kb < C::kKB; ++kb) s[kb] = f32x16{};
+#pragma unroll
+    for (int c = 0; c < C::kDC; ++c)
+#pragma unroll
+      for (int kb = 0; kb < C::kKB; ++kb) s[kb] = mfma_bf16(tl.read_rows(ks, kb * 32, c), qf[c], s[kb]);
+    const int rel = k0 + 4 * hi - vlo;
+#pragma unroll
+    for (int kb = 0; kb < C::kKB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (!Band::in_range(rel + kb * 32 + 8 * (i >> 2) + (i & 3), 0, vspan)) s[kb][i] = -INFINITY;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < C::kKB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(s[kb][i], s[kb][i + 1]));
+    mx = max_halves(mx);
+    const float mt = (mx == -INFINITY) ? -INFINITY : mx * sl2;
+    if (__builtin_amdgcn_ballot_w64(mt > m + kLazyRescale) != 0) {
+      const float m_new = fmaxf(m, mt);
+      const float ref = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = fast_exp2(m - ref);
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < C::kDB; ++db) oacc[db] *= alpha;
+      m = m_new;
+    }
+    const float ref = (m == -INFINITY) ? 0.f : m;
+    u32x4 pw[C::kKB][2];
+    float rs0 = 0.f, rs1 = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < C::kKB; ++kb)
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          float p0 = fast_exp2(fmaf(s[kb][8 * c2 + e], sl2, -ref));
+          float p1 = fast_exp2(fmaf(s[kb][8 * c2 + e + 1], sl2, -ref));
+          if (s[kb][8 * c2 + e] == -INFINITY) p0 = 0.f;
+          if (s[kb][8 * c2 + e + 1] == -INFINITY) p1 = 0.f;
+          pw[kb][c2][e >> 1] = pack_bf16x2(p0, p1);
+          rs0 += p0;
+          rs1 += p1;
+        }
+    l += rs0 + rs1;
+#pragma unroll
+    for (int kb = 0; kb < C::kKB; ++kb)
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+        for (int db = 0; db < C::kDB; ++db)
+          oacc[db] = mfma_bf16(tl.read_cols_tr(vs, kb * 32 + 16 * c2, 32 * db), bf16x8_of(pw[kb][c2]), oacc[db]);
+  };
+
+  if (t_lo < t_hi) load_tile(t_lo);
+  int t = t_lo;
+  for (; t < f_lo; ++t) masked_block(t, true);  // up to block f_lo's copy
+
+  if (n > 0) {
+    f32x16 sc[C::kKB];          // scores of the wave's current block
+    u32x4 pw[C::kKB][2];        // its probabilities as bf16 pairs
+    // Phase A as one stream of product steps: steps 0-15 the P V products
+    // (two transposing reads each), steps 16-31 the score products (one K
+    // row read each); P V first, so that the previous block's bf16 P is dead
+    // before the new scores are written.  Operand reads run kAhead steps
+    // ahead of their products through a ring, hand-scheduled (the scheduler
+    // would otherwise issue all 48 reads first and run out of registers).
+    constexpr int kHalf = C::kDC * C::kKB;
+    constexpr int kAhead = 6;
+    auto phase_a = [&](auto kb_tag, auto vb_tag, auto pv_tag, auto s_tag) __attribute__((always_inline)) {
+      constexpr int KB = decltype(kb_tag)::value, VB = decltype(vb_tag)::value;
+      constexpr bool PV = decltype(pv_tag)::value, SC = decltype(s_tag)::value;
+      constexpr int J0 = PV ? 0 : kHalf, J1 = SC ? 2 * kHalf : kHalf;
+      auto read = [&](auto j_tag) __attribute__((always_inline)) -> bf16x8 {
+        constexpr int J = decltype(j_tag)::value;
+        if constexpr (J >= kHalf) {
+          constexpr int c = (J - kHalf) / C::kKB, kb = (J - kHalf) % C::kKB;
+          return tl.read_rows(sk[KB], kb * 32, c);
+        } else {
+          constexpr int kb = J / (2 * C::kDB), c2 = (J / C::kDB) % 2, db = J % C::kDB;
+          return tl.read_cols_tr(sv[VB], kb * 32 + 16 * c2, 32 * db);
+        }
+      };
+      auto product = [&](auto j_tag, const bf16x8& op) __attribute__((always_inline)) {
+        constexpr int J = decltype(j_tag)::value;
+        if constexpr (J >= kHalf) {
+          constexpr int c = (J - kHalf) / C::kKB, kb = (J - kHalf) % C::kKB;
+          sc[kb] = mfma_bf16(op, qf[c], c == 0 ? f32x16{} : sc[kb]);
+        } else {
+          constexpr int kb = J / (2 * C::kDB), c2 = (J / C::kDB) % 2, db = J % C::kDB;
+          oacc[db] = mfma_bf16(op, bf16x8_of(pw[kb][c2]), oacc[db]);
+        }
+      };
+      bf16x8 ring[kAhead];
+      phase_barrier();
+      static_for<J0, (J0 + kAhead < J1 ? J0 + kAhead : J1)>([&](auto j) __attribute__((always_inline)) {
+        ring[(decltype(j)::value - J0) % kAhead] = read(j);
+      });
+      __builtin_amdgcn_sched_barrier(0);
+      static_for<J0, J1>([&](auto j) __attribute__((always_inline)) {
+        constexpr int J = decltype(j)::value;
+        product(j, ring[(J - J0) % kAhead]);
+        if constexpr (J + kAhead < J1) ring[(J - J0) % kAhead] = read(std::integral_constant<int, J + kAhead>{});
+        __builtin_amdgcn_sched_barrier(0);  // each product with the read kAhead steps ahead
+      });
+    };
+    auto probs = [&]() __attribute__((always_inline)) -> float {
+      const float ref = (m == -INFINITY) ? 0.f : m;
+      float rs0 = 0.f, rs1 = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < C::kKB; ++kb)
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+          for (int e = 0; e < 8; e += 2) {
+            const float p0 = fast_exp2(fmaf(sc[kb][8 * c2 + e], sl2, -ref));
+            const float p1 = fast_exp2(fmaf(sc[kb][8 * c2 + e + 1], sl2, -ref));
+            pw[kb][c2][e >> 1] = pack_bf16x2(p0, p1);
+            rs0 += p0;
+            rs1 += p1;
+          }
+      return rs0 + rs1;
+    };
+    // Phase B: the softmax of the wave's scores against the running
+    // reference; only when a probability might pass 2^16 or a row has no
+    // reference yet is the block maximum taken (lazy rescale, as above).
+    auto phase_b = [&]() __attribute__((always_inline)) {
+      float rs = probs();
+      if (__builtin_amdgcn_ballot_w64(!(rs <= kFastSum) || m == -INFINITY) != 0) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < C::kKB; ++kb)
+#pragma unroll
+          for (int e = 0; e < 16; e += 2) mx = fmaxf(mx, fmaxf(sc[kb][e], sc[kb][e + 1]));
+        mx = max_halves(mx);
+        const float mt = mx * sl2;
+        if (__builtin_amdgcn_ballot_w64(mt > m + kLazyRescale) != 0) {
+          const float m_new = fmaxf(m, mt);
+          const float alpha = fast_exp2(m - m_new);
+          l *= alpha;
+#pragma unroll
+          for (int db = 0; db < C::kDB; ++db) oacc[db] *= alpha;
+          m = m_new;
+        }
+        rs = probs();
+      }
+      l += rs;
+    };
+    // Copies by waves 4-7 in their phase B (vector work, while waves 0-3
+    // run products): in B(i) (which starts at the barrier that ends every
+    // read of blocks f_lo + i and f_lo + i - 1) K of block f_lo + i + 2 (up
+    // to f_hi) and V of f_lo + i + 1 (up to f_hi), both first read two
+    // half-steps later; waves 4-7 wait for them before the barrier in the
+    // middle of their next step, which precedes the first read.
+    TileDma<D, C::kBN, 4> dma4;
+    dma4.init(wave & 3, lane);
+    auto step = [&](auto p_tag, auto pv_tag, auto s_tag, int i) __attribute__((always_inline)) {
+      constexpr int P = decltype(p_tag)::value;  // i mod 2
+      phase_a(std::integral_constant<int, P>{}, std::integral_constant<int, P ^ 1>{}, pv_tag, s_tag);
+      if (grp == 1) wait_lds_dma();
+      phase_barrier();
+      if (grp == 1) {
+        const int tk = f_lo + i + 2, tv = f_lo + i + 1;
+        if (tk <= f_hi && tk < t_hi) {
+          const int k0 = tk * C::kBN;
+          dma4.load(kp + (size_t)k0 * D, n_k - k0, sk_addr + P * C::KV::kBytes);
+        }
+        if (tv <= f_hi && tv < t_hi) {
+          const int k0 = tv * C::kBN;
+          dma4.load(vp + (size_t)k0 * D, n_k - k0, sv_addr + (P ^ 1) * C::KV::kBytes);
+        }
+      }
+      if constexpr (decltype(s_tag)::value) phase_b();
+    };
+    using Z = std::integral_constant<int, 0>;
+    using O = std::integral_constant<int, 1>;
+    // Block f_lo (K and V) was started by the previous block or the first
+    // copy; every wave waits for its part before the ping-pong starts, and
+    // waves 4-7 start K of block f_lo + 1 (read first at step 1).
+    wait_lds_dma();
+    if (grp == 1) {
+      if (f_lo + 1 <= f_hi && f_lo + 1 < t_hi) {
+        const int k0 = (f_lo + 1) * C::kBN;
+        dma4.load(kp + (size_t)k0 * D, n_k - k0, sk_addr + C::KV::kBytes);
+      }
+      phase_barrier();
+    }
+    step(Z{}, F{}, T{}, 0);  // scores of block f_lo only
+    int i = 1;
+    for (; i + 1 < n; i += 2) {
+      step(O{}, T{}, T{}, i);
+      step(Z{}, T{}, T{}, i + 1);
+    }
+    if (i < n) {
+      step(O{}, T{}, T{}, i);
+      ++i;
+    }
+    // i == n: the last P V product only
+    if (n & 1) step(O{}, T{}, F{}, n);
+    else step(Z{}, T{}, F{}, n);
+    if (grp == 0) phase_barrier();
+    t = f_hi;
+  }
+  // After the ping-pong: block f_hi's K was started at step n - 1 and its V
+  // at step n (nothing beyond); the masked blocks continue with one block of
+  // look-ahead.
+  for (; t < t_hi; ++t) masked_block(t, true);
+
+  const float lt = sum_halves(l);
+  if constexpr (MERGE) {
+    if (qi < n_q) merge_store(a, (size_t)bh * n_q + qi, hi, oacc, m, lt);
+    return;
+  }
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  if (qi < n_q) {
+    __bf16* op = static_cast<__bf16*>(a.o) + ((size_t)bh * n_q + qi) * D;
+#pragma unroll
+    for (int db = 0; db < C::kDB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        bf16x4 r;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r[e] = (__bf16)(oacc[db][4 * g4 + e] * inv);
+        *reinterpret_cast<bf16x4*>(op + 32 * db + 8 * g4 + 4 * hi) = r;
+      }
+    if (hi == 0) a.lse[(size_t)bh * n_q + qi] = (m + fast_log2(lt)) * kLn2;
+  }
+}
+
 // ------------------------------------------------------------------ fp32
 
 // Online-softmax update of one 32-query block held as S^T fragments
@@ -728,11 +1072,24 @@ constexpr long long kCausalBalanceWgs = 512;
 constexpr long long kIdleHalfWgs = 128;
 
 template <int D, bool CAUSAL, bool MERGE>
+hipError_t fwd_bf16_pp(const FwdArgs& a, hipStream_t stream) {
+  using C = Bf16FwdCfg<D, 8>;
+  const int n_qtiles = (a.n_q + C::kBM - 1) / C::kBM;
+  return launch(fwd_bf16_pp_kernel<D, CAUSAL, MERGE>, n_qtiles * a.BH, C::kThreads, a, n_qtiles, stream);
+}
+
+template <int D, bool CAUSAL, bool MERGE>
 hipError_t fwd_bf16_t(const FwdArgs& a, hipStream_t stream) {
   const long long wide_wgs = (long long)a.BH * ((a.n_q + Bf16FwdCfg<D, 8>::kBM - 1) / Bf16FwdCfg<D, 8>::kBM);
   const bool narrow = a.n_q <= kShortRows || a.window >= 0 ||
                       (CAUSAL ? wide_wgs < kCausalBalanceWgs : wide_wgs <= kIdleHalfWgs);
-  return narrow ? fwd_bf16_w<D, CAUSAL, 4, MERGE>(a, stream) : fwd_bf16_w<D, CAUSAL, 8, MERGE>(a, stream);
+  if (narrow) return fwd_bf16_w<D, CAUSAL, 4, MERGE>(a, stream);
+  // 256-row workgroups at d = 128 take the ping-pong kernel (bitwise the same
+  // results; c3 243 -> 231 us, causal 133 -> 128 us, n = 8192 918 -> 870 us
+  // on one box); at d = 64 it measured slower (147 -> 150 us) and d <= 64
+  // keeps the plain 8-wave kernel.
+  if constexpr (D == 128) return fwd_bf16_pp<D, CAUSAL, MERGE>(a, stream);
+  else return fwd_bf16_w<D, CAUSAL, 8, MERGE>(a, stream);
 }
 
 template <int D, bool CAUSAL, bool MERGE>
