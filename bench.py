@@ -13,7 +13,14 @@ roofline   = the kernel taking the largest share of the step, its algorithmic
              FLOP per launch over its mean launch time from HIP events recorded
              around it inside the timed loop, against the bf16 dense
              matrix-core peak.
-cpu_baseline = the fp64 oracle timed on a bounded sample of the same workload.
+cpu_baseline = the fp64 oracle timed on a bounded sample of the same workload,
+             with the CPU model and the BLAS library (vendor, threads).
+flops      = each pass counted two ways: literal 4*B*H*n^2*d and algorithmic
+             (visible pairs, 2 products forward, 5 backward).
+
+--workload configs times each workload's hot call, one ring-attention step
+(fa_forward_merge against fa_forward + fa_lse_merge) and, unless
+--no-cpu-baseline, the fp64 oracle on every workload.
 
 With --workload decode the step is instead one split-KV decoding call
 (fa_decode: 4 sequences x 64 query heads over 8 K/V heads, one new query row
@@ -107,28 +114,52 @@ def kernel_source_digest(kernel: str) -> str:
     return h.hexdigest()
 
 
-def cpu_baseline(w, budget_s: float):
-    """The fp64 oracle (forward + explicit backward) on whole (b, h) units of
-    the same workload, repeated until about ``budget_s`` seconds of CPU work."""
-    import numpy as np
-
-    import oracle
-
+def host_info():
+    """What the CPU figures ran on: the CPU model (/proc/cpuinfo), the cores
+    this process may use, and the BLAS library numpy calls (vendor, version,
+    threads)."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = None
     try:
         import threadpoolctl
 
-        info = threadpoolctl.threadpool_info()
-        threads = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
+        for i in threadpoolctl.threadpool_info():
+            if i.get("user_api") == "blas":
+                blas = {"vendor": i.get("internal_api"), "version": i.get("version"),
+                        "threads": i.get("num_threads"), "library": os.path.basename(i.get("filepath") or "")}
+                break
     except Exception:  # noqa: BLE001
-        threads = None
+        pass
+    return {"cpu_model": model, "cores_available": len(os.sched_getaffinity(0)), "blas": blas}
+
+
+def _f64(torch_tensor):
+    import numpy as np
+
+    return torch_tensor.float().numpy().astype(np.float64)
+
+
+def cpu_baseline(w, budget_s: float):
+    """The fp64 oracle (forward + explicit backward) on whole (b, h) units of
+    the same workload, repeated until about ``budget_s`` seconds of CPU work."""
+    import oracle
+
+    host = host_info()
     B, H, n, d = w.q.shape
     units = [(0, h) for h in range(H)]
     t0 = time.perf_counter()
     done = 0
     while done < len(units):
         b, h = units[done]
-        q, k, v, do = (x[b, h].to(dtype=w.q.dtype).float().numpy().astype(np.float64)
-                       for x in (w.q, w.k, w.v, w.do))
+        q, k, v, do = (_f64(x[b, h]) for x in (w.q, w.k, w.v, w.do))
         oracle.attention_fwd(q, k, v, w.scale, w.causal)
         oracle.attention_bwd(q, k, v, do, w.scale, w.causal)
         done += 1
@@ -139,10 +170,72 @@ def cpu_baseline(w, budget_s: float):
     return {
         "value": flops / dt / 1e12,
         "unit": "TFLOP/s",
-        "cores": threads,
+        "cores": (host["blas"] or {}).get("threads"),
         "kind": "oracle",
         "sample": f"{done} of {B * H} (b,h) units, fp64 numpy forward + explicit backward, {dt:.1f} s",
+        "cpu_model": host["cpu_model"],
+        "cores_available": host["cores_available"],
+        "blas": host["blas"],
     }
+
+
+def cpu_oracle_configs(workloads, log):
+    """The fp64 oracle timed on every workload (baseline only, never a
+    target): c1-c3 the full forward, c4 the 256 checked rows plus one full
+    head (x32, an extrapolation), c5 the full forward + explicit backward.
+    TFLOP/s use the GPU's algorithmic counts."""
+    import oracle
+
+    res = {"host": host_info()}
+
+    def fwd_full(name, w):
+        B, H, n, d = w.q.shape
+        t0 = time.perf_counter()
+        for b in range(B):
+            for h in range(H):
+                oracle.attention_fwd(_f64(w.q[b, h]), _f64(w.k[b, h]), _f64(w.v[b, h]), w.scale, w.causal)
+        dt = time.perf_counter() - t0
+        fl = 4 * d * B * H * visible_pairs(n, n, w.causal)
+        res[name] = {"s": round(dt, 3), "tflops": round(fl / dt / 1e12, 6), "scope": "full forward"}
+        log(f"cpu oracle {name}: {dt:.1f} s")
+
+    fwd_full("c1", workloads.c1())
+    fwd_full("c2", workloads.c2())
+    fwd_full("c3_noncausal", workloads.c3(False))
+    fwd_full("c3_causal", workloads.c3(True))
+
+    w = workloads.c4()
+    B, H, n, d = w.q.shape
+    qf, kf, vf = (_f64(x) for x in (w.q, w.k, w.v))
+    t0 = time.perf_counter()
+    oracle.attention_rows(qf, kf, vf, workloads.c4_rows(), w.scale, True)
+    t_rows = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    oracle.attention_fwd(qf[0, 0], kf[0, 0], vf[0, 0], w.scale, True)
+    t_head = time.perf_counter() - t0
+    del qf, kf, vf
+    fl = 4 * d * B * H * visible_pairs(n, n, True)
+    res["c4_causal"] = {"s_256_rows": round(t_rows, 3), "s_one_head": round(t_head, 3),
+                        "s_full_extrapolated": round(32 * t_head, 2),
+                        "tflops": round(fl / (32 * t_head) / 1e12, 6),
+                        "scope": "256 checked rows timed; one full head timed, x32 extrapolation"}
+    log(f"cpu oracle c4: rows {t_rows:.1f} s, one head {t_head:.1f} s")
+    del w
+
+    w = workloads.c5()
+    B, H, n, d = w.q.shape
+    t0 = time.perf_counter()
+    for b in range(B):
+        for h in range(H):
+            q, k, v, do = (_f64(x[b, h]) for x in (w.q, w.k, w.v, w.do))
+            oracle.attention_fwd(q, k, v, w.scale, True)
+            oracle.attention_bwd(q, k, v, do, w.scale, True)
+    dt = time.perf_counter() - t0
+    pairs = B * H * visible_pairs(n, n, True)
+    res["c5_fwd_bwd_causal"] = {"s": round(dt, 3), "tflops": round(14 * d * pairs / dt / 1e12, 6),
+                                "scope": "full forward + explicit backward"}
+    log(f"cpu oracle c5: {dt:.1f} s")
+    return res
 
 
 def calibration_copy(torch, dev):
@@ -458,6 +551,41 @@ def run_configs(args, torch, fa, workloads, dev):
     del o_parts, lse_parts, mo, ml
     torch.cuda.empty_cache()
 
+    # One ring-attention step at the c3 shape: 4096 local query rows of 32
+    # heads take a 4096-key chunk and fold it into the running (O, LSE).
+    # Fused: fa_forward_merge, one launch.  Separate: fa_forward into a part,
+    # then fa_lse_merge of (running, part), whose O makes a round trip
+    # through HBM.  Out of place (the running result is double-buffered).
+    w3 = workloads.c3(False)
+    q3, k3, v3 = (t.to(dev) for t in (w3.q, w3.k, w3.v))
+    B, H, n, d = q3.shape
+    g = torch.Generator(device="cpu").manual_seed(16)
+    ring = {}
+    for acc in (torch.bfloat16, torch.float32):
+        o_run = torch.randn(B, H, n, d, generator=g).to(acc).to(dev)
+        l_run = (torch.randn(B, H, n, generator=g) * 2.0 + 8.0).to(dev)
+        o_new, l_new = torch.empty_like(o_run), torch.empty_like(l_run)
+        us = _median_us(torch, lambda: fa.forward_merge(q3, k3, v3, o_run, l_run, scale=w3.scale,
+                                                          out=o_new, lse=l_new), 10)
+        ring[f"fused_{str(acc).split('.')[-1]}_running_o_us"] = round(us, 1)
+    parts = torch.empty((2, B, H, n, d), dtype=torch.bfloat16, device=dev)
+    lparts = torch.empty((2, B, H, n), dtype=torch.float32, device=dev)
+    parts[0] = torch.randn(B, H, n, d, generator=g).to(torch.bfloat16).to(dev)
+    lparts[0] = (torch.randn(B, H, n, generator=g) * 2.0 + 8.0).to(dev)
+    mo = torch.empty((B, H, n, d), dtype=torch.bfloat16, device=dev)
+    ml = torch.empty((B, H, n), dtype=torch.float32, device=dev)
+
+    def separate():
+        fa.forward(q3, k3, v3, scale=w3.scale, out=parts[1], lse=lparts[1])
+        fa.lse_merge(parts, lparts, out=mo, lse=ml)
+
+    ring["separate_bf16_running_o_us"] = round(_median_us(torch, separate, 10), 1)
+    ring["saved_pct_bf16"] = round(100 * (1 - ring["fused_bfloat16_running_o_us"]
+                                          / ring["separate_bf16_running_o_us"]), 1)
+    res["ring_step_c3_chunk4096"] = ring
+    del q3, k3, v3, o_run, l_run, o_new, l_new, parts, lparts, mo, ml
+    torch.cuda.empty_cache()
+
     # Short-sequence sweep: B=16, H=32, d=128 bf16 non-causal forward, input
     # sets rotated so that the bytes touched between two calls of the same
     # set exceed the 256 MB last-level cache.
@@ -505,7 +633,186 @@ def run_configs(args, torch, fa, workloads, dev):
         "hbm_sweep": sweep,
         "sclk_mhz_mean_c3_forward": sclk,
     }
+    if not args.no_cpu_baseline:
+        out["cpu_oracle"] = cpu_oracle_configs(workloads, lambda m: print(m, file=sys.stderr, flush=True))
     print(json.dumps(out), flush=True)
+    return 0
+
+
+# ------------------------------------------------ profiler summaries
+# rocprofv3 writes CSV files (kernel trace, kernel stats, counter
+# collection); these turn them into the short summaries kept under profiles/
+# and the per-kernel traffic records load_traffic() reads.
+
+STAGE_PATTERNS = [("bwd_preprocess", "bwd_preprocess"), ("bwd_dkdv", "bwd_dkdv"), ("bwd_dq", "bwd_dq"),
+                  ("decode", "decode_bf16"), ("lse_merge", "lse_merge"), ("fwd", "fwd_")]
+COPY_KIB = 512 * 1024  # the calibration copy reads and writes 512 MiB
+
+
+def stage_of(kernel_name: str):
+    for stage, pat in STAGE_PATTERNS:
+        if pat in kernel_name:
+            return stage
+    return None
+
+
+def _csv_rows(directory: str, suffix: str):
+    import csv
+    import glob
+
+    files = sorted(glob.glob(os.path.join(directory, "**", f"*{suffix}"), recursive=True))
+    if not files:
+        raise FileNotFoundError(f"no *{suffix} under {directory}")
+    rows = []
+    for f in files:
+        with open(f, newline="") as fh:
+            rows += list(csv.DictReader(fh))
+    return rows
+
+
+def _counter_per_dispatch(directory: str, counter: str):
+    """{kernel name: [value per dispatch, in dispatch order]} for one counter."""
+    per = {}
+    rows = [r for r in _csv_rows(directory, "counter_collection.csv") if r.get("Counter_Name") == counter]
+    rows.sort(key=lambda r: int(r.get("Dispatch_Id") or 0))
+    for r in rows:
+        per.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return per
+
+
+def _copy_kernel(fetch: dict):
+    """The calibration copy: the non-library kernel that read the most (the
+    fill that creates its source writes as much but reads nothing)."""
+    cands = {k: max(v) for k, v in fetch.items() if stage_of(k) is None}
+    return max(cands, key=cands.get)
+
+
+def record_traffic(fetch_dir: str, write_dir: str, tag: str, commands: list[str]) -> str:
+    fetch = _counter_per_dispatch(fetch_dir, "FETCH_SIZE")
+    write = _counter_per_dispatch(write_dir, "WRITE_SIZE")
+    copy_f = _copy_kernel(fetch)
+    copy_w = copy_f
+    ff = COPY_KIB / max(fetch[copy_f])
+    wf = COPY_KIB / max(write[copy_w])
+    lines = [f"# HBM traffic counters: {tag}", "",
+             "Commands (from the repository root, on one MI355X; two separate counter runs, then this summary):",
+             "", "```", "export TMPDIR=/tmp", *commands, "```", "",
+             "Calibration: the elementwise copy run by --calibration-copy reads and writes exactly 512 MiB "
+             f"({COPY_KIB} KiB).",
+             f"Its FETCH_SIZE reads {max(fetch[copy_f]):.0f} KiB and WRITE_SIZE {max(write[copy_w]):.0f} KiB, "
+             f"so the scale factors are fetch x{ff:.3f}, write x{wf:.3f}.", "",
+             "| kernel | dispatches | FETCH_SIZE KiB/launch | WRITE_SIZE KiB/launch | scaled HBM bytes/launch |",
+             "|---|---|---|---|---|"]
+    for name in sorted(fetch, key=lambda k: (stage_of(k) is None, str(stage_of(k)), k)):
+        stage = stage_of(name)
+        if stage is None or name not in write:
+            continue
+        # the last dispatches are the timed ones; the first may run on cold caches
+        fk = fetch[name][-1]
+        wk = write[name][-1]
+        nbytes = int(round((fk * ff + wk * wf) * 1024))
+        lines.append(f"| {stage}: `{name[:90]}` | {len(fetch[name])} | {fk:.0f} | {wk:.0f} | {nbytes} |")
+        src = KERNEL_SOURCES.get(stage)
+        if src:
+            rec = {"kernel": stage, "kernel_name": name, "workload": tag, "source": src,
+                   "source_sha256": kernel_source_digest(stage), "fetch_kib": fk, "write_kib": wk,
+                   "fetch_factor": ff, "write_factor": wf, "bytes_per_launch": nbytes,
+                   "summary": f"profiles/traffic_{tag}.md"}
+            with open(os.path.join(ROOT, "profiles", f"traffic_{stage}.json"), "w") as f:
+                json.dump(rec, f, indent=1)
+    lines.append(f"| copy 512 MiB: `{copy_w[:90]}` | 1 | {max(fetch[copy_f]):.0f} | {max(write[copy_w]):.0f} | "
+                 f"{2 * COPY_KIB * 1024} |")
+    path = os.path.join(ROOT, "profiles", f"traffic_{tag}.md")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return path
+
+
+def summarize_trace(trace_dir: str, tag: str, commands: list[str], timed: int, note: str) -> str:
+    """Per-kernel calls, mean/min/max and share from the kernel stats, plus
+    the mean of the last ``timed`` dispatches of each kernel from the trace."""
+    stats = _csv_rows(trace_dir, "kernel_stats.csv")
+    trace = _csv_rows(trace_dir, "kernel_trace.csv")
+    durs = {}
+    for r in sorted(trace, key=lambda r: int(r.get("Start_Timestamp") or 0)):
+        durs.setdefault(r["Kernel_Name"], []).append(
+            (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    lines = [f"# Kernel trace: {tag}", "", "Command (from the repository root, on one MI355X), then this summary:",
+             "", "```", "export TMPDIR=/tmp", *commands, "```", "", note, "",
+             "| kernel | calls | mean us | min us | max us | share | mean us of the timed calls |",
+             "|---|---|---|---|---|---|---|"]
+    for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"])):
+        name = r["Name"]
+        d = durs.get(name, [])
+        last = d[-timed:] if timed else d
+        tail = f"{sum(last) / len(last):.1f} (last {len(last)})" if last else "-"
+        lines.append(f"| `{name[:110]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
+                     f"{float(r['Percentage']):.1f}% | {tail} |")
+    path = os.path.join(ROOT, "profiles", f"kernel_trace_{tag}.md")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return path
+
+
+def summarize_counters(dirs: list[str], tag: str, commands: list[str]) -> str:
+    """SQ/GRBM counter passes (one directory each) -> per-kernel means and the
+    derived figures: MFMA utilisation at the running clock, vector and LDS
+    instructions per product, co-issue and LDS-wait cycles per SIMD."""
+    simds, xcds = 1024, 8
+    per = {}
+    for d in dirs:
+        for r in _csv_rows(d, "counter_collection.csv"):
+            stage = stage_of(r["Kernel_Name"])
+            if stage is None:
+                continue
+            per.setdefault(stage, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    mean = {k: {c: sum(v) / len(v) for c, v in cs.items()} for k, cs in per.items()}
+    lines = [f"# Counters: {tag}", "", "Commands (from the repository root, on one MI355X; one counter pass per run), "
+             "then this summary:", "", "```", "export TMPDIR=/tmp", *commands, "```", "",
+             f"Mean per launch.  SQ counters are summed over the {simds} SIMDs, GRBM_GUI_ACTIVE over the {xcds} XCDs.  "
+             "Each 32x32x16 bf16 product adds 32 to SQ_VALU_MFMA_BUSY_CYCLES, so MFMA utilisation at the running "
+             "clock = (MFMA_BUSY / 1024) / (GRBM_GUI_ACTIVE / 8).  SQ_ACTIVE_INST_VALU and SQ_WAIT_INST_LDS count "
+             "quad-cycles (x4 / 1024 per SIMD); co-issue = SQ_VALU_MFMA_COEXEC_CYCLES / 1024.", "",
+             "| kernel | MFMA instr | MFMA busy cyc/SIMD | GPU active cyc/XCD | MFMA util (running clock) | "
+             "VALU instr / MFMA | VALU active cyc/SIMD | MFMA+VALU co-issue cyc/SIMD | LDS instr / MFMA | "
+             "LDS bank conflicts | LDS-wait cyc/SIMD |", "|---|---|---|---|---|---|---|---|---|---|---|"]
+
+    def g(m, c):
+        return m.get(c, float("nan"))
+
+    for k in sorted(mean):
+        m = mean[k]
+        mf = g(m, "SQ_INSTS_MFMA")
+        busy = g(m, "SQ_VALU_MFMA_BUSY_CYCLES") / simds
+        act = g(m, "GRBM_GUI_ACTIVE") / xcds
+        ratio = (lambda a: a / mf if mf else float("nan"))
+        lines.append(f"| {k} | {mf:.0f} | {busy:.0f} | {act:.0f} | {100 * busy / act:.1f} % | "
+                     f"{ratio(g(m, 'SQ_INSTS_VALU')):.2f} | {4 * g(m, 'SQ_ACTIVE_INST_VALU') / simds:.0f} | "
+                     f"{g(m, 'SQ_VALU_MFMA_COEXEC_CYCLES') / simds:.0f} | {ratio(g(m, 'SQ_INSTS_LDS')):.2f} | "
+                     f"{g(m, 'SQ_LDS_BANK_CONFLICT'):.0f} | {4 * g(m, 'SQ_WAIT_INST_LDS') / simds:.0f} |")
+    lines += ["", "Raw means:", "", "| kernel | counter | value |", "|---|---|---|"]
+    for k in sorted(mean):
+        for c in sorted(mean[k]):
+            lines.append(f"| {k} | {c} | {mean[k][c]:.0f} |")
+    path = os.path.join(ROOT, "profiles", f"counters_{tag}.md")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return path
+
+
+def profile_main(argv):
+    """python bench.py summarize-trace DIR TAG TIMED NOTE CMD...
+       python bench.py record-traffic FETCH_DIR WRITE_DIR TAG CMD...
+       python bench.py summarize-counters DIR[,DIR...] TAG CMD..."""
+    if argv[0] == "summarize-counters":
+        print(summarize_counters(argv[1].split(","), argv[2], argv[3:]))
+    elif argv[0] == "summarize-trace":
+        print(summarize_trace(argv[1], argv[2], argv[5:], int(argv[3]), argv[4]))
+    elif argv[0] == "record-traffic":
+        print(record_traffic(argv[1], argv[2], argv[3], argv[4:]))
+    else:
+        raise SystemExit(profile_main.__doc__)
     return 0
 
 
@@ -632,6 +939,24 @@ def main(argv=None):
     achieved = flops[dominant] / dom_t / 1e12
     traffic = load_traffic(dominant, f"c3_fwdbwd_{'causal' if causal else 'noncausal'}_b{B}h{H}n{n}d{d}")
     fwd_lit = 4 * B * H * n * n * d / (per_stage["fwd"] * 1e-3) / 1e12
+    # Each pass counted two ways: literal 4*B*H*n^2*d (the metric's formula,
+    # all n^2 pairs, one product pair per pass), and algorithmic (visible
+    # pairs; forward 2 products, backward 5, 2*d FLOP per pair each).
+    t_fwd = per_stage["fwd"] * 1e-3
+    t_bwd = (per_stage["bwd_preprocess"] + per_stage["bwd_dkdv"] + per_stage["bwd_dq"]) * 1e-3
+    lit = 4 * B * H * n * n * d
+    pairs = B * H * visible_pairs(n, n, causal)
+    flop_report = {
+        "fwd": {"ms": round(t_fwd * 1e3, 4), "flop_literal": lit, "flop_algorithmic": 4 * d * pairs,
+                "tflops_literal": round(lit / t_fwd / 1e12, 2),
+                "tflops_algorithmic": round(4 * d * pairs / t_fwd / 1e12, 2)},
+        "bwd": {"ms": round(t_bwd * 1e3, 4), "flop_literal": lit, "flop_algorithmic": 10 * d * pairs,
+                "tflops_literal": round(lit / t_bwd / 1e12, 2),
+                "tflops_algorithmic": round(10 * d * pairs / t_bwd / 1e12, 2)},
+        "step": {"flop_literal": 2 * lit, "flop_algorithmic": step_flops,
+                 "tflops_literal": round(2 * lit / (ms_per_step * 1e-3) / 1e12, 2),
+                 "tflops_algorithmic": round(value, 2)},
+    }
     fwd_pct = 100 * flops["fwd"] / (per_stage["fwd"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS
 
     out = {
@@ -654,6 +979,7 @@ def main(argv=None):
         "sclk_mhz_mean_fwd": sclk,
         "fwd_pct_bf16_peak_at_sclk": round(fwd_pct * PEAK_SCLK_MHZ / sclk, 2) if sclk else None,
         "kernels": kernels,
+        "flops": flop_report,
         "roofline": {
             "kernel": dominant,
             "bound": "mfma",
@@ -672,4 +998,6 @@ def main(argv=None):
 
 
 if __name__ == "__main__":
+    if len(sys.argv) > 1 and sys.argv[1] in ("summarize-trace", "record-traffic", "summarize-counters"):
+        sys.exit(profile_main(sys.argv[1:]))
     sys.exit(main())
