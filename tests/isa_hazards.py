@@ -11,9 +11,17 @@ operand of another product) whose distance from the product, minimised over
 all paths, is below the requirement.  Chained accumulation (the register as
 the C operand of the next product) is interlocked and not checked.
 
-Requirements used: passes + 2 wait states, the figure the compiler itself
-emits in straight-line code (18 for the 16-pass fp32 32x32x2 product, 10 for
-the 8-pass bf16 32x32x16 product).
+Requirements used: the wait states the compiler itself puts between a
+product and a read of its result in straight-line gfx950 code (s_nop 15 +
+s_nop 1 = 18 for the fp32 32x32x2 product, s_nop 11 = 12 for the bf16
+32x32x16 product, s_nop 7 = 8 for the bf16 16x16x32 product), the same for
+a vector, store, LDS-write, AGPR-copy or product-operand read.
+
+The reverse direction is checked too: a product that reads an operand (A, B
+or the accumulator C) written by a vector instruction needs 2 wait states
+after it (the compiler emits s_nop 0 plus the s_waitcnt before the product,
+or s_nop 1).  The compiler counts both for its own products; products
+written as inline assembly are counted by nobody but this check.
 """
 from __future__ import annotations
 
@@ -22,10 +30,11 @@ from collections import defaultdict
 
 NEED = {
     "v_mfma_f32_32x32x2_f32": 18,
-    "v_mfma_f32_32x32x16_bf16": 10,
-    "v_mfma_f32_16x16x32_bf16": 6,
+    "v_mfma_f32_32x32x16_bf16": 12,
+    "v_mfma_f32_16x16x32_bf16": 8,
 }
 DEFAULT_NEED = 18  # unknown products: the longest requirement above
+VALU_TO_PRODUCT = 2
 
 
 def need_of(op: str) -> int:
@@ -113,19 +122,27 @@ def check_function(items: list[tuple[str, str]]) -> list[tuple[str, str, tuple[s
         op, ops = _ops(ins)
         return int(ops[0], 0) + 1 if op == "s_nop" else 1
 
-    def nearest(bi: int, pos: int, reg, budget: int, seen: frozenset):
-        """(wait states, needed) of the closest product writing reg before
-        (bi, pos) on any path, minimising wait states - needed; None if no
-        product within budget."""
+    def writer_need(op: str, valu: bool):
+        """Wait states a reader needs after a write by op: products (valu
+        False) or vector instructions (valu True); None for other writers."""
+        if op.startswith("v_mfma"):
+            return None if valu else need_of(op)
+        if valu and op.startswith("v_"):
+            return VALU_TO_PRODUCT
+        return None
+
+    def nearest(bi: int, pos: int, reg, budget: int, seen: frozenset, valu: bool = False):
+        """(wait states, needed) of the closest writer of reg before (bi, pos)
+        on any path that is a product (valu False) or a vector instruction
+        (valu True), minimising wait states - needed; None if there is none
+        within budget or another instruction writes reg first."""
         dist = 0
         lst = blocks[bi]["ins"]
         for j in range(pos - 1, -1, -1):
             op, ops = _ops(lst[j])
-            if op.startswith("v_mfma"):
-                if ops and reg in registers(ops[0]):
-                    return dist, need_of(op)
-            elif ops and not op.startswith("s_") and not _is_store(op) and reg in registers(ops[0]):
-                return None  # rewritten by something else first
+            if ops and not op.startswith("s_") and not _is_store(op) and reg in registers(ops[0]):
+                need = writer_need(op, valu)
+                return None if need is None else (dist, need)
             dist += states(lst[j])
             if dist >= budget:
                 return None
@@ -133,7 +150,7 @@ def check_function(items: list[tuple[str, str]]) -> list[tuple[str, str, tuple[s
         for p in preds.get(bi, []):
             if (p, reg) in seen:
                 continue
-            r = nearest(p, len(blocks[p]["ins"]), reg, budget - dist, seen | {(p, reg)})
+            r = nearest(p, len(blocks[p]["ins"]), reg, budget - dist, seen | {(p, reg)}, valu)
             if r is not None:
                 r = (r[0] + dist, r[1])
                 if best is None or r[0] - r[1] < best[0] - best[1]:
@@ -158,6 +175,12 @@ def check_function(items: list[tuple[str, str]]) -> list[tuple[str, str, tuple[s
                     r = nearest(bi, j, reg, budget, frozenset())
                     if r is not None and r[0] < r[1]:
                         out.append((b["label"], ins, reg, r[0], r[1]))
+            if op.startswith("v_mfma"):
+                for tok in ops[1:4]:
+                    for reg in registers(tok):
+                        r = nearest(bi, j, reg, VALU_TO_PRODUCT + 1, frozenset(), valu=True)
+                        if r is not None and r[0] < r[1]:
+                            out.append((b["label"], ins, reg, r[0], r[1]))
     return out
 
 

@@ -12,7 +12,7 @@ from isa_hazards import check_text
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "exact_attention_05_amd", "csrc")
-SOURCES = ["fa_fwd.hip", "fa_bwd.hip", "fa_decode.hip"]
+SOURCES = ["fa_fwd.hip", "fa_fwd_merge.hip", "fa_bwd.hip", "fa_decode.hip"]
 
 
 def _device_asm(src: str, out_dir: str) -> str:
@@ -87,3 +87,20 @@ def test_checker_ignores_accumulation_chains():
 .Lfunc_end0:
 """
     assert not check_text(frag)
+
+
+def test_checker_flags_a_vector_write_just_before_a_product():
+    frag = """_Zk:
+	v_xor_b32_e32 v20, s0, v20
+{pad}
+	v_mfma_f32_32x32x16_bf16 v[0:15], v[16:19], v[20:23], 0
+	s_nop 15
+	v_add_f32_e32 v30, v3, v31
+	s_endpgm
+.Lfunc_end0:
+"""
+    assert check_text(frag.format(pad=""))                 # 0 wait states < 2
+    assert check_text(frag.format(pad="\ts_nop 0"))        # 1
+    assert not check_text(frag.format(pad="\ts_nop 1"))    # 2
+    # a load writing the operand is not a vector write (s_waitcnt covers it)
+    assert not check_text(frag.format(pad="").replace("v_xor_b32_e32 v20, s0, v20", "ds_read_b128 v[20:23], v1"))
