@@ -178,6 +178,9 @@ __global__ __launch_bounds__(WAVES * 64) void bwd_dkdv_bf16_kernel(BwdArgs a, in
                       : bf16x8{};
     vf[c] = key < n_k ? *reinterpret_cast<const bf16x8*>(vp + (size_t)key * D + 16 * c + 8 * hi)
                       : bf16x8{};
+    // moved into AGPRs once: the products read them there
+    asm volatile("" : "+a"(kf[c]));
+    asm volatile("" : "+a"(vf[c]));
   }
 
   // Query stages holding rows that see some key of this workgroup.
@@ -214,6 +217,10 @@ __global__ __launch_bounds__(WAVES * 64) void bwd_dkdv_bf16_kernel(BwdArgs a, in
     }
   };
 
+  // Register files: the dK, dV accumulators (compiler-placed products) and
+  // the K, V operands in AGPRs for the whole pass; S and dP, which the vector
+  // code reads, in vector registers (products written as inline assembly,
+  // see mfma_bf16_v).
   f32x16 dk[C::kDB], dv[C::kDB];
 #pragma unroll
   for (int db = 0; db < C::kDB; ++db) { dk[db] = f32x16{}; dv[db] = f32x16{}; }
@@ -282,8 +289,6 @@ __global__ __launch_bounds__(WAVES * 64) void bwd_dkdv_bf16_kernel(BwdArgs a, in
     constexpr bool FIRST = decltype(first_tag)::value;
     const char* qt = sq[BUF];
     const char* gt = sdo[BUF];
-    s = f32x16{};
-    dp = f32x16{};
     static_for<0, (C::kS1 < C::kAhead ? C::kS1 : C::kAhead)>([&](auto i) __attribute__((always_inline)) {
       fa[decltype(i)::value] = tqt.read_rows(qt, R0, decltype(i)::value);
       fb[decltype(i)::value] = tqt.read_rows(gt, R0, decltype(i)::value);
@@ -299,8 +304,13 @@ __global__ __launch_bounds__(WAVES * 64) void bwd_dkdv_bf16_kernel(BwdArgs a, in
         fa[(c + C::kAhead) % C::kRing] = tqt.read_rows(qt, R0, c + C::kAhead);
         fb[(c + C::kAhead) % C::kRing] = tqt.read_rows(gt, R0, c + C::kAhead);
       }
-      s = mfma_bf16(fa[c % C::kRing], kf[c], s);
-      dp = mfma_bf16(fb[c % C::kRing], vf[c], dp);
+      if constexpr (c == 0) {
+        s = mfma_bf16_v0(fa[0], kf[0]);
+        dp = mfma_bf16_v0(fb[0], vf[0]);
+      } else {
+        mfma_bf16_v(s, fa[c % C::kRing], kf[c]);
+        mfma_bf16_v(dp, fb[c % C::kRing], vf[c]);
+      }
       static_for<c * 8 / C::kS1, (c + 1) * 8 / C::kS1>([&](auto pr) __attribute__((always_inline)) {
         stage_b(decltype(pr)::value);
       });
@@ -325,6 +335,7 @@ __global__ __launch_bounds__(WAVES * 64) void bwd_dkdv_bf16_kernel(BwdArgs a, in
         dv[db] = mfma_bf16(fa[f % C::kRing], bf16x8_of(pb[c2]), dv[db]);
         dk[db] = mfma_bf16(fb[f % C::kRing], bf16x8_of(dsb[c2]), dk[db]);
       }
+      if constexpr (f == 0) fence_results(s, dp);  // S and dP are read from here on
       static_for<f * 16 / C::kS2, (f + 1) * 16 / C::kS2>([&](auto i) __attribute__((always_inline)) {
         stage_a(mask_tag, decltype(i)::value, qrow0);
       });
@@ -354,11 +365,13 @@ __global__ __launch_bounds__(WAVES * 64) void bwd_dkdv_bf16_kernel(BwdArgs a, in
   };
 
   // Stages [b_lo, b_hi) need no mask: every row sees every key of the
-  // workgroup (none when its keys run past n_k).  The others -- causal
-  // diagonal, window edges, a ragged last stage -- are masked.
-  int b_lo = nblocks, b_hi = nblocks;
-  if (k0 + C::kBK <= n_k) {
-    const int full_lo = band.q_full_lo(k0 + C::kBK), full_hi = min(n_q, band.q_full_hi(k0));
+  // workgroup below n_k.  The others -- causal diagonal, window edges, a
+  // ragged last stage -- are masked.  Keys past n_k need no mask: their K and
+  // V rows are zero, a product keeps each key's column apart, and their dK
+  // and dV are never stored.
+  int b_lo, b_hi;
+  {
+    const int full_lo = band.q_full_lo(k1), full_hi = min(n_q, band.q_full_hi(k0));
     b_lo = min(nblocks, max(0, (full_lo - qb_first * C::kBQ + C::kBQ - 1) / C::kBQ));
     b_hi = max(b_lo, min(nblocks, (full_hi - qb_first * C::kBQ) / C::kBQ));
   }
@@ -387,13 +400,14 @@ __global__ __launch_bounds__(WAVES * 64) void bwd_dkdv_bf16_kernel(BwdArgs a, in
     for (int r0 = 0; r0 < C::kBQ; r0 += 32) {
       const int qs = (qb_first + b) * C::kBQ + r0;
       if (qs + 32 <= wq_lo || qs >= wq_hi) continue;  // no row here sees a key of this wave
-      s = f32x16{};
-      dp = f32x16{};
+      s = mfma_bf16_v0(tqt.read_rows(qt, r0, 0), kf[0]);
+      dp = mfma_bf16_v0(tqt.read_rows(gt, r0, 0), vf[0]);
 #pragma unroll
-      for (int c = 0; c < C::kDC; ++c) {
-        s = mfma_bf16(tqt.read_rows(qt, r0, c), kf[c], s);
-        dp = mfma_bf16(tqt.read_rows(gt, r0, c), vf[c], dp);
+      for (int c = 1; c < C::kDC; ++c) {
+        mfma_bf16_v(s, tqt.read_rows(qt, r0, c), kf[c]);
+        mfma_bf16_v(dp, tqt.read_rows(gt, r0, c), vf[c]);
       }
+      fence_results(s, dp);
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         lv[g4] = *reinterpret_cast<const f32x4*>(&slse[buf][r0 + 8 * g4 + 4 * hi]);

@@ -153,6 +153,35 @@ __device__ __forceinline__ void settle_acc(f32x16 (&x)[N], f32x16 (&y)[N]) {
   }
 }
 
+// ---- bf16 products with the register file of each operand chosen here
+// In a kernel that needs more than the 256 vector registers, the compiler
+// gives every product the accumulation registers (AGPRs) for its result, and
+// vector code that reads a result copies it back one register at a time.
+// Written as inline assembly, a product whose result the vector code reads
+// (scores) can keep it in vector registers, with its constant B operand in
+// AGPRs.  The compiler counts no wait states around inline assembly: a
+// kernel using these fences each product's result (fence_results) before
+// any read of it; the vector writes of their A operands are loads, which the
+// compiler's own s_waitcnt covers.  The hazard check on the built assembly
+// verifies every path.
+
+// c = a b (zero accumulator): c in vector registers, b in AGPRs.
+__device__ __forceinline__ f32x16 mfma_bf16_v0(bf16x8 a, bf16x8 b) {
+  f32x16 c;
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "a"(b));
+  return c;
+}
+// c += a b: c in vector registers, b in AGPRs.
+__device__ __forceinline__ void mfma_bf16_v(f32x16& c, bf16x8 a, bf16x8 b) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "a"(b));
+}
+// 12 wait states inside a statement that takes the two results x and y, so
+// every later read of them depends on it; placed after the last product that
+// writes them.
+__device__ __forceinline__ void fence_results(f32x16& x, f32x16& y) {
+  asm volatile("s_nop 11" : "+v"(x), "+v"(y));
+}
+
 // Calls f(std::integral_constant<int, I>{}) for I = BEGIN .. END-1, so that
 // the index is a compile-time constant in the body.
 template <int BEGIN, int END, typename F>
