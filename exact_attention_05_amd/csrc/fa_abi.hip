@@ -10,6 +10,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <atomic>
 #include <mutex>
 
 // Scratch memory of fa_backward_noalloc: the backward workspace (the two
@@ -347,6 +348,29 @@ int noalloc_scratch(void* stream, void** out) {
 }
 
 }  // namespace
+
+namespace fa {
+
+int compute_units(hipStream_t stream) {
+  static std::atomic<int> cached[kMaxDevices] = {};
+  int dev = -1;
+  if (stream != nullptr) {
+    hipDevice_t d = -1;
+    if (hipStreamGetDevice(stream, &d) != hipSuccess) return 0;
+    dev = d;
+  } else if (hipGetDevice(&dev) != hipSuccess) {
+    return 0;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 0;
+    cached[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+}  // namespace fa
 
 extern "C" {
 

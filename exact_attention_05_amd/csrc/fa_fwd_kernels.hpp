@@ -522,65 +522,92 @@ void fwd_bf16_pp_kernel(FwdArgs a, int n_qtiles) {
   __shared__ __attribute__((aligned(1024))) char sk[2][C::KV::kBytes];
   __shared__ __attribute__((aligned(1024))) char sv[2][C::KV::kBytes];
 
-  int bh, qt;
-  if (CAUSAL) {
-    costliest_first(blockIdx.x, gridDim.x, n_qtiles, bh, qt);
-    qt = n_qtiles - 1 - qt;
-  } else {
-    const int work = xcd_remap(blockIdx.x, gridDim.x);
-    bh = work / n_qtiles;
-    qt = work - bh * n_qtiles;
-  }
-
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = wave >> 2;  // 0: waves 0-3, 1: waves 4-7, one half-step behind
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int hi = lane >> 5;
-  const int q0 = qt * C::kBM;
-  const int qw = q0 + wave * 32;
-  const int qi = qw + l32;
   const int n_q = a.n_q, n_k = a.n_k;
   const float sl2 = a.scale_log2;
-
-  const __bf16* qp = static_cast<const __bf16*>(a.q) + (size_t)bh * n_q * D;
-  const int kvh = kv_head_index(bh, a.H, a.group);
-  const __bf16* kp = static_cast<const __bf16*>(a.k) + (size_t)kvh * n_k * D;
-  const __bf16* vp = static_cast<const __bf16*>(a.v) + (size_t)kvh * n_k * D;
-
-  bf16x8 qf[C::kDC];
-#pragma unroll
-  for (int c = 0; c < C::kDC; ++c) {
-    if (qi < n_q)
-      qf[c] = *reinterpret_cast<const bf16x8*>(qp + (size_t)qi * D + 16 * c + 8 * hi);
-    else
-      qf[c] = bf16x8{};
-  }
-
   const Band band = band_of(a, CAUSAL);
-  const int q_end = min(n_q, q0 + C::kBM);
-  const int t_lo = band.key_lo(q0) / C::kBN;
-  const int t_hi = max(t_lo, (band.key_hi(q_end) + C::kBN - 1) / C::kBN);
-  const int f_lo = min(t_hi, max(t_lo, (band.key_full_lo(q_end) + C::kBN - 1) / C::kBN));
-  const int f_hi = max(f_lo, min(t_hi, band.key_full_hi(q0) / C::kBN));
-  const int n = f_hi - f_lo;  // blocks of the ping-pong
-  int vlo, vspan;
-  band.key_range(qi, vlo, vspan);
 
   TileDma<D, C::kBN, C::kWaves> dma;
   dma.init(wave, lane);
+  TileDma<D, C::kBN, 4> dma4;
+  dma4.init(wave & 3, lane);
   TileLane<D, C::kBN> tl;
   tl.init(lane);
   const uint32_t sk_addr = lds_address(&sk[0][0]);
   const uint32_t sv_addr = lds_address(&sv[0][0]);
-  // Block t lives in buffer (t - f_lo) mod 2.
-  auto bufof = [&](int t) { return (t - f_lo) & 1; };
-  auto load_tile = [&](int t) {
-    const int k0 = t * C::kBN;
-    dma.load(kp + (size_t)k0 * D, n_k - k0, sk_addr + bufof(t) * C::KV::kBytes);
-    dma.load(vp + (size_t)k0 * D, n_k - k0, sv_addr + bufof(t) * C::KV::kBytes);
+
+  // Tile w of the launch (a query tile of one head) and its key blocks:
+  // [t_lo, t_hi) visited, [f_lo, f_hi) unmasked (the ping-pong).  Without
+  // the causal mask a workgroup may take several tiles (w, w + gridDim.x,
+  // ...: a grid of one workgroup per compute unit), the next tile's Q and
+  // first K/V block loading while the current tile's output is written.
+  struct TileW {
+    int bh, q0, t_lo, t_hi, f_lo, f_hi;
+    const __bf16 *qp, *kp, *vp;
   };
+  auto tile_of = [&](int w) {
+    TileW tw;
+    int qt;
+    if (CAUSAL) {
+      costliest_first(w, n_qtiles * a.BH, n_qtiles, tw.bh, qt);
+      qt = n_qtiles - 1 - qt;
+    } else {
+      const int work = xcd_remap(w, n_qtiles * a.BH);
+      tw.bh = work / n_qtiles;
+      qt = work - tw.bh * n_qtiles;
+    }
+    tw.q0 = qt * C::kBM;
+    const int q_end = min(n_q, tw.q0 + C::kBM);
+    tw.t_lo = band.key_lo(tw.q0) / C::kBN;
+    tw.t_hi = max(tw.t_lo, (band.key_hi(q_end) + C::kBN - 1) / C::kBN);
+    tw.f_lo = min(tw.t_hi, max(tw.t_lo, (band.key_full_lo(q_end) + C::kBN - 1) / C::kBN));
+    tw.f_hi = max(tw.f_lo, min(tw.t_hi, band.key_full_hi(tw.q0) / C::kBN));
+    tw.qp = static_cast<const __bf16*>(a.q) + (size_t)tw.bh * n_q * D;
+    const int kvh = kv_head_index(tw.bh, a.H, a.group);
+    tw.kp = static_cast<const __bf16*>(a.k) + (size_t)kvh * n_k * D;
+    tw.vp = static_cast<const __bf16*>(a.v) + (size_t)kvh * n_k * D;
+    return tw;
+  };
+  // Block t of tile tw lives in buffer (t - tw.f_lo) mod 2.
+  auto load_tile_of = [&](const TileW& tw, int t) {
+    const int k0 = t * C::kBN;
+    const int buf = (t - tw.f_lo) & 1;
+    dma.load(tw.kp + (size_t)k0 * D, n_k - k0, sk_addr + buf * C::KV::kBytes);
+    dma.load(tw.vp + (size_t)k0 * D, n_k - k0, sv_addr + buf * C::KV::kBytes);
+  };
+  bf16x8 qf[C::kDC];
+  auto load_q = [&](const TileW& tw) {
+    const int row = tw.q0 + wave * 32 + l32;
+#pragma unroll
+    for (int c = 0; c < C::kDC; ++c) {
+      if (row < n_q)
+        qf[c] = *reinterpret_cast<const bf16x8*>(tw.qp + (size_t)row * D + 16 * c + 8 * hi);
+      else
+        qf[c] = bf16x8{};
+    }
+  };
+
+  const int total = n_qtiles * a.BH;
+  TileW tw = tile_of(blockIdx.x);
+  load_q(tw);
+  if (tw.t_lo < tw.t_hi) load_tile_of(tw, tw.t_lo);
+  for (int w = blockIdx.x; w < total; w += gridDim.x) {
+  const int bh = tw.bh, q0 = tw.q0;
+  const int t_lo = tw.t_lo, t_hi = tw.t_hi, f_lo = tw.f_lo, f_hi = tw.f_hi;
+  const __bf16* const kp = tw.kp;
+  const __bf16* const vp = tw.vp;
+  const int qw = q0 + wave * 32;
+  const int qi = qw + l32;
+  const int n = f_hi - f_lo;  // blocks of the ping-pong
+  int vlo, vspan;
+  band.key_range(qi, vlo, vspan);
+  auto bufof = [&](int t) { return (t - f_lo) & 1; };
+  auto load_tile = [&](int t) { load_tile_of(tw, t); };
 
   f32x16 oacc[C::kDB];
 #pragma unroll
@@ -655,8 +682,7 @@ void fwd_bf16_pp_kernel(FwdArgs a, int n_qtiles) {
           oacc[db] = mfma_bf16(tl.read_cols_tr(vs, kb * 32 + 16 * c2, 32 * db), bf16x8_of(pw[kb][c2]), oacc[db]);
   };
 
-  if (t_lo < t_hi) load_tile(t_lo);
-  int t = t_lo;
+  int t = t_lo;  // block t_lo's copy was started with the tile's Q load
   for (; t < f_lo; ++t) masked_block(t, true);  // up to block f_lo's copy
 
   if (n > 0) {
@@ -755,8 +781,6 @@ void fwd_bf16_pp_kernel(FwdArgs a, int n_qtiles) {
     // to f_hi) and V of f_lo + i + 1 (up to f_hi), both first read two
     // half-steps later; waves 4-7 wait for them before the barrier in the
     // middle of their next step, which precedes the first read.
-    TileDma<D, C::kBN, 4> dma4;
-    dma4.init(wave & 3, lane);
     auto step = [&](auto p_tag, auto pv_tag, auto s_tag, int i) __attribute__((always_inline)) {
       constexpr int P = decltype(p_tag)::value;  // i mod 2
       phase_a(std::integral_constant<int, P>{}, std::integral_constant<int, P ^ 1>{}, pv_tag, s_tag);
@@ -809,10 +833,20 @@ void fwd_bf16_pp_kernel(FwdArgs a, int n_qtiles) {
   // look-ahead.
   for (; t < t_hi; ++t) masked_block(t, true);
 
+  // The next tile's Q and first K/V block, once every wave is done with
+  // this tile's (Q is in registers: this wave's last product has issued;
+  // the barrier covers the LDS buffers).
+  if (w + (int)gridDim.x < total) {
+    __syncthreads();
+    tw = tile_of(w + gridDim.x);
+    load_q(tw);
+    if (tw.t_lo < tw.t_hi) load_tile_of(tw, tw.t_lo);
+  }
+
   const float lt = sum_halves(l);
   if constexpr (MERGE) {
     if (qi < n_q) merge_store(a, (size_t)bh * n_q + qi, hi, oacc, m, lt);
-    return;
+    continue;
   }
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   if (qi < n_q) {
@@ -827,6 +861,7 @@ void fwd_bf16_pp_kernel(FwdArgs a, int n_qtiles) {
         *reinterpret_cast<bf16x4*>(op + 32 * db + 8 * g4 + 4 * hi) = r;
       }
     if (hi == 0) a.lse[(size_t)bh * n_q + qi] = (m + fast_log2(lt)) * kLn2;
+  }
   }
 }
 
@@ -1075,7 +1110,17 @@ template <int D, bool CAUSAL, bool MERGE>
 hipError_t fwd_bf16_pp(const FwdArgs& a, hipStream_t stream) {
   using C = Bf16FwdCfg<D, 8>;
   const int n_qtiles = (a.n_q + C::kBM - 1) / C::kBM;
-  return launch(fwd_bf16_pp_kernel<D, CAUSAL, MERGE>, n_qtiles * a.BH, C::kThreads, a, n_qtiles, stream);
+  const int total = n_qtiles * a.BH;
+  // Without the mask every tile costs the same: one workgroup per compute
+  // unit (one fills it) walks tiles w, w + grid, ..., each loading the next
+  // tile while it writes the current one.  Causal tiles differ in cost and
+  // keep one workgroup each, dispatched costliest first.
+  int grid = total;
+  if (!CAUSAL) {
+    const int cus = compute_units(stream);
+    if (cus > 0 && total > cus) grid = cus;
+  }
+  return launch(fwd_bf16_pp_kernel<D, CAUSAL, MERGE>, grid, C::kThreads, a, n_qtiles, stream);
 }
 
 template <int D, bool CAUSAL, bool MERGE>

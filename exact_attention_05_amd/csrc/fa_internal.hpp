@@ -210,6 +210,10 @@ struct MergeArgs {
 
 // Each launcher enqueues its kernel(s) on `stream` and returns the HIP status
 // of the launch.  Shapes were validated by the caller.
+// Compute units of the device that `stream` runs on (0 if unknown); cached
+// per device.
+int compute_units(hipStream_t stream);
+
 hipError_t launch_fwd_bf16(const FwdArgs& a, int d, bool causal, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdArgs& a, int d, bool causal, hipStream_t stream);
 // The same passes with the epilogue merging into a.o_prior, a.lse_prior.
