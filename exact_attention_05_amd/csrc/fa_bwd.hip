@@ -40,7 +40,10 @@
 // LSE_i and D_i are one register each, and dQ^T += K^T dS^T reads K^T
 // through the transposing read.  Key blocks that need no mask for any row of
 // the workgroup run through a separate code path, two at a time with fixed
-// LDS buffers.
+// LDS buffers.  At d = 128 with 256-row workgroups the two waves of each
+// SIMD run half a step apart instead (bwd_dq_bf16_pp_kernel): one wave's
+// products (dQ of the previous key block, S and dP of this one) beside the
+// other wave's exponentials.
 //
 // Masks: the query offset and sliding window of the extended entry points
 // (see Band) decide which query stages or key blocks a workgroup visits at
@@ -693,6 +696,282 @@ void bwd_dq_bf16_kernel(BwdArgs a, int n_qtiles) {
   }
 }
 
+// bf16 stage 3 at d = 128, the two waves of each SIMD half a step apart
+// (as the forward's ping-pong kernel): a wave's step i is
+//   phase A(i): dQ^T += K^T dS^T of block f_lo + i - 1 (if i > 0), then
+//               S^T = K Q^T and dP^T = V dO^T of block f_lo + i (if i < n)
+//   phase B(i): P = exp2(scale_log2 S - LSE2), dS = P o (dP - D), bf16
+// so that one wave's vector work runs beside the other wave's products.
+// Phase A reads two K blocks (K^T of the previous block for dQ, K rows of
+// this one for S): K blocks take four LDS buffers (three would do; four
+// keep the buffer indices compile-time constants in a loop unrolled by
+// four), V blocks two.  Waves 4-7
+// run one barrier behind and issue the copies in their phase B: in B(i) K
+// and V of block f_lo + i + 2, into the buffers of blocks f_lo + i - 1 (K,
+// last read in A(i)) and f_lo + i (V, last read in A(i)); they wait for the
+// copies before the barrier in the middle of their next step, which
+// precedes the first read.  Blocks that need a mask (before f_lo: window
+// edges; from f_hi on: causal diagonal, key tail) take the plain path.
+// The same products as bwd_dq_bf16_kernel, except that dP is accumulated
+// from zero and D subtracted in phase B (a tile of -D as the products'
+// starting value would hold 16 more registers), so the two kernels' dQ may
+// differ in the last bf16 bit.  c3 dQ 331.9 -> 321.8 us, causal B=2 H=16
+// 176.4 -> 172.6 us, n = 8192 1290.5 -> 1240.3 us (same box).
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_dq_bf16_pp_kernel(BwdArgs a, int n_qtiles) {
+  using C = DqCfg<D, 8>;
+  constexpr int kKBufs = 4;
+  __shared__ __attribute__((aligned(1024))) char sv[2][C::KV::kBytes];
+  __shared__ __attribute__((aligned(1024))) char sk[kKBufs][C::KV::kBytes];
+
+  int bh, qt;
+  if (CAUSAL) {
+    costliest_first(blockIdx.x, gridDim.x, n_qtiles, bh, qt);
+    qt = n_qtiles - 1 - qt;
+  } else {
+    const int work = xcd_remap(blockIdx.x, gridDim.x);
+    bh = work / n_qtiles;
+    qt = work - bh * n_qtiles;
+  }
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;  // 0: waves 0-3, 1: waves 4-7, one half-step behind
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+  const int n_q = a.n_q, n_k = a.n_k;
+  const float sl2 = a.scale_log2;
+  const int q0 = qt * C::kBM;
+  const int qw = q0 + wave * 32;
+  const int qi = qw + l32;  // this lane's query (column of S^T)
+
+  const __bf16* qp = static_cast<const __bf16*>(a.q) + (size_t)bh * n_q * D;
+  const __bf16* dop = static_cast<const __bf16*>(a.dO) + (size_t)bh * n_q * D;
+  const int kvh = kv_head_index(bh, a.H, a.group);
+  const __bf16* kp = static_cast<const __bf16*>(a.k) + (size_t)kvh * n_k * D;
+  const __bf16* vp = static_cast<const __bf16*>(a.v) + (size_t)kvh * n_k * D;
+
+  bf16x8 qf[C::kDC], gf[C::kDC];
+#pragma unroll
+  for (int c = 0; c < C::kDC; ++c) {
+    if (qi < n_q) {
+      qf[c] = *reinterpret_cast<const bf16x8*>(qp + (size_t)qi * D + 16 * c + 8 * hi);
+      gf[c] = *reinterpret_cast<const bf16x8*>(dop + (size_t)qi * D + 16 * c + 8 * hi);
+    } else {
+      qf[c] = bf16x8{};
+      gf[c] = bf16x8{};
+    }
+  }
+  // Rows past n_q have zero Q and dO, so their (unstored) dQ stays finite.
+  const float lse2 = (qi < n_q) ? a.lse2[(size_t)bh * n_q + qi] : 0.f;
+  const float dlt = (qi < n_q) ? a.delta[(size_t)bh * n_q + qi] : 0.f;
+
+  const Band band = band_of(a, CAUSAL);
+  const int q_end = min(n_q, q0 + C::kBM);
+  const int t_lo = band.key_lo(q0) / C::kBN;
+  const int t_hi = max(t_lo, (band.key_hi(q_end) + C::kBN - 1) / C::kBN);
+  const int f_lo = min(t_hi, max(t_lo, (band.key_full_lo(q_end) + C::kBN - 1) / C::kBN));
+  const int f_hi = max(f_lo, min(t_hi, band.key_full_hi(q0) / C::kBN));
+  const int n = f_hi - f_lo;  // blocks of the ping-pong
+  int vlo, vspan;  // keys this lane's query sees: [vlo, vlo + vspan]
+  band.key_range(qi, vlo, vspan);
+
+  TileDma<D, C::kBN, C::kWaves> dma;
+  dma.init(wave, lane);
+  TileDma<D, C::kBN, 4> dma4;
+  dma4.init(wave & 3, lane);
+  TileLane<D, C::kBN> tkv;
+  tkv.init(lane);
+  const uint32_t sk_addr = lds_address(&sk[0][0]);
+  const uint32_t sv_addr = lds_address(&sv[0][0]);
+  // Block t: K in buffer (t - f_lo) mod 3, V in buffer (t - f_lo) mod 2.
+  auto kbufof = [&](int t) { return (t - f_lo) & (kKBufs - 1); };
+  auto vbufof = [&](int t) { return (t - f_lo) & 1; };
+  auto load_tile = [&](int t) {
+    const int k0 = t * C::kBN;
+    dma.load(kp + (size_t)k0 * D, n_k - k0, sk_addr + kbufof(t) * C::KV::kBytes);
+    dma.load(vp + (size_t)k0 * D, n_k - k0, sv_addr + vbufof(t) * C::KV::kBytes);
+  };
+
+  f32x16 dq[C::kDB];
+#pragma unroll
+  for (int db = 0; db < C::kDB; ++db) dq[db] = f32x16{};
+
+  // A masked block (plain path): wait for block t, barrier, start the copy
+  // of block t + 1, then S, dP, masked dS and dQ for both 32-key halves.
+  // dP^T accumulates from -D, so the products give dP - D directly.
+  auto masked_block = [&](int t) {
+    wait_lds_dma();
+    __syncthreads();
+    if (t + 1 < t_hi) load_tile(t + 1);
+    const char* ks = sk[kbufof(t)];
+    const char* vs = sv[vbufof(t)];
+    const int k0 = t * C::kBN;
+#pragma unroll
+    for (int kb = 0; kb < C::kKB; ++kb) {
+      // every key of the sub-block hidden from this wave
+      if (k0 + kb * 32 >= band.key_hi(qw + 32) || k0 + kb * 32 + 32 <= band.key_lo(qw)) continue;
+      f32x16 s = f32x16{}, dp;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) dp[i] = -dlt;
+#pragma unroll
+      for (int c = 0; c < C::kDC; ++c) {
+        s = mfma_bf16(tkv.read_rows(ks, kb * 32, c), qf[c], s);
+        dp = mfma_bf16(tkv.read_rows(vs, kb * 32, c), gf[c], dp);
+      }
+      u32x4 dsb[2];
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) {
+        float p0 = fast_exp2(fmaf(s[i], sl2, -lse2));
+        float p1 = fast_exp2(fmaf(s[i + 1], sl2, -lse2));
+        const int rel = k0 + kb * 32 + 4 * hi - vlo + 8 * (i >> 2) + (i & 3);  // key - vlo
+        if (!Band::in_range(rel, 0, vspan)) p0 = 0.f;
+        if (!Band::in_range(rel + 1, 0, vspan)) p1 = 0.f;
+        dsb[i >> 3][(i & 7) >> 1] = pack_bf16x2(p0 * dp[i], p1 * dp[i + 1]);
+      }
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+        for (int db = 0; db < C::kDB; ++db)
+          dq[db] = mfma_bf16(tkv.read_cols_tr(ks, kb * 32 + 16 * c2, 32 * db), bf16x8_of(dsb[c2]), dq[db]);
+    }
+  };
+
+  if (t_lo < t_hi) load_tile(t_lo);
+  int t = t_lo;
+  for (; t < f_lo; ++t) masked_block(t);  // up to block f_lo's copy
+
+  if (n > 0) {
+    f32x16 s[C::kKB], dp[C::kKB];  // S^T and dP^T of the wave's current block
+    u32x4 dsb[C::kKB][2];          // its dS as bf16 pairs
+    // Phase A as one stream of product steps: steps 0-15 the dQ products of
+    // the previous block (two transposing K reads each), then for c = 0..7
+    // the S and dP products of both 32-key halves (one K or V row read
+    // each).  Operand reads run kAhead steps ahead through a ring.
+    constexpr int kDq = 2 * C::kKB * C::kDB;   // 16
+    constexpr int kSd = 2 * C::kKB * C::kDC;   // 32
+    constexpr int kAhead = 4;
+    // kc_tag: K buffer of this step's block (the previous block's is the
+    // one before it, mod 4), V buffer kc mod 2; compile-time in the unrolled
+    // loop, run-time in the last few steps.
+    auto phase_a = [&](auto kc_tag, auto dq_tag, auto sd_tag) __attribute__((always_inline)) {
+      constexpr bool DQ = decltype(dq_tag)::value, SD = decltype(sd_tag)::value;
+      constexpr int J0 = DQ ? 0 : kDq, J1 = SD ? kDq + kSd : kDq;
+      const int kc = value_of(kc_tag);
+      const char* kprev = sk[(kc + kKBufs - 1) & (kKBufs - 1)];  // K of the previous block (dQ)
+      const char* kcur = sk[kc];                                 // K and V of this block (S, dP)
+      const char* vcur = sv[kc & 1];
+      auto read = [&](auto j_tag) __attribute__((always_inline)) -> bf16x8 {
+        constexpr int J = decltype(j_tag)::value;
+        if constexpr (J < kDq) {
+          constexpr int kb = J / (2 * C::kDB), c2 = (J / C::kDB) % 2, db = J % C::kDB;
+          return tkv.read_cols_tr(kprev, kb * 32 + 16 * c2, 32 * db);
+        } else {
+          constexpr int c = (J - kDq) / (2 * C::kKB), kb = ((J - kDq) / 2) % C::kKB, v = (J - kDq) % 2;
+          return tkv.read_rows(v ? vcur : kcur, kb * 32, c);
+        }
+      };
+      auto product = [&](auto j_tag, const bf16x8& op) __attribute__((always_inline)) {
+        constexpr int J = decltype(j_tag)::value;
+        if constexpr (J < kDq) {
+          constexpr int kb = J / (2 * C::kDB), c2 = (J / C::kDB) % 2, db = J % C::kDB;
+          dq[db] = mfma_bf16(op, bf16x8_of(dsb[kb][c2]), dq[db]);
+        } else {
+          constexpr int c = (J - kDq) / (2 * C::kKB), kb = ((J - kDq) / 2) % C::kKB, v = (J - kDq) % 2;
+          if constexpr (v == 0)
+            s[kb] = mfma_bf16(op, qf[c], c == 0 ? f32x16{} : s[kb]);
+          else
+            dp[kb] = mfma_bf16(op, gf[c], c == 0 ? f32x16{} : dp[kb]);
+        }
+      };
+      bf16x8 ring[kAhead];
+      phase_barrier();
+      static_for<J0, (J0 + kAhead < J1 ? J0 + kAhead : J1)>([&](auto j) __attribute__((always_inline)) {
+        ring[(decltype(j)::value - J0) % kAhead] = read(j);
+      });
+      __builtin_amdgcn_sched_barrier(0);
+      static_for<J0, J1>([&](auto j) __attribute__((always_inline)) {
+        constexpr int J = decltype(j)::value;
+        product(j, ring[(J - J0) % kAhead]);
+        if constexpr (J + kAhead < J1) ring[(J - J0) % kAhead] = read(std::integral_constant<int, J + kAhead>{});
+        __builtin_amdgcn_sched_barrier(0);  // each product with the read kAhead steps ahead
+      });
+    };
+    // Phase B: dS = P o (dP - D) of both halves, rounded to bf16 pairs.
+    auto phase_b = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int kb = 0; kb < C::kKB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; i += 2) {
+          const float p0 = fast_exp2(fmaf(s[kb][i], sl2, -lse2));
+          const float p1 = fast_exp2(fmaf(s[kb][i + 1], sl2, -lse2));
+          dsb[kb][i >> 3][(i & 7) >> 1] = pack_bf16x2(p0 * (dp[kb][i] - dlt), p1 * (dp[kb][i + 1] - dlt));
+        }
+    };
+    auto step = [&](auto kc_tag, auto dq_tag, auto sd_tag, int i) __attribute__((always_inline)) {
+      phase_a(kc_tag, dq_tag, sd_tag);
+      if (grp == 1) wait_lds_dma();
+      phase_barrier();
+      if (grp == 1) {
+        const int tn = f_lo + i + 2;
+        if (tn <= f_hi && tn < t_hi) {
+          const int k0 = tn * C::kBN;
+          dma4.load(kp + (size_t)k0 * D, n_k - k0, sk_addr + kbufof(tn) * C::KV::kBytes);
+          dma4.load(vp + (size_t)k0 * D, n_k - k0, sv_addr + vbufof(tn) * C::KV::kBytes);
+        }
+      }
+      if constexpr (decltype(sd_tag)::value) phase_b();
+    };
+    // Block f_lo was started by the previous block or the first copy; every
+    // wave waits for its part before the ping-pong starts, and waves 4-7
+    // start block f_lo + 1 (read first at step 1).
+    wait_lds_dma();
+    if (grp == 1) {
+      if (f_lo + 1 <= f_hi && f_lo + 1 < t_hi) {
+        const int k0 = (f_lo + 1) * C::kBN;
+        dma4.load(kp + (size_t)k0 * D, n_k - k0, sk_addr + kbufof(f_lo + 1) * C::KV::kBytes);
+        dma4.load(vp + (size_t)k0 * D, n_k - k0, sv_addr + vbufof(f_lo + 1) * C::KV::kBytes);
+      }
+      phase_barrier();
+    }
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    step(I0{}, F{}, T{}, 0);  // S and dP of block f_lo only
+    int i = 1;
+    for (; i + 3 < n; i += 4) {
+      step(I1{}, T{}, T{}, i);
+      step(I2{}, T{}, T{}, i + 1);
+      step(I3{}, T{}, T{}, i + 2);
+      step(I0{}, T{}, T{}, i + 3);
+    }
+    for (; i < n; ++i) step(i & (kKBufs - 1), T{}, T{}, i);
+    step(n & (kKBufs - 1), T{}, F{}, n);  // the last dQ products only
+    if (grp == 0) phase_barrier();
+    t = f_hi;
+  }
+  // After the ping-pong: block f_hi's K and V were started at step n - 2
+  // (or before the first step when n = 1; nothing beyond); the masked blocks
+  // continue with one block of look-ahead.
+  for (; t < t_hi; ++t) masked_block(t);
+
+  if (qi < n_q) {
+    __bf16* dqp = static_cast<__bf16*>(a.dq) + ((size_t)bh * n_q + qi) * D;
+#pragma unroll
+    for (int db = 0; db < C::kDB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        bf16x4 r;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r[e] = (__bf16)(dq[db][4 * g4 + e] * a.scale);
+        *reinterpret_cast<bf16x4*>(dqp + 32 * db + 8 * g4 + 4 * hi) = r;
+      }
+  }
+}
+
 // ------------------------------------------------------ fp32 stages 2, 3
 //
 // Same dataflow on the 32x32x2 f32 matrix cores: operands are single floats
@@ -1091,6 +1370,17 @@ hipError_t dkdv_bf16_t(const BwdArgs& a, hipStream_t s) {
   }
 }
 
+template <int D, bool CAUSAL>
+hipError_t dq_bf16_pp(const BwdArgs& a, hipStream_t s) {
+  using C = DqCfg<D, 8>;
+  const int n_qtiles = (a.n_q + C::kBM - 1) / C::kBM;
+  BwdArgs args = a;
+  int nt = n_qtiles;
+  void* params[] = {&args, &nt};
+  return launch_raw(reinterpret_cast<const void*>(bwd_dq_bf16_pp_kernel<D, CAUSAL>), n_qtiles * a.BH,
+                    C::kThreads, params, s);
+}
+
 template <int D, bool CAUSAL, int WAVES>
 hipError_t dq_bf16_w(const BwdArgs& a, hipStream_t s) {
   using C = DqCfg<D, WAVES>;
@@ -1119,7 +1409,11 @@ hipError_t dq_bf16_t(const BwdArgs& a, hipStream_t s) {
   const long long wide_wgs = (long long)a.BH * ((a.n_q + DqCfg<D, 8>::kBM - 1) / DqCfg<D, 8>::kBM);
   const bool narrow = a.n_q <= kDqShortRows || a.window >= 0 ||
                       (CAUSAL ? wide_wgs < kDqCausalBalanceWgs : wide_wgs <= kDqIdleHalfWgs);
-  return narrow ? dq_bf16_w<D, CAUSAL, 4>(a, s) : dq_bf16_w<D, CAUSAL, 8>(a, s);
+  if (narrow) return dq_bf16_w<D, CAUSAL, 4>(a, s);
+  // 256-row workgroups at d = 128 take the ping-pong kernel; at d <= 64 the
+  // 8-wave kernel is kept.
+  if constexpr (D == 128) return dq_bf16_pp<D, CAUSAL>(a, s);
+  else return dq_bf16_w<D, CAUSAL, 8>(a, s);
 }
 
 template <int D, bool CAUSAL>

@@ -182,6 +182,14 @@ __device__ __forceinline__ void fence_results(f32x16& x, f32x16& y) {
   asm volatile("s_nop 11" : "+v"(x), "+v"(y));
 }
 
+// An index given either as a compile-time constant (std::integral_constant)
+// or as a run-time int.
+template <typename X>
+__device__ __forceinline__ constexpr int value_of(X x) {
+  if constexpr (std::is_integral_v<X>) return x;
+  else return X::value;
+}
+
 // Calls f(std::integral_constant<int, I>{}) for I = BEGIN .. END-1, so that
 // the index is a compile-time constant in the body.
 template <int BEGIN, int END, typename F>

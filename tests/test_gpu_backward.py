@@ -72,6 +72,22 @@ def test_dkdv_workgroup_widths_agree_bitwise(dev):
                    q[0, h], k[0, h], v[0, h], do[0, h], scale, False, 2e-2)
 
 
+@pytest.mark.parametrize("B,H,n,causal", [(1, 32, 1100, False), (2, 32, 2100, True), (1, 40, 4000, False)])
+def test_dq_two_wave_ping_pong_shapes(dev, B, H, n, causal):
+    """Shapes whose dQ stage takes the d = 128 ping-pong kernel (256-row
+    workgroups, more than 1024 rows, enough workgroups), with ragged row and
+    key counts (a masked key-tail block after the ping-pong, a ragged last
+    query tile) and, causal, the diagonal blocks after it.  The first, a
+    middle and the last (b, h) unit against the oracle."""
+    d = 128
+    q, k, v, do = workloads.random_qkv(6100 + n + H, B, H, n, n, d, torch.bfloat16, with_do=True)
+    scale = 1 / math.sqrt(d)
+    _, _, dq, dk, dv = gpu_fwd_bwd(dev, q, k, v, do, scale, causal)
+    for b, h in ((0, 0), (B - 1, H // 2), (B - 1, H - 1)):
+        check_unit(f"B{B} H{H} n{n} causal={causal} unit ({b},{h})", (dq[b, h], dk[b, h], dv[b, h]),
+                   q[b, h], k[b, h], v[b, h], do[b, h], scale, causal, 2e-2)
+
+
 SHAPES = [(1, 1, 1, 1), (1, 2, 17, 17), (2, 1, 63, 65), (1, 1, 65, 63), (1, 2, 129, 129),
           (1, 1, 257, 300), (1, 1, 300, 257), (1, 1, 5, 600), (1, 1, 600, 5), (1, 1, 1000, 1000)]
 
