@@ -534,6 +534,44 @@ def run_configs(args, torch, fa, workloads, dev):
     del q, k, v, do, o, lse, ws, dq, dk, dv
     torch.cuda.empty_cache()
 
+    # Per visible pair, how masked passes compare with full attention (B=1,
+    # H=32, n=4096, d=128 bf16): forward and whole backward under no mask,
+    # the causal mask, a +-256 window and a causal 512 window.
+    def band_pairs(n, causal, window):
+        tot = 0
+        for i in range(n):
+            lo, hi = 0, n - 1
+            if causal:
+                hi = min(hi, i)
+            if window is not None:
+                lo, hi = max(lo, i - window), min(hi, i + window)
+            tot += max(0, hi - lo + 1)
+        return tot
+
+    wq = workloads.c3(False)
+    q, k, v = (t.to(dev) for t in (wq.q, wq.k, wq.v))
+    do = torch.randn(q.shape, generator=torch.Generator().manual_seed(7)).to(torch.bfloat16).to(dev)
+    B, H, n, d = q.shape
+    ws = fa.backward_workspace(B, H, n, n, d, q.dtype, dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    masks = {}
+    for name, causal, window in (("full", False, None), ("causal", True, None), ("window256", False, 256),
+                                 ("causal_window512", True, 512)):
+        o, lse = fa.forward(q, k, v, causal=causal, window=window)
+        uf = _median_us(torch, lambda: fa.forward(q, k, v, causal=causal, window=window, out=o, lse=lse), 10)
+        ub = _median_us(torch, lambda: fa.backward(q, k, v, o, do, lse, causal=causal, window=window, dq=dq,
+                                                    dk=dk, dv=dv, workspace=ws), 10)
+        pairs = B * H * band_pairs(n, causal, window)
+        masks[name] = {"fwd_us": round(uf, 1), "bwd_us": round(ub, 1), "pairs": pairs,
+                       "fwd_tflops": round(4 * d * pairs / (uf * 1e-6) / 1e12, 1),
+                       "bwd_tflops": round(10 * d * pairs / (ub * 1e-6) / 1e12, 1)}
+    for name in masks:
+        masks[name]["fwd_rate_vs_full"] = round(masks[name]["fwd_tflops"] / masks["full"]["fwd_tflops"], 3)
+        masks[name]["bwd_rate_vs_full"] = round(masks[name]["bwd_tflops"] / masks["full"]["bwd_tflops"], 3)
+    res["masks_b1h32n4096d128"] = masks
+    del q, k, v, do, ws, dq, dk, dv, o, lse
+    torch.cuda.empty_cache()
+
     # LSE merge of 8 bf16 parts of the c3 shape (the results of 8 key chunks,
     # as a sequence-sharded step combines them): HBM-bound, algorithmic bytes
     # = the parts (o and lse) read once and the result written once; 302 MB
