@@ -84,6 +84,40 @@ SHAPES = [
 ]
 
 
+@pytest.mark.parametrize("B,H,n", [(1, 40, 4096), (1, 33, 2100), (2, 36, 1100)])
+def test_workgroups_walking_several_tiles(dev, B, H, n):
+    """d = 128 bf16 without the mask and with more 256-row tiles than compute
+    units: each workgroup walks tiles w, w + grid, ..., loading the next
+    tile while it writes the current one, some workgroups one tile more
+    than others (640, 297 and 360 tiles on 256 compute units; ragged row
+    counts).  Every head is computed by some workgroup's first, second or
+    third tile: the first, a middle and the last head against the oracle,
+    and every head bitwise equal to calls on slices of heads small enough
+    for one tile per workgroup on the same kernel (more than 128 and at most
+    256 tiles)."""
+    d = 128
+    q, k, v = workloads.random_qkv(7300 + n + H, B, H, n, n, d, torch.bfloat16)
+    scale = 1 / math.sqrt(d)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    o, lse = fa.forward(qd, kd, vd, scale=scale)
+    torch.cuda.synchronize()
+    for b, h in ((0, 0), (B - 1, H // 2), (B - 1, H - 1)):
+        ro, rl = oracle.attention_fwd(np64(q[b, h]), np64(k[b, h]), np64(v[b, h]), scale, False)
+        assert_close(f"O B{B} H{H} n{n} ({b},{h})", o[b, h].cpu(), ro, tol_for(torch.bfloat16))
+        assert_close(f"LSE B{B} H{H} n{n} ({b},{h})", lse[b, h].cpu(), rl, TOL_LSE)
+    tiles = -(-n // 256)
+    per = 256 // tiles  # heads per slice: 129..256 tiles
+    assert 128 < per * tiles <= 256
+    for b in range(B):
+        for h0 in range(0, H, per):
+            h1 = min(H, h0 + per)
+            if (h1 - h0) * tiles <= 128:
+                h0 = max(0, h1 - per)
+            o1, l1 = fa.forward(qd[b:b + 1, h0:h1].contiguous(), kd[b:b + 1, h0:h1].contiguous(),
+                                vd[b:b + 1, h0:h1].contiguous(), scale=scale)
+            assert torch.equal(o1[0], o[b, h0:h1]) and torch.equal(l1[0], lse[b, h0:h1]), f"heads {b},{h0}:{h1}"
+
+
 @pytest.mark.parametrize("d", [32, 64, 128])
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 @pytest.mark.parametrize("causal", [False, True])
