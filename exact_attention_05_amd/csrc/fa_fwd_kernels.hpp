@@ -1069,6 +1069,194 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdArgs a, int n_qtiles) {
   }
 }
 
+// Key-split float32 forward, for shapes whose query rows are too few to fill
+// the GPU with 128-row workgroups but which have many keys (one head of a few
+// thousand rows).  The four waves of a workgroup share one 32-row block and
+// take its 32-key steps w, w + 4, w + 8, ...: each through its own LDS tile
+// and with no workgroup barrier in the loop (the next step's rows load into
+// registers while the current one is used), with the products and the
+// online softmax of fwd_f32_kernel.  At the end the waves' partial results
+// over their key subsets merge through LDS exactly as the online softmax
+// merges blocks ("Attention Mechanism: Revolusi Representasi Sequence",
+// section 13): weights exp2(m_w - max_w m_w) on each wave's O and l.
+template <int D>
+struct F32SplitCfg {
+  static constexpr int kWaves = 4;
+  static constexpr int kThreads = kWaves * 64;
+  static constexpr int kBN = 32;                       // keys per wave step
+  static constexpr int kDB = D / 32;
+  static constexpr int kKStride = D + 2;               // floats (as fwd_f32_kernel)
+  static constexpr int kVStride = D + 8;
+  static constexpr int kChunks = D / 4;                // 16-byte chunks per row
+  static constexpr int kLoads = kBN * kChunks / 64;    // per lane, one wave loading a step
+  static constexpr int kTile = kBN * (kKStride + kVStride);  // floats per wave
+  static constexpr int kOPitch = D + 1;                // merge rows (conflict-free columns)
+  static constexpr int kMerge = kWaves * 32 * kOPitch + 2 * kWaves * 32;
+  static constexpr int kSmem = kWaves * kTile > kMerge ? kWaves * kTile : kMerge;
+  static constexpr int kColsPerThread = D * 32 / kThreads;  // merge: 8 threads per row
+  static_assert(kLoads * 64 == kBN * kChunks, "step load split");
+  static_assert(kColsPerThread * kThreads == D * 32, "merge split");
+};
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256) void fwd_f32_split_kernel(FwdArgs a, int n_rb) {
+  using C = F32SplitCfg<D>;
+  __shared__ __attribute__((aligned(16))) float smem[C::kSmem];
+
+  const int work = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = work / n_rb;
+  const int q0 = (work - bh * n_rb) * 32;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+  const int n_q = a.n_q, n_k = a.n_k;
+  float* const sk = smem + wave * C::kTile;
+  float* const sv = sk + C::kBN * C::kKStride;
+
+  const float* qp = static_cast<const float*>(a.q) + (size_t)bh * n_q * D;
+  const int kvh = kv_head_index(bh, a.H, a.group);
+  const float* kp = static_cast<const float*>(a.k) + (size_t)kvh * n_k * D;
+  const float* vp = static_cast<const float*>(a.v) + (size_t)kvh * n_k * D;
+
+  const int qi = q0 + l32;
+  float qf[D / 2];
+#pragma unroll
+  for (int c = 0; c < D / 2; ++c) qf[c] = (qi < n_q) ? qp[(size_t)qi * D + 2 * c + hi] : 0.f;
+
+  const Band band = band_of(a, CAUSAL);
+  const int q_end = min(n_q, q0 + 32);
+  const int t_lo = band.key_lo(q0) / C::kBN;
+  const int t_hi = max(t_lo, (band.key_hi(q_end) + C::kBN - 1) / C::kBN);
+  int vlo, vspan;  // keys this lane's query sees: [vlo, vlo + vspan]
+  band.key_range(qi, vlo, vspan);
+  const int wfull_lo = band.key_full_lo(q0 + 32), wfull_hi = band.key_full_hi(q0);
+
+  f32x4 kst[C::kLoads], vst[C::kLoads];
+  auto gload = [&](int t) {
+#pragma unroll
+    for (int i = 0; i < C::kLoads; ++i) {
+      const int idx = lane + i * 64;
+      const int row = idx / C::kChunks;
+      const int ch = idx - row * C::kChunks;
+      const int key = t * C::kBN + row;
+      if (key < n_k) {
+        kst[i] = *reinterpret_cast<const f32x4*>(kp + (size_t)key * D + ch * 4);
+        vst[i] = *reinterpret_cast<const f32x4*>(vp + (size_t)key * D + ch * 4);
+      } else {
+        kst[i] = f32x4{};
+        vst[i] = f32x4{};
+      }
+    }
+  };
+  // The wave's own tile: its LDS accesses run in program order, so the
+  // previous step's reads are done before these writes land.
+  auto swrite = [&]() {
+#pragma unroll
+    for (int i = 0; i < C::kLoads; ++i) {
+      const int idx = lane + i * 64;
+      const int row = idx / C::kChunks;
+      const int ch = idx - row * C::kChunks;
+      float* kd = &sk[row * C::kKStride + ch * 4];
+      kd[0] = kst[i][0]; kd[1] = kst[i][1]; kd[2] = kst[i][2]; kd[3] = kst[i][3];
+      *reinterpret_cast<f32x4*>(&sv[row * C::kVStride + ch * 4]) = vst[i];
+    }
+  };
+
+  f32x16 oacc[C::kDB];
+#pragma unroll
+  for (int db = 0; db < C::kDB; ++db) oacc[db] = f32x16{};
+  float m = -INFINITY, l = 0.f;
+
+  int t = t_lo + wave;
+  if (t < t_hi) gload(t);
+  for (; t < t_hi; t += C::kWaves) {
+    swrite();
+    if (t + C::kWaves < t_hi) gload(t + C::kWaves);
+    const int k0 = t * C::kBN;
+
+    f32x16 s[1];
+    s[0] = f32x16{};
+#pragma unroll
+    for (int c = 0; c < D / 2; ++c) s[0] = mfma_f32(sk[l32 * C::kKStride + 2 * c + hi], qf[c], s[0]);
+
+    const bool need_mask = k0 < wfull_lo || k0 + C::kBN > wfull_hi;
+    float alpha;
+    if (need_mask) {
+      uint32_t bits = 0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const bool h = !Band::in_range(k0 + 4 * hi - vlo + 8 * (i >> 2) + (i & 3), 0, vspan);
+        bits |= (h ? 1u : 0u) << i;
+      }
+      alpha = softmax_block<1, true>(s, m, l, a.scale_log2, &bits);
+    } else {
+      alpha = softmax_block<1, false>(s, m, l, a.scale_log2, nullptr);
+    }
+#pragma unroll
+    for (int db = 0; db < C::kDB; ++db) oacc[db] *= alpha;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int key = 8 * (i >> 2) + 4 * hi + (i & 3);
+#pragma unroll
+      for (int db = 0; db < C::kDB; ++db)
+        oacc[db] = mfma_f32(sv[key * C::kVStride + 32 * db + l32], s[0][i], oacc[db]);
+    }
+    settle_acc(oacc);
+  }
+
+  // Merge: each wave's O (rows = queries), m and l; then 8 threads per row
+  // combine the waves.  A wave with no step has m = -inf, l = 0, O = 0.
+  __syncthreads();
+  float* const mo = smem;
+  float* const mm = smem + C::kWaves * 32 * C::kOPitch;
+  float* const ml = mm + C::kWaves * 32;
+  const float lt = sum_halves(l);
+#pragma unroll
+  for (int db = 0; db < C::kDB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      mo[(wave * 32 + l32) * C::kOPitch + 32 * db + 8 * (i >> 2) + 4 * hi + (i & 3)] = oacc[db][i];
+  if (hi == 0) {
+    mm[wave * 32 + l32] = m;
+    ml[wave * 32 + l32] = lt;
+  }
+  __syncthreads();
+  const int r = tid / (C::kThreads / 32);
+  const int col0 = (tid % (C::kThreads / 32)) * C::kColsPerThread;
+  float mx = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < C::kWaves; ++w) mx = fmaxf(mx, mm[w * 32 + r]);
+  float wgt[C::kWaves];
+  float lsum = 0.f;
+#pragma unroll
+  for (int w = 0; w < C::kWaves; ++w) {
+    const float mw = mm[w * 32 + r];
+    wgt[w] = mw == -INFINITY ? 0.f : fast_exp2(mw - mx);
+    lsum += wgt[w] * ml[w * 32 + r];
+  }
+  const int row = q0 + r;
+  if (row < n_q) {
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+    float* op = static_cast<float*>(a.o) + ((size_t)bh * n_q + row) * D + col0;
+#pragma unroll
+    for (int c4 = 0; c4 < C::kColsPerThread; c4 += 4) {
+      f32x4 res;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float acc = 0.f;
+#pragma unroll
+        for (int w = 0; w < C::kWaves; ++w) acc = fmaf(wgt[w], mo[(w * 32 + r) * C::kOPitch + col0 + c4 + e], acc);
+        res[e] = acc * inv;
+      }
+      *reinterpret_cast<f32x4*>(op + c4) = res;
+    }
+    if (col0 == 0) a.lse[(size_t)bh * n_q + row] = lsum > 0.f ? (mx + fast_log2(lsum)) * kLn2 : -INFINITY;
+  }
+}
+
 template <typename Kernel>
 hipError_t launch(Kernel kernel, int grid, int block, const FwdArgs& a, int n_qtiles,
                   hipStream_t stream) {
@@ -1135,6 +1323,12 @@ hipError_t fwd_bf16_t(const FwdArgs& a, hipStream_t stream) {
   // keeps the plain 8-wave kernel.
   if constexpr (D == 128) return fwd_bf16_pp<D, CAUSAL, MERGE>(a, stream);
   else return fwd_bf16_w<D, CAUSAL, 8, MERGE>(a, stream);
+}
+
+template <int D, bool CAUSAL>
+hipError_t fwd_f32_split_t(const FwdArgs& a, hipStream_t stream) {
+  const int n_rb = (a.n_q + 31) / 32;
+  return launch(fwd_f32_split_kernel<D, CAUSAL>, n_rb * a.BH, F32SplitCfg<D>::kThreads, a, n_rb, stream);
 }
 
 template <int D, bool CAUSAL, bool MERGE>

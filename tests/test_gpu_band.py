@@ -122,9 +122,10 @@ def test_sliding_window_workload_size(dev):
         assert_close(f"LSE head {h}", lse[0, h], rl, TOL_LSE)
 
 
-# Few query tiles but many keys: fa_forward_ext runs these on the split-key
-# kernel (one chunk, keys spread over the waves of a workgroup and merged in
-# LDS) instead of the forward kernel; the backward is unchanged.
+# Few query tiles but many keys: the forward runs these on a split-key
+# kernel (keys spread over the waves of a workgroup and merged in LDS):
+# bf16 on the decoding kernel with one chunk, float32 on the key-split
+# float32 kernel; the backward is unchanged.
 STARVED = [  # B, H, H_kv, n_q, n_k, causal, q_offset, window, d
     (1, 1, 1, 2048, 2048, True, 0, -1, 128),
     (1, 2, 2, 1000, 3000, False, 500, 300, 64),
@@ -134,10 +135,11 @@ STARVED = [  # B, H, H_kv, n_q, n_k, causal, q_offset, window, d
 ]
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
 @pytest.mark.parametrize("case", STARVED, ids=lambda c: "B{}H{}kv{}_{}x{}_c{}_off{}_w{}_d{}".format(*c))
-def test_starved_shapes_parity(dev, case):
+def test_starved_shapes_parity(dev, case, dtype):
     B, H, h_kv, n_q, n_k, causal, off, w, d = case
-    q, k, v, do = draw(4700 + n_q + n_k + d, B, H, h_kv, n_q, n_k, d, torch.bfloat16)
+    q, k, v, do = draw(4700 + n_q + n_k + d, B, H, h_kv, n_q, n_k, d, dtype)
     scale = 1 / math.sqrt(d)
     got = run(dev, q, k, v, do, scale, causal, off, w)
-    check(f"{case}", got, q, k, v, do, scale, causal, off, w, torch.bfloat16)
+    check(f"{case}", got, q, k, v, do, scale, causal, off, w, dtype)
