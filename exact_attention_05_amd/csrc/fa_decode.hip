@@ -17,8 +17,9 @@
 // ----------------------
 // The group * n_q query rows that share one K/V head (section 12, grouped
 // K/V heads) are packed into 32-row blocks, so each K/V step is read once for
-// the whole group.  A workgroup is 4 waves and owns one (batch, K/V head,
-// row block, chunk); wave w takes the chunk's 32-key steps w, w+4, w+8, ...
+// the whole group.  A workgroup is W waves (4, or 8 for small grids at
+// d <= 64) and owns one (batch, K/V head, row block, chunk); wave w takes the
+// chunk's 32-key steps w, w+W, w+2W, ...
 // and runs on its own, without workgroup barriers: the K and V rows of its
 // next step load into registers while the current step, already written to
 // the wave's own swizzled LDS tiles, is used with the forward pass's scheme
@@ -26,7 +27,7 @@
 // against 98 us at one on the 32K-context workload): S^T = K Q^T
 // on the 32x32x16 bf16 matrix cores (Q in registers), an online softmax per
 // query column, O^T += V^T P^T with V^T from the transposing LDS read.  At
-// the end the four waves' (m, l, O) are merged through LDS: the same
+// the end the waves' (m, l, O) are merged through LDS: the same
 // rescaling, by exp2(m_w - max_w m_w).
 //
 // Merge kernel
@@ -42,9 +43,9 @@
 namespace fa {
 namespace {
 
-template <int D>
+template <int D, int W>
 struct DecCfg {
-  static constexpr int kWaves = 4;
+  static constexpr int kWaves = W;
   static constexpr int kThreads = kWaves * 64;
   static constexpr int kSub = 32;              // keys per wave step
   static constexpr int kDepth = 1;             // steps loading while one is computed
@@ -60,9 +61,9 @@ struct DecCfg {
                                         ? kWaves * 2 * T::kBytes : kScratchFloats * 4;
 };
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void decode_bf16_kernel(DecArgs a) {
-  using C = DecCfg<D>;
+template <int D, bool CAUSAL, int W>
+__global__ __launch_bounds__(W * 64) void decode_bf16_kernel(DecArgs a) {
+  using C = DecCfg<D, W>;
   using T = typename C::T;
   // Per wave: its K step then its V step; reused for the merge at the end.
   __shared__ __attribute__((aligned(1024))) char smem[C::kSmemBytes];
@@ -257,6 +258,7 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecArgs a) {
   __syncthreads();
 
   // Thread (q = tid % 32, columns d0 .. d0 + kPer - 1) of packed row q.
+  if (tid >= 256) return;  // the output: 8 threads per row, D / 8 columns each
   const int q = tid & 31;
   const int d0 = (tid >> 5) * C::kPer;
   float mq = -INFINITY;
@@ -396,13 +398,29 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(MergeArgs a) {
   if (c == 0) a.lse[row] = s > 0.f ? ref + fast_log2(s) * kLn2 : -INFINITY;
 }
 
-template <int D, bool CAUSAL>
-hipError_t decode_t(const DecArgs& a, hipStream_t stream) {
+template <int D, bool CAUSAL, int W>
+hipError_t decode_w(const DecArgs& a, int grid, hipStream_t stream) {
   DecArgs args = a;
   void* params[] = {&args};
+  return hipLaunchKernel(reinterpret_cast<const void*>(decode_bf16_kernel<D, CAUSAL, W>), dim3(grid),
+                         dim3(DecCfg<D, W>::kThreads), params, 0, stream);
+}
+
+// Eight waves per workgroup (two per SIMD, each taking every eighth key step)
+// when the grid has at most one workgroup per compute unit and d <= 64 (at
+// d = 128 eight waves would spill): one wave per SIMD runs each step's
+// dependent chain alone, a second one overlaps it.  Measured on MI355X (bf16
+// forward, one chunk): B=1 H=1 n=4096 d=64 33.1 -> 23.7 us, d=32 25.2 -> 17.6
+// us, H=2 2048 x 8192 keys 61.6 -> 42.2 us; with 512 workgroups (H=4
+// n=4096) 43.3 -> 46.5 us, where four waves stay.
+template <int D, bool CAUSAL>
+hipError_t decode_t(const DecArgs& a, hipStream_t stream) {
   const int grid = a.B * a.h_kv * a.n_splits * a.n_rb;
-  return hipLaunchKernel(reinterpret_cast<const void*>(decode_bf16_kernel<D, CAUSAL>), dim3(grid),
-                         dim3(DecCfg<D>::kThreads), params, 0, stream);
+  if constexpr (D <= 64) {
+    const int cus = compute_units(stream);
+    if (cus > 0 && grid <= cus) return decode_w<D, CAUSAL, 8>(a, grid, stream);
+  }
+  return decode_w<D, CAUSAL, 4>(a, grid, stream);
 }
 
 template <int D, typename TI, typename TO>
