@@ -239,6 +239,16 @@ bool starved_f32(int B, int H, int n_q) {
   const long long tiles = (long long)B * H * ((n_q + 127) / 128);
   return tiles <= kStarvedTilesF32;
 }
+// Among those, shapes whose 32-row blocks would fill at most half of the 256
+// compute units take 16-row blocks (16x16x4 products: twice the LDS reads per
+// product, so only where the blocks are that few).  Measured on MI355X: c2
+// 100.2 -> 78.1 us, d = 128 194.5 -> 147.0 us, B=1 H=4 1024 x 8192 keys
+// d = 128 377.3 -> 285.8 us; at 256 blocks of 32 (H=2, n=4096, d=64)
+// 102.0 -> 114.1 us, where 32-row blocks stay.
+constexpr long long kStarvedBlocks16 = 128;
+bool starved_f32_16(int B, int H, int n_q) {
+  return (long long)B * H * ((n_q + 31) / 32) <= kStarvedBlocks16;
+}
 
 int forward_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                  int H_kv, int n_q, int n_k, int d, float scale, int causal, int dtype,
@@ -254,7 +264,8 @@ int forward_impl(const void* q, const void* k, const void* v, void* o, float* ls
   fa::FwdArgs a = make_fwd(q, k, v, o, lse, B, H, H_kv, n_q, n_k, scale, q_offset, window);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (dtype == FA_DTYPE_FP32 && starved_f32(B, H, n_q))
-    return status_of(fa::launch_fwd_f32_split(a, d, causal != 0, s));
+    return status_of(starved_f32_16(B, H, n_q) ? fa::launch_fwd_f32_split16(a, d, causal != 0, s)
+                                               : fa::launch_fwd_f32_split(a, d, causal != 0, s));
   return status_of(dtype == FA_DTYPE_BF16 ? fa::launch_fwd_bf16(a, d, causal != 0, s)
                                           : fa::launch_fwd_f32(a, d, causal != 0, s));
 }

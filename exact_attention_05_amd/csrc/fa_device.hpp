@@ -13,6 +13,10 @@
 //    A: lane l holds row (l % 32), k = l / 32;  B: col (l % 32), k = l / 32
 //    C: as above.
 //
+//  v_mfma_f32_16x16x4_f32    C[16x16] += A[16x4] * B[4x16]
+//    A: lane l holds row (l % 16), k = l / 16;  B: col (l % 16), k = l / 16
+//    C: lane l, element i holds row 4*(l/16) + i, col (l % 16)
+//
 //  ds_read_b64_tr_b16: within each group of 16 lanes, lane 4r+j supplies the
 //    address of 4 consecutive 16-bit values = row r, columns 4j..4j+3 of a
 //    4 x 16 tile; lane i of the group receives column i (rows 0..3).
@@ -40,6 +44,10 @@ __device__ __forceinline__ f32x16 mfma_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
 
 __device__ __forceinline__ f32x16 mfma_f32(float a, float b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma_f32_16(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
 // `p` must point into LDS (a __shared__ array); it is converted to the LDS

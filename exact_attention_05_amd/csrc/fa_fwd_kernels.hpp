@@ -1257,6 +1257,206 @@ __global__ __launch_bounds__(256) void fwd_f32_split_kernel(FwdArgs a, int n_rb)
   }
 }
 
+// The same with 16-row blocks on the 16x16x4 float32 products, for shapes
+// whose 32-row blocks still leave compute units idle (one head of 4096 rows:
+// 128 blocks of 32 for 256 compute units).  S^T = K Q^T per 16 keys: lane l
+// holds keys 4(l/16) + i, i = 0..3, of query l % 16.  In O^T += V^T P^T the
+// key dimension of product i is laid out so that lane group g = l / 16
+// contracts key 4g + i: the lane's own probability i is then its B operand,
+// and V is read at that key.  Rows of the LDS tiles are D + 4 floats apart,
+// so that the four lane groups' reads fall into different banks.
+template <int D>
+struct F32Split16Cfg {
+  static constexpr int kWaves = 4;
+  static constexpr int kThreads = kWaves * 64;
+  static constexpr int kBN = 32;                       // keys per wave step (two 16-key sub-blocks)
+  static constexpr int kDB = D / 16;                   // 16-row blocks of O^T
+  static constexpr int kPitch = D + 4;                 // floats per K or V row in LDS
+  static constexpr int kChunks = D / 4;
+  static constexpr int kLoads = kBN * kChunks / 64;
+  static constexpr int kTile = 2 * kBN * kPitch;       // K then V, floats per wave
+  static constexpr int kOPitch = D + 1;
+  static constexpr int kMerge = kWaves * 16 * kOPitch + 2 * kWaves * 16;
+  static constexpr int kSmem = kWaves * kTile > kMerge ? kWaves * kTile : kMerge;
+  static constexpr int kColsPerThread = D / 16;        // merge: 16 threads per row
+  static_assert(kLoads * 64 == kBN * kChunks, "step load split");
+};
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256) void fwd_f32_split16_kernel(FwdArgs a, int n_rb) {
+  using C = F32Split16Cfg<D>;
+  __shared__ __attribute__((aligned(16))) float smem[C::kSmem];
+
+  const int work = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = work / n_rb;
+  const int q0 = (work - bh * n_rb) * 16;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int l16 = lane & 15;
+  const int g = lane >> 4;
+  const int n_q = a.n_q, n_k = a.n_k;
+  float* const sk = smem + wave * C::kTile;
+  float* const sv = sk + C::kBN * C::kPitch;
+
+  const float* qp = static_cast<const float*>(a.q) + (size_t)bh * n_q * D;
+  const int kvh = kv_head_index(bh, a.H, a.group);
+  const float* kp = static_cast<const float*>(a.k) + (size_t)kvh * n_k * D;
+  const float* vp = static_cast<const float*>(a.v) + (size_t)kvh * n_k * D;
+
+  const int qi = q0 + l16;
+  float qf[D / 4];
+#pragma unroll
+  for (int c = 0; c < D / 4; ++c) qf[c] = (qi < n_q) ? qp[(size_t)qi * D + 4 * c + g] : 0.f;
+
+  const Band band = band_of(a, CAUSAL);
+  const int q_end = min(n_q, q0 + 16);
+  const int t_lo = band.key_lo(q0) / C::kBN;
+  const int t_hi = max(t_lo, (band.key_hi(q_end) + C::kBN - 1) / C::kBN);
+  int vlo, vspan;  // keys this lane's query sees: [vlo, vlo + vspan]
+  band.key_range(qi, vlo, vspan);
+  const int wfull_lo = band.key_full_lo(q0 + 16), wfull_hi = band.key_full_hi(q0);
+  const float sl2 = a.scale_log2;
+
+  f32x4 kst[C::kLoads], vst[C::kLoads];
+  auto gload = [&](int t) {
+#pragma unroll
+    for (int i = 0; i < C::kLoads; ++i) {
+      const int idx = lane + i * 64;
+      const int row = idx / C::kChunks;
+      const int ch = idx - row * C::kChunks;
+      const int key = t * C::kBN + row;
+      if (key < n_k) {
+        kst[i] = *reinterpret_cast<const f32x4*>(kp + (size_t)key * D + ch * 4);
+        vst[i] = *reinterpret_cast<const f32x4*>(vp + (size_t)key * D + ch * 4);
+      } else {
+        kst[i] = f32x4{};
+        vst[i] = f32x4{};
+      }
+    }
+  };
+  // The wave's own tile: its LDS accesses run in program order.
+  auto swrite = [&]() {
+#pragma unroll
+    for (int i = 0; i < C::kLoads; ++i) {
+      const int idx = lane + i * 64;
+      const int row = idx / C::kChunks;
+      const int ch = idx - row * C::kChunks;
+      *reinterpret_cast<f32x4*>(&sk[row * C::kPitch + ch * 4]) = kst[i];
+      *reinterpret_cast<f32x4*>(&sv[row * C::kPitch + ch * 4]) = vst[i];
+    }
+  };
+
+  f32x4 oacc[C::kDB];
+#pragma unroll
+  for (int db = 0; db < C::kDB; ++db) oacc[db] = f32x4{};
+  float m = -INFINITY, l = 0.f;  // running maximum (log2 units) and this lane's partial sum
+
+  int t = t_lo + wave;
+  if (t < t_hi) gload(t);
+  for (; t < t_hi; t += C::kWaves) {
+    swrite();
+    if (t + C::kWaves < t_hi) gload(t + C::kWaves);
+    const int k0 = t * C::kBN;
+
+    f32x4 s[2];
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+      s[sb] = f32x4{};
+#pragma unroll
+      for (int c = 0; c < D / 4; ++c) s[sb] = mfma_f32_16(sk[(16 * sb + l16) * C::kPitch + 4 * c + g], qf[c], s[sb]);
+    }
+    const bool need_mask = k0 < wfull_lo || k0 + C::kBN > wfull_hi;
+    if (need_mask) {
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (!Band::in_range(k0 + 16 * sb + 4 * g + i - vlo, 0, vspan)) s[sb][i] = -INFINITY;
+    }
+    // Online softmax over the step's 32 keys: the lane's 8 values, then the
+    // four lane groups of the query.
+    float mx = -INFINITY;
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[sb][i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mt = (mx == -INFINITY) ? -INFINITY : mx * sl2;
+    const float m_new = fmaxf(m, mt);
+    const float ref = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = fast_exp2(m - ref);
+    float p[2][4];
+    float rs = 0.f;
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float pv = fast_exp2(fmaf(s[sb][i], sl2, -ref));
+        if (need_mask && s[sb][i] == -INFINITY) pv = 0.f;
+        p[sb][i] = pv;
+        rs += pv;
+      }
+    l = alpha * l + rs;
+    m = m_new;
+#pragma unroll
+    for (int db = 0; db < C::kDB; ++db) oacc[db] *= alpha;
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int db = 0; db < C::kDB; ++db)
+          oacc[db] = mfma_f32_16(sv[(16 * sb + 4 * g + i) * C::kPitch + 16 * db + l16], p[sb][i], oacc[db]);
+  }
+
+  // Merge: each wave's O (rows = queries), m and l (summed over the four
+  // lane groups); then 16 threads per row combine the waves.
+  __syncthreads();
+  float* const mo = smem;
+  float* const mm = smem + C::kWaves * 16 * C::kOPitch;
+  float* const ml = mm + C::kWaves * 16;
+  float lt = l + __shfl_xor(l, 16);
+  lt += __shfl_xor(lt, 32);
+#pragma unroll
+  for (int db = 0; db < C::kDB; ++db)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) mo[(wave * 16 + l16) * C::kOPitch + 16 * db + 4 * g + j] = oacc[db][j];
+  if (g == 0) {
+    mm[wave * 16 + l16] = m;
+    ml[wave * 16 + l16] = lt;
+  }
+  __syncthreads();
+  const int r = tid / 16;
+  const int col0 = (tid % 16) * C::kColsPerThread;
+  float mq = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < C::kWaves; ++w) mq = fmaxf(mq, mm[w * 16 + r]);
+  float wgt[C::kWaves];
+  float lsum = 0.f;
+#pragma unroll
+  for (int w = 0; w < C::kWaves; ++w) {
+    const float mw = mm[w * 16 + r];
+    wgt[w] = mw == -INFINITY ? 0.f : fast_exp2(mw - mq);
+    lsum += wgt[w] * ml[w * 16 + r];
+  }
+  const int row = q0 + r;
+  if (row < n_q) {
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+    float* op = static_cast<float*>(a.o) + ((size_t)bh * n_q + row) * D + col0;
+#pragma unroll
+    for (int c = 0; c < C::kColsPerThread; ++c) {
+      float acc = 0.f;
+#pragma unroll
+      for (int w = 0; w < C::kWaves; ++w) acc = fmaf(wgt[w], mo[(w * 16 + r) * C::kOPitch + col0 + c], acc);
+      op[c] = acc * inv;
+    }
+    if (col0 == 0) a.lse[(size_t)bh * n_q + row] = lsum > 0.f ? (mq + fast_log2(lsum)) * kLn2 : -INFINITY;
+  }
+}
+
 template <typename Kernel>
 hipError_t launch(Kernel kernel, int grid, int block, const FwdArgs& a, int n_qtiles,
                   hipStream_t stream) {
@@ -1329,6 +1529,12 @@ template <int D, bool CAUSAL>
 hipError_t fwd_f32_split_t(const FwdArgs& a, hipStream_t stream) {
   const int n_rb = (a.n_q + 31) / 32;
   return launch(fwd_f32_split_kernel<D, CAUSAL>, n_rb * a.BH, F32SplitCfg<D>::kThreads, a, n_rb, stream);
+}
+
+template <int D, bool CAUSAL>
+hipError_t fwd_f32_split16_t(const FwdArgs& a, hipStream_t stream) {
+  const int n_rb = (a.n_q + 15) / 16;
+  return launch(fwd_f32_split16_kernel<D, CAUSAL>, n_rb * a.BH, F32Split16Cfg<D>::kThreads, a, n_rb, stream);
 }
 
 template <int D, bool CAUSAL, bool MERGE>

@@ -219,6 +219,8 @@ hipError_t launch_fwd_f32(const FwdArgs& a, int d, bool causal, hipStream_t stre
 // Float32 forward with the keys of each 32-row block split over the four
 // waves of a workgroup (for shapes with few query rows and many keys).
 hipError_t launch_fwd_f32_split(const FwdArgs& a, int d, bool causal, hipStream_t stream);
+// The same with 16-row blocks (16x16x4 products), for still fewer rows.
+hipError_t launch_fwd_f32_split16(const FwdArgs& a, int d, bool causal, hipStream_t stream);
 // The same passes with the epilogue merging into a.o_prior, a.lse_prior.
 hipError_t launch_fwd_merge_bf16(const FwdArgs& a, int d, bool causal, hipStream_t stream);
 hipError_t launch_fwd_merge_f32(const FwdArgs& a, int d, bool causal, hipStream_t stream);

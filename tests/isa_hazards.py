@@ -14,7 +14,8 @@ the C operand of the next product) is interlocked and not checked.
 Requirements used: the wait states the compiler itself puts between a
 product and a read of its result in straight-line gfx950 code (s_nop 15 +
 s_nop 1 = 18 for the fp32 32x32x2 product, s_nop 11 = 12 for the bf16
-32x32x16 product, s_nop 7 = 8 for the bf16 16x16x32 product), the same for
+32x32x16 product, s_nop 9 = 10 for the fp32 16x16x4 product, s_nop 7 = 8
+for the bf16 16x16x32 product), the same for
 a vector, store, LDS-write, AGPR-copy or product-operand read.
 
 The reverse direction is checked too: a product that reads an operand (A, B
@@ -31,6 +32,7 @@ from collections import defaultdict
 NEED = {
     "v_mfma_f32_32x32x2_f32": 18,
     "v_mfma_f32_32x32x16_bf16": 12,
+    "v_mfma_f32_16x16x4_f32": 10,
     "v_mfma_f32_16x16x32_bf16": 8,
 }
 DEFAULT_NEED = 18  # unknown products: the longest requirement above
