@@ -135,6 +135,26 @@ STARVED = [  # B, H, H_kv, n_q, n_k, causal, q_offset, window, d
 ]
 
 
+# Float32 shapes with at most 128 tiles of 128 rows but more than 128 blocks
+# of 32: the forward takes the 32-row key-split kernel (the shapes above take
+# the 16-row one).
+F32_SPLIT32 = [  # B, H, H_kv, n_q, n_k, causal, q_offset, window, d
+    (1, 2, 2, 4096, 4096, True, 0, -1, 64),
+    (2, 4, 2, 1000, 1500, False, 300, 200, 128),
+    (1, 8, 8, 600, 2000, False, 0, -1, 32),
+]
+
+
+@pytest.mark.parametrize("case", F32_SPLIT32, ids=lambda c: "B{}H{}kv{}_{}x{}_c{}_off{}_w{}_d{}".format(*c))
+def test_fp32_32_row_key_split_parity(dev, case):
+    B, H, h_kv, n_q, n_k, causal, off, w, d = case
+    assert B * H * -(-n_q // 128) <= 128 < B * H * -(-n_q // 32)
+    q, k, v, do = draw(4900 + n_q + n_k + d, B, H, h_kv, n_q, n_k, d, torch.float32)
+    scale = 1 / math.sqrt(d)
+    got = run(dev, q, k, v, do, scale, causal, off, w)
+    check(f"{case}", got, q, k, v, do, scale, causal, off, w, torch.float32)
+
+
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
 @pytest.mark.parametrize("case", STARVED, ids=lambda c: "B{}H{}kv{}_{}x{}_c{}_off{}_w{}_d{}".format(*c))
 def test_starved_shapes_parity(dev, case, dtype):
