@@ -72,7 +72,7 @@ extern "C" {
 typedef enum fa_status {
   FA_OK = 0,
   FA_ERR_INVALID_ARG = 1,   /* NULL pointer, size < 1, bad causal, non-finite or negative scale */
-  FA_ERR_UNSUPPORTED = 2,   /* head width d or dtype this build does not provide */
+  FA_ERR_UNSUPPORTED = 2,   /* head width d or dtype the library does not provide */
   FA_ERR_WORKSPACE = 3,     /* backward workspace missing or smaller than required */
   FA_ERR_LAUNCH = 4,        /* the HIP runtime refused a kernel launch */
   FA_ERR_ALIGNMENT = 5,     /* a tensor pointer is not aligned as required */

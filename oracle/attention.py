@@ -27,7 +27,7 @@ pages by eye:
   D_i = sum_k dO_ik O_ik, dS = P o (dP - D), dQ = scale dS K,
   dK = scale dS^T Q.
 
-Readings where the pages are silent or garbled (each is listed in the design doc):
+Readings where the pages are silent or garbled:
 
 * the scale is an explicit argument; every workload uses 1/sqrt(d);
 * causal alignment when n_q != n_k is top-left: key j is hidden from query i
