@@ -888,6 +888,10 @@ void bwd_dq_bf16_pp_kernel(BwdArgs a, int n_qtiles) {
       };
       bf16x8 ring[kAhead];
       phase_barrier();
+      // The product phase issues at raised wave priority, so that on each
+      // SIMD its products and operand reads go ahead of the other wave's
+      // vector work (c3 dQ 318.7 -> 315.2 us, bitwise the same results).
+      __builtin_amdgcn_s_setprio(1);
       static_for<J0, (J0 + kAhead < J1 ? J0 + kAhead : J1)>([&](auto j) __attribute__((always_inline)) {
         ring[(decltype(j)::value - J0) % kAhead] = read(j);
       });
@@ -898,6 +902,7 @@ void bwd_dq_bf16_pp_kernel(BwdArgs a, int n_qtiles) {
         if constexpr (J + kAhead < J1) ring[(J - J0) % kAhead] = read(std::integral_constant<int, J + kAhead>{});
         __builtin_amdgcn_sched_barrier(0);  // each product with the read kAhead steps ahead
       });
+      __builtin_amdgcn_s_setprio(0);
     };
     // Phase B: dS = P o (dP - D) of both halves, rounded to bf16 pairs.
     auto phase_b = [&]() __attribute__((always_inline)) {
