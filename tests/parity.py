@@ -42,6 +42,14 @@ def np64(t: torch.Tensor) -> np.ndarray:
 # Every other shape is held to the plain bounds.
 RTOL_BF16_TERMS = 2.0 ** -7
 MANY_ROWS_PER_KEY = 16
+# Under a mask the same regime can hold for single elements of shapes the
+# rule above does not cover: the first keys of a causal window are seen by
+# up to w + 1 rows of each query head of their group, whose early
+# probabilities (and dS) are large.  The band checks therefore give the same
+# allowance to every element whose sum of absolute terms, computed from the
+# oracle, reaches MANY_TERMS_SUM (the "~20 or more" of the rule above), and
+# hold every other element to the plain bound.
+MANY_TERMS_SUM = 20.0
 
 
 def bf16_grad_rtol(dtype: torch.dtype, n_q: int, n_k: int, group: int = 1) -> float:
@@ -74,8 +82,10 @@ def half_ulp_bf16(x) -> np.ndarray:
     return np.where(a > 0, np.exp2(e - 8.0), 0.0)
 
 
-def assert_close(name: str, got, ref, tol: float, rtol: float = 0.0, mag=None, rounded_bf16=None) -> float:
-    """Element-wise |got - ref| <= tol + rtol * mag (mag defaults to |ref|),
+def assert_close(name: str, got, ref, tol: float, rtol: float = 0.0, mag=None, rounded_bf16=None,
+                 rtol_from: float = 0.0) -> float:
+    """Element-wise |got - ref| <= tol + rtol * mag (mag defaults to |ref|;
+    the rtol term only where mag >= rtol_from),
     plus, for a bfloat16 result, the rounding of that result to bfloat16 (half
     an ulp at max(|got|, |ref|)): tol bounds the arithmetic, and the output
     format adds its own rounding on top, which alone passes 2e-2 once
@@ -89,7 +99,7 @@ def assert_close(name: str, got, ref, tol: float, rtol: float = 0.0, mag=None, r
     assert np.all(np.isfinite(got)), f"{name}: non-finite values"
     err = np.abs(got - ref)
     mag = np.abs(ref) if mag is None else np.asarray(mag, dtype=np.float64)
-    bound = tol + rtol * mag
+    bound = tol + np.where(mag >= rtol_from, rtol * mag, 0.0)
     if rounded_bf16:
         bound = bound + half_ulp_bf16(np.maximum(np.abs(got), np.abs(np.where(np.isfinite(ref), ref, 0.0))))
     excess = err - bound
@@ -97,7 +107,8 @@ def assert_close(name: str, got, ref, tol: float, rtol: float = 0.0, mag=None, r
     worst = float(np.max(err))
     msg = (f"{name}: max |err| {worst:.3e}; worst vs bound at {tuple(int(i) for i in idx)} "
            f"(got {got[idx]:.6g}, ref {ref[idx]:.6g}, err {err[idx]:.3e}, bound {float(bound[idx] if np.ndim(bound) else bound):.3e}), "
-           f"tol {tol:.1e} rtol {rtol:.1e}{' +half-ulp bf16' if rounded_bf16 else ''}")
+           f"tol {tol:.1e} rtol {rtol:.1e}{f' where mag >= {rtol_from:g}' if rtol_from else ''}"
+           f"{' +half-ulp bf16' if rounded_bf16 else ''}")
     print(msg)
     assert float(excess[idx]) <= 0.0, msg
     return worst
