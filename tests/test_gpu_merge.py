@@ -177,3 +177,29 @@ def test_ring_attention_backward_by_chunks(dev):
     assert_close("ring dQ", dq.cpu(), rq, 2e-2 + 4 * 2.0 ** -9 * float(np.max(np.abs(rq))))
     assert_close("ring dK", torch.cat(dks, dim=2).cpu(), rk, 2e-2)
     assert_close("ring dV", torch.cat(dvs, dim=2).cpu(), rv, 2e-2)
+
+
+@pytest.mark.parametrize("acc", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("causal", [False, True])
+def test_chained_key_chunks_on_the_wide_kernels(dev, acc, causal):
+    # Shapes large enough for 256-row workgroups (the d = 128 ping-pong
+    # kernel with its merging epilogue, and for the non-causal pass its
+    # persistent tile loop): three chunks, the last ragged, merged in place;
+    # a few heads against the oracle over all keys.
+    B, H, n_q, n_k, d = 2, 48, 1400, 1500, 128
+    cuts = [(0, 640), (640, 1281), (1281, 1500)]
+    off = n_k - n_q if causal else 0
+    q, k, v, _ = draw(5300 + int(causal), B, H, H, n_q, n_k, d, torch.bfloat16)
+    scale = 1 / math.sqrt(d)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    o = torch.full(q.shape, float("nan"), dtype=acc, device=dev)
+    lse = torch.full(q.shape[:3], -math.inf, dtype=torch.float32, device=dev)
+    for a, b in cuts:
+        fa.forward_merge(qd, kd[:, :, a:b].contiguous(), vd[:, :, a:b].contiguous(), o, lse, causal=causal,
+                         scale=scale, q_offset=off - a, out=o, lse=lse)
+    torch.cuda.synchronize()
+    oc, lc = o.cpu(), lse.cpu()
+    for b, h in ((0, 0), (1, 47), (1, 20)):
+        check_band(f"acc {acc} causal={causal} ({b}, {h})", oc[b:b + 1, h:h + 1], lc[b:b + 1, h:h + 1],
+                   q[b:b + 1, h:h + 1], k[b:b + 1, h:h + 1], v[b:b + 1, h:h + 1], scale, causal, off, -1,
+                   tol_for(torch.bfloat16), rounded_bf16=(acc == torch.bfloat16))
