@@ -445,7 +445,7 @@ def _sclk_sampler():
 
 def _sclk_under_load(launch, torch, settle_s=1.5, min_s=1.0, max_s=8.0, want=3):
     """Mean shader clock (MHz) over amd-smi samples taken while `launch()`
-    (a batch of GPU work) runs back to back.  The driver refreshes the value
+    (a batch of GPU work) runs back to back.  The amdgpu kernel module refreshes the value
     about once a second, so samples are only counted after settle_s seconds
     of load, for at least min_s more seconds and until `want` of them are
     in, or max_s seconds of load in all."""
