@@ -26,7 +26,9 @@
 // (deeper register rings measured no faster: 101 us at three steps ahead
 // against 98 us at one on the 32K-context workload): S^T = K Q^T
 // on the 32x32x16 bf16 matrix cores (Q in registers), an online softmax per
-// query column, O^T += V^T P^T with V^T from the transposing LDS read.  At
+// query column whose reference maximum moves only when a step raises it by
+// more than 2^8 (the output is rescaled then, not at every step), O^T +=
+// V^T P^T with V^T from the transposing LDS read.  At
 // the end the waves' (m, l, O) are merged through LDS: the same
 // rescaling, by exp2(m_w - max_w m_w).
 //
@@ -42,6 +44,11 @@
 
 namespace fa {
 namespace {
+
+// Largest amount (log2 units) by which a row's scores may exceed the
+// reference maximum its probabilities are taken against: they stay below
+// 2^8, and their sums over any key range fit a float with room to spare.
+constexpr float kLazyRescale = 8.0f;
 
 template <int D, int W>
 struct DecCfg {
@@ -174,15 +181,23 @@ __global__ __launch_bounds__(W * 64) void decode_bf16_kernel(DecArgs a) {
     }
     float mx = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[i]);
+    for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(s[i], s[i + 1]));
     mx = max_halves(mx);
-    const float m_new = fmaxf(m, mx == -INFINITY ? -INFINITY : mx * sl2);
-    const float ref = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = fast_exp2(m - ref);  // 0 while the row has seen nothing
-    l *= alpha;
+    const float mt = mx == -INFINITY ? -INFINITY : mx * sl2;
+    // The reference maximum m moves only when a step raises some row's
+    // maximum by more than kLazyRescale (log2 units), and then for every row
+    // of the wave; otherwise the probabilities are taken against the old
+    // reference (at most 2^kLazyRescale each) and the output is not
+    // rescaled.  Exact in real arithmetic: O and l share the reference.
+    if (__builtin_amdgcn_ballot_w64(mt > m + kLazyRescale) != 0) {
+      const float m_new = fmaxf(m, mt);
+      const float alpha = fast_exp2(m - (m_new == -INFINITY ? 0.f : m_new));  // 0 while the row saw nothing
+      l *= alpha;
 #pragma unroll
-    for (int db = 0; db < C::kDB; ++db) oacc[db] *= alpha;
-    m = m_new;
+      for (int db = 0; db < C::kDB; ++db) oacc[db] *= alpha;
+      m = m_new;
+    }
+    const float ref = m == -INFINITY ? 0.f : m;
     // P = exp2(scale_log2 * S - ref) as bf16 pairs, in the order of the
     // transposing V read (element i is key 8(i/4) + 4(l/32) + i%4).
     u32x4 pw[2];
@@ -206,7 +221,6 @@ __global__ __launch_bounds__(W * 64) void decode_bf16_kernel(DecArgs a) {
 #pragma unroll
       for (int db = 0; db < C::kDB; ++db)
         oacc[db] = mfma_bf16(tl.read_cols_tr(vt, 16 * c2, 32 * db), bf16x8_of(pw[c2]), oacc[db]);
-    settle_acc(oacc);
   };
 
   // The wave's steps through a ring of kDepth register sets: step j is
@@ -229,6 +243,8 @@ __global__ __launch_bounds__(W * 64) void decode_bf16_kernel(DecArgs a) {
       });
     }
   }
+
+  settle_acc(oacc);  // the loop's last products, before the merge reads them
 
   // Merge the four waves: each scales its O^T by exp2(m_w - M), M the
   // largest m_w of the query, and the sums add up.
