@@ -49,7 +49,10 @@
  * Stream   Work is enqueued on `stream` (a hipStream_t; NULL = the null
  *          stream) and the call returns once it is enqueued; results are
  *          valid after the caller synchronises that stream.  The calls keep
- *          no state and are safe to make from several threads.
+ *          no state and are safe to make from several threads.  They put
+ *          nothing on the stream but kernel launches (no allocation, memset,
+ *          copy or synchronisation), so a caller may record them into a HIP
+ *          graph by stream capture and replay it.
  * Sizes    B, H, n_q, n_k >= 1; d is 32, 64 or 128; B*H and each of n_q, n_k
  *          at most 2^31 - 1; scale finite and >= 0; causal 0 or 1.
  * Errors   Every argument is validated on the host before anything is
