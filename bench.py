@@ -683,11 +683,14 @@ def run_configs(args, torch, fa, workloads, dev):
 # and the per-kernel traffic records load_traffic() reads.
 
 STAGE_PATTERNS = [("bwd_preprocess", "bwd_preprocess"), ("bwd_dkdv", "bwd_dkdv"), ("bwd_dq", "bwd_dq"),
-                  ("decode", "decode_bf16"), ("lse_merge", "lse_merge"), ("fwd", "fwd_")]
+                  ("bwd_reduce", "bwd_reduce_slices"), ("decode", "decode_bf16"), ("lse_merge", "lse_merge"),
+                  ("fwd", "fwd_")]
 COPY_KIB = 512 * 1024  # the calibration copy reads and writes 512 MiB
 
 
 def stage_of(kernel_name: str):
+    """The library stage a profiled kernel belongs to, from its (demangled or
+    mangled) name; None for kernels outside the library, such as torch's."""
     for stage, pat in STAGE_PATTERNS:
         if pat in kernel_name:
             return stage
