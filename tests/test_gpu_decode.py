@@ -1,6 +1,7 @@
 """GPU parity of split-KV decoding (fa_decode) and of the merge of results
 over disjoint key sets (fa_lse_merge) against the fp64 oracle."""
 import math
+import random
 
 import numpy as np
 import pytest
@@ -57,6 +58,62 @@ def test_decode_parity(dev, case):
     torch.cuda.synchronize()
     off_ = n_k - n_q if off is None else off
     check_band(str(case), o.cpu(), lse.cpu(), q, k, v, scale, causal, off_, -1 if w is None else w, 2e-2)
+
+
+def _random_decode_cases(seed=23, count=14):
+    # Seeded shapes around the fixed cases above: several batch entries and
+    # group sizes (up to 64 query heads, so up to two 32-row blocks per K/V
+    # head and step), 1-40 new rows, caches from one key to several thousand
+    # (ragged against the 128-key chunk blocks), offsets that put rows before
+    # the first key, windows, and chunk counts up to more than the cache holds.
+    r = random.Random(seed)
+    out = []
+    for i in range(count):
+        h_kv = r.choice([1, 2, 3, 4, 8])
+        group = r.choice([g for g in (1, 2, 4, 5, 8, 16) if h_kv * g <= 64])
+        n_q = r.randint(1, 16) if r.random() < 0.8 else r.randint(17, 40)
+        n_k = r.randint(1, 6000)
+        causal = i % 3 != 2
+        u = r.random()
+        off = None if u < 0.45 else -r.randint(1, n_q) if u < 0.6 else r.randint(0, n_k)
+        w = None if r.random() < 0.7 else r.randint(0, 400)
+        splits = None if r.random() < 0.5 else r.randint(1, 12)
+        out.append((r.randint(1, 3), h_kv * group, h_kv, n_q, n_k, r.choice([32, 64, 128]), causal, off, w,
+                    splits))
+    return out
+
+
+@pytest.mark.parametrize("case", _random_decode_cases(),
+                         ids=lambda c: "B{}H{}kv{}_q{}_k{}_d{}_c{}_off{}_w{}_s{}".format(*c))
+def test_decode_random_cases(dev, case):
+    test_decode_parity(dev, case)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("n_q,splits", [(1, None), (1, 1), (3, 5)])
+def test_decode_running_max_stress(dev, d, n_q, splits):
+    # The decoding kernel keeps a reference maximum per row and rescales its
+    # sums only when a block's maximum passes it by a margin; the query rows
+    # of a K/V group share a wave, so one row's jump rescales all of them.
+    # K/V head 0: key j scores c * f(j) for a query row of constant c, with f
+    # rising slowly (well under the margin per 32 keys), a jump past the
+    # margin at key 1800 and a spike near the end; its four query heads rise
+    # at different rates or fall (c = -1).  K/V head 1: scores near -30.
+    B, H, h_kv, n_k = 1, 8, 2, 3000
+    scale = 1 / math.sqrt(d)
+    q, k, v = draw(5900 + d + n_q, B, H, h_kv, n_q, n_k, d, torch.float32)
+    j = torch.arange(n_k, dtype=torch.float32)
+    f = 0.012 * j + 12.0 * (j >= 1800).float() + 15.0 * (j == n_k - 5).float()
+    k[0, 0] = (f / (d * scale))[:, None].expand(n_k, d)
+    for h, c in enumerate((1.0, 0.5, -1.0, 1.5)):
+        q[0, h] = c
+    q[0, 4:] = -q[0, 4:].abs() * 2.0
+    k[0, 1] = k[0, 1].abs() * 2.0
+    q, k, v = (t.to(torch.bfloat16) for t in (q, k, v))
+    o, lse = fa.decode(q.to(dev), k.to(dev), v.to(dev), causal=True, scale=scale, n_splits=splits)
+    torch.cuda.synchronize()
+    check_band(f"d={d} n_q={n_q} splits={splits}", o.cpu(), lse.cpu(), q, k, v, scale, True, n_k - n_q, -1,
+               2e-2)
 
 
 def test_decode_workload_size_sampled_heads(dev):
