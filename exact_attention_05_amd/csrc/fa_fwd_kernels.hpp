@@ -1264,10 +1264,13 @@ __global__ __launch_bounds__(256) void fwd_f32_split_kernel(FwdArgs a, int n_rb)
 // key dimension of product i is laid out so that lane group g = l / 16
 // contracts key 4g + i: the lane's own probability i is then its B operand,
 // and V is read at that key.  Rows of the LDS tiles are D + 4 floats apart,
-// so that the four lane groups' reads fall into different banks.
-template <int D>
+// so that the four lane groups' reads fall into different banks.  W waves
+// split the keys: 4, or 8 (two per SIMD, so that one wave's products run
+// beside the other's softmax and loads) where they fit in registers and LDS
+// (d <= 64: 175 registers, 136 KiB) and every wave gets several key steps.
+template <int D, int W>
 struct F32Split16Cfg {
-  static constexpr int kWaves = 4;
+  static constexpr int kWaves = W;
   static constexpr int kThreads = kWaves * 64;
   static constexpr int kBN = 32;                       // keys per wave step (two 16-key sub-blocks)
   static constexpr int kDB = D / 16;                   // 16-row blocks of O^T
@@ -1282,9 +1285,10 @@ struct F32Split16Cfg {
   static_assert(kLoads * 64 == kBN * kChunks, "step load split");
 };
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void fwd_f32_split16_kernel(FwdArgs a, int n_rb) {
-  using C = F32Split16Cfg<D>;
+template <int D, bool CAUSAL, int W>
+__global__ __launch_bounds__(W * 64) void fwd_f32_split16_kernel(FwdArgs a, int n_rb) {
+  using C = F32Split16Cfg<D, W>;
+  static_assert(W == 4 || (W == 8 && D <= 64), "eight waves only where their tiles fit in LDS");
   __shared__ __attribute__((aligned(16))) float smem[C::kSmem];
 
   const int work = xcd_remap(blockIdx.x, gridDim.x);
@@ -1413,7 +1417,7 @@ __global__ __launch_bounds__(256) void fwd_f32_split16_kernel(FwdArgs a, int n_r
   }
 
   // Merge: each wave's O (rows = queries), m and l (summed over the four
-  // lane groups); then 16 threads per row combine the waves.
+  // lane groups); then 16 threads per row (the first 256) combine the waves.
   __syncthreads();
   float* const mo = smem;
   float* const mm = smem + C::kWaves * 16 * C::kOPitch;
@@ -1429,6 +1433,7 @@ __global__ __launch_bounds__(256) void fwd_f32_split16_kernel(FwdArgs a, int n_r
     ml[wave * 16 + l16] = lt;
   }
   __syncthreads();
+  if (tid >= 256) return;
   const int r = tid / 16;
   const int col0 = (tid % 16) * C::kColsPerThread;
   float mq = -INFINITY;
@@ -1531,10 +1536,21 @@ hipError_t fwd_f32_split_t(const FwdArgs& a, hipStream_t stream) {
   return launch(fwd_f32_split_kernel<D, CAUSAL>, n_rb * a.BH, F32SplitCfg<D>::kThreads, a, n_rb, stream);
 }
 
+// Eight waves from this many keys on (four 32-key steps per wave); below it
+// half of them would have one step or none.  Measured on MI355X, 4 -> 8
+// waves: c2 fp32 (n = 4096, d = 64) 77.5 -> 60.7 us, d = 32 44.3 -> 33.7
+// us, H=2 n=2048 d=64 40.8 -> 33.9 us; c1 (128 keys) 4.8 -> 5.7 us.
+constexpr int kSplit16WideKeys = 1024;
+
 template <int D, bool CAUSAL>
 hipError_t fwd_f32_split16_t(const FwdArgs& a, hipStream_t stream) {
   const int n_rb = (a.n_q + 15) / 16;
-  return launch(fwd_f32_split16_kernel<D, CAUSAL>, n_rb * a.BH, F32Split16Cfg<D>::kThreads, a, n_rb, stream);
+  if constexpr (D <= 64) {
+    if (a.n_k >= kSplit16WideKeys)
+      return launch(fwd_f32_split16_kernel<D, CAUSAL, 8>, n_rb * a.BH, F32Split16Cfg<D, 8>::kThreads, a, n_rb,
+                    stream);
+  }
+  return launch(fwd_f32_split16_kernel<D, CAUSAL, 4>, n_rb * a.BH, F32Split16Cfg<D, 4>::kThreads, a, n_rb, stream);
 }
 
 template <int D, bool CAUSAL, bool MERGE>

@@ -174,6 +174,33 @@ def test_fp32_32_row_key_split_parity(dev, case):
     check(f"{case}", got, q, k, v, do, scale, causal, off, w, torch.float32)
 
 
+# Float32 shapes with at most 128 blocks of 32 rows (the 16-row key-split
+# kernel): at d <= 64 from 1024 keys on its eight-wave form (the keys spread
+# over eight waves, two per SIMD), below that and at d = 128 its four-wave
+# form; both sides of the 1024-key boundary, masks, offsets, a window and
+# shared K/V heads.
+F32_SPLIT16 = [  # B, H, H_kv, n_q, n_k, causal, q_offset, window, d
+    (1, 1, 1, 4096, 4096, False, 0, -1, 64),
+    (1, 1, 1, 1500, 1024, True, 0, -1, 64),
+    (1, 1, 1, 1500, 1023, True, 0, -1, 64),
+    (1, 2, 1, 700, 3001, False, 0, -1, 32),
+    (2, 1, 1, 257, 2000, True, 1743, -1, 32),
+    (1, 2, 2, 900, 5000, False, 2000, 600, 64),
+    (1, 4, 2, 500, 1100, True, -17, -1, 64),
+    (1, 1, 1, 2000, 2000, False, 0, -1, 128),
+]
+
+
+@pytest.mark.parametrize("case", F32_SPLIT16, ids=lambda c: "B{}H{}kv{}_{}x{}_c{}_off{}_w{}_d{}".format(*c))
+def test_fp32_16_row_key_split_parity(dev, case):
+    B, H, h_kv, n_q, n_k, causal, off, w, d = case
+    assert B * H * -(-n_q // 32) <= 128
+    q, k, v, do = draw(5300 + n_q + n_k + d, B, H, h_kv, n_q, n_k, d, torch.float32)
+    scale = 1 / math.sqrt(d)
+    got = run(dev, q, k, v, do, scale, causal, off, w)
+    check(f"{case}", got, q, k, v, do, scale, causal, off, w, torch.float32)
+
+
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
 @pytest.mark.parametrize("case", STARVED, ids=lambda c: "B{}H{}kv{}_{}x{}_c{}_off{}_w{}_d{}".format(*c))
 def test_starved_shapes_parity(dev, case, dtype):
