@@ -48,8 +48,7 @@ DECODE = [  # B, H, H_kv, n_q, n_k, d, causal, q_offset (None: n_k - n_q), windo
 ]
 
 
-@pytest.mark.parametrize("case", DECODE, ids=lambda c: "B{}H{}kv{}_q{}_k{}_d{}_c{}_off{}_w{}_s{}".format(*c))
-def test_decode_parity(dev, case):
+def check_decode_case(dev, case):
     B, H, h_kv, n_q, n_k, d, causal, off, w, splits = case
     q, k, v = draw(5000 + n_k + d + n_q, B, H, h_kv, n_q, n_k, d)
     scale = 1 / math.sqrt(d)
@@ -58,6 +57,11 @@ def test_decode_parity(dev, case):
     torch.cuda.synchronize()
     off_ = n_k - n_q if off is None else off
     check_band(str(case), o.cpu(), lse.cpu(), q, k, v, scale, causal, off_, -1 if w is None else w, 2e-2)
+
+
+@pytest.mark.parametrize("case", DECODE, ids=lambda c: "B{}H{}kv{}_q{}_k{}_d{}_c{}_off{}_w{}_s{}".format(*c))
+def test_decode_parity(dev, case):
+    check_decode_case(dev, case)
 
 
 def _random_decode_cases(seed=23, count=14):
@@ -86,7 +90,7 @@ def _random_decode_cases(seed=23, count=14):
 @pytest.mark.parametrize("case", _random_decode_cases(),
                          ids=lambda c: "B{}H{}kv{}_q{}_k{}_d{}_c{}_off{}_w{}_s{}".format(*c))
 def test_decode_random_cases(dev, case):
-    test_decode_parity(dev, case)
+    check_decode_case(dev, case)
 
 
 @pytest.mark.parametrize("d", [64, 128])
