@@ -120,8 +120,9 @@ def decode_gqa(B: int = 4, H: int = 64, H_kv: int = 8, n_k: int = 32768, d: int 
 
 def random_qkv(seed: int, B: int, H: int, n_q: int, n_k: int, d: int,
                dtype: torch.dtype = torch.bfloat16, with_do: bool = False, std: float = 1.0):
-    """Generic seeded N(0, std^2) draws for test shapes: q (B,H,n_q,d), k, v
-    (B,H,n_k,d) and optionally dO (B,H,n_q,d)."""
+    """Generic seeded draws for test shapes, in the order q (B,H,n_q,d), k,
+    v (B,H,n_k,d) and optionally dO (B,H,n_q,d): q and k N(0, std^2) (std
+    sets the score magnitude), v and dO N(0, 1)."""
     gen = torch.Generator().manual_seed(seed)
     q = torch.randn(B, H, n_q, d, generator=gen) * std
     k = torch.randn(B, H, n_k, d, generator=gen) * std
