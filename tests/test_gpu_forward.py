@@ -204,8 +204,12 @@ def test_large_magnitude_inputs(dev):
         check_full(dev, q, k, v, 1 / math.sqrt(128), causal, "std 8")
 
 
-def test_repeatable_bitwise(dev):
-    q, k, v = workloads.random_qkv(12, 2, 4, 777, 777, 128, torch.bfloat16)
+# bf16 on the d = 128 kernels; fp32 with few row blocks and 1500 keys on the
+# eight-wave 16-row key-split kernel (its merge order is fixed)
+@pytest.mark.parametrize("B,H,n,d,dtype", [(2, 4, 777, 128, torch.bfloat16), (1, 2, 1500, 64, torch.float32)],
+                         ids=["bf16", "fp32_key_split"])
+def test_repeatable_bitwise(dev, B, H, n, d, dtype):
+    q, k, v = workloads.random_qkv(12, B, H, n, n, d, dtype)
     qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
     for causal in (False, True):
         a = fa.forward(qd, kd, vd, causal=causal)
@@ -214,10 +218,11 @@ def test_repeatable_bitwise(dev):
         assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
 
 
-@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
-def test_writes_stay_in_bounds(dev, dtype):
+@pytest.mark.parametrize("dtype,H,n", [(torch.bfloat16, 3, 200), (torch.float32, 3, 200), (torch.float32, 2, 1500)],
+                         ids=["bf16", "fp32", "fp32_eight_wave_key_split"])
+def test_writes_stay_in_bounds(dev, dtype, H, n):
     # Outputs are views into larger buffers filled with a canary value.
-    B, H, n, d = 1, 3, 200, 64
+    B, d = 1, 64
     q, k, v = (t.to(dev) for t in workloads.random_qkv(13, B, H, n, n, d, dtype))
     pad = 4096
     ob = torch.full((pad + B * H * n * d + pad,), 1234.0, dtype=dtype, device=dev)
